@@ -1,0 +1,138 @@
+/*
+ * focus_nvfp4.h -- C ABI of libfocus_nvfp4, the FOCUS NVFP4 quantizer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  "FOCUS NVFP4 scales for Llama-3.2-1B-Instruct (our
+ * reproduction)", section "What this is", gives the method: per weight
+ * tensor W [out_features, in_features] a frozen FP32 tensor scale s2 (field
+ * table, row s2), per 16 consecutive elements along in_features an FP32
+ * block factor m (row m), per 8-element half of a block an FP32 logit q
+ * (row q), and three equations:
+ *     S_b  = e4m3(clamp(max|w_b| * m_b / (6 * s2), 2^-6, 448))
+ *     c_i  = E2M1(clamp(w_i / (S_b * sigmoid(q_k) * s2), -6, 6))
+ *     w'_i = c_i * S_b * s2
+ * with E2M1 rounded to nearest, ties to even, and a block whose scaled
+ * maximum is zero taking scale 1 before the clamp.  The stored result is
+ * plain NVFP4: E2M1 codes, one E4M3 scale byte per 16 elements, one FP32
+ * scale per tensor (same section, paragraph after the equations).  The same
+ * page quantizes activations with one scale per token.
+ *
+ * Arithmetic contract.  Every operation is one IEEE binary32 operation with
+ * round-to-nearest-even, in the order printed above: t = (a*m)/(6*s2),
+ * d = (S*sig)*s2, x = w/d, w' = bf16((c*S)*s2); sigmoid(q) = 1/(1+expf(-q))
+ * with expf correctly rounded.  E4M3 is the OCP E4M3FN format (max 448).
+ * Where the page is silent:
+ *   - codes are packed two per byte, element 2j in the low nibble;
+ *   - scale bytes are linear, row-major [rows, cols/16];
+ *   - a negative element that rounds to zero keeps its sign (code 0x8);
+ *   - sub-block k (0: elements 0-7, 1: elements 8-15) of block b of row r
+ *     uses q[r, 2b+k];
+ *   - s2 == 0 (an all-zero tensor or token) gives scale byte 0x38 (1.0) for
+ *     every block and signed-zero codes.
+ *
+ * Conventions for every call.
+ *   - All data pointers are DEVICE pointers on the current HIP device,
+ *     allocated and owned by the caller; the library allocates nothing and
+ *     keeps no state.  Tensors are dense and row-major.
+ *   - BF16 data is passed as uint16_t bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call is
+ *     asynchronous and stream-ordered; none synchronizes.
+ *   - Arguments are validated on the host before any HIP call.  A failed
+ *     check returns an error status and leaves every output untouched.
+ *     FOCUS_ERR_HIP reports a failed kernel launch.
+ *   - Value preconditions are documented, not checked (a check would need a
+ *     device-to-host round trip): inputs finite; s2 finite and >= 0; the
+ *     denominators (S_b*sigmoid(q_k))*s2 nonzero, which holds for
+ *     q > -30 and amax|W| > 2^-100.  q = +inf is allowed (sigmoid = 1).
+ *   - An empty tensor (rows == 0 or cols == 0) is a no-op returning FOCUS_OK
+ *     (focus_tensor_scale with numel == 0 writes s2 = 0).
+ */
+#ifndef FOCUS_NVFP4_H
+#define FOCUS_NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FOCUS_NVFP4_ABI_VERSION 1
+
+typedef enum focus_status {
+    FOCUS_OK = 0,
+    FOCUS_ERR_NULL = 1,   /* a required pointer is NULL */
+    FOCUS_ERR_SHAPE = 2,  /* negative size, cols % 16 != 0, or size overflow */
+    FOCUS_ERR_ALIGN = 3,  /* a pointer is not aligned as documented */
+    FOCUS_ERR_HIP = 4,    /* a HIP launch failed */
+    FOCUS_ERR_RANGE = 5   /* an argument is outside its documented range */
+} focus_status;
+
+/* Returns FOCUS_NVFP4_ABI_VERSION of the built library. */
+int focus_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* focus_status_string(int status);
+
+/*
+ * Tensor scale (field table, row s2): s2 = amax|W| / (6*448), one binary32
+ * division by 2688.  The maximum is exact (an integer maximum over the BF16
+ * magnitude bits).
+ *   w_bf16    [numel] BF16, 16-byte aligned.
+ *   numel     >= 0 elements (any count).
+ *   s2_out    one float, 4-byte aligned; also the accumulator of the
+ *             reduction, so it must not alias w.
+ *   amax_out  one float or NULL; receives amax|W|.
+ * Three kernels on `stream`: clear, reduce (atomic max), finalize.
+ */
+int focus_tensor_scale(const uint16_t* w_bf16, int64_t numel,
+                       float* s2_out, float* amax_out, void* stream);
+
+/*
+ * The quantizer: equations S_b, c_i and (optionally) w'_i.
+ *   w_bf16  [rows, cols] BF16, cols % 16 == 0, 16-byte aligned.
+ *   m       [rows, cols/16] FP32, 4-byte aligned, or NULL for m = 1.
+ *   q       [rows, cols/8] FP32, 8-byte aligned, or NULL for sigmoid = 1.
+ *   s2      one FP32 (device pointer), e.g. written by focus_tensor_scale.
+ *   codes   [rows, cols/2] bytes out, 8-byte aligned.
+ *   scales  [rows, cols/16] E4M3 bytes out.
+ *   w_deq   [rows, cols] BF16 out, 16-byte aligned, or NULL to skip the
+ *           dequantized output.
+ * One kernel launch.  Outputs must not overlap inputs.
+ */
+int focus_quantize(const uint16_t* w_bf16, int64_t rows, int64_t cols,
+                   const float* m, const float* q, const float* s2,
+                   uint8_t* codes, uint8_t* scales, uint16_t* w_deq,
+                   void* stream);
+
+/*
+ * Dequantize stored NVFP4 data (equation w'_i): out = bf16((c*S)*s2).
+ *   codes   [rows, cols/2] bytes, 8-byte aligned; scales [rows, cols/16].
+ *   s2      s2_per_row == 0: one float used for every row (weights);
+ *           s2_per_row == 1: [rows] floats, one per row (activations).
+ *   out     [rows, cols] BF16, 16-byte aligned.
+ * One kernel launch.  Bitwise equal to focus_quantize's w_deq.
+ */
+int focus_dequantize(const uint8_t* codes, const uint8_t* scales,
+                     const float* s2, int s2_per_row,
+                     int64_t rows, int64_t cols, uint16_t* out, void* stream);
+
+/*
+ * Per-token activation quantization (one scale per token, section "What
+ * this is"): for each row t of X [tokens, hidden], s2_t = amax|x_t| / 2688,
+ * then the quantizer with m = 1 and sigmoid = 1.
+ *   x_bf16  [tokens, hidden] BF16, hidden % 16 == 0, 16-byte aligned.
+ *   codes   [tokens, hidden/2] out, 8-byte aligned.
+ *   scales  [tokens, hidden/16] out.
+ *   s2_out  [tokens] FP32 out.
+ *   x_deq   [tokens, hidden] BF16 out, 16-byte aligned, or NULL.
+ * One kernel launch (one wavefront per token).
+ */
+int focus_quantize_act_per_token(const uint16_t* x_bf16, int64_t tokens, int64_t hidden,
+                                 uint8_t* codes, uint8_t* scales, float* s2_out,
+                                 uint16_t* x_deq, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FOCUS_NVFP4_H */
