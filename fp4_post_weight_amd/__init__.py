@@ -1,0 +1,169 @@
+"""fp4_post_weight_amd -- the FOCUS NVFP4 quantizer on AMD MI355X (gfx950).
+
+A thin binding over the C ABI of ``libfocus_nvfp4.so`` (declared in
+``include/focus_nvfp4.h``): argument marshalling only.  Every step of the
+quantizer runs in the library's HIP kernels; torch supplies device memory
+(``torch.empty`` on the input's device) and the current HIP stream.  If the
+library has not been built, every call raises ``FocusLibraryMissing``; there
+is no fallback.
+
+Calls (same names as the C ABI, without the ``focus_`` prefix):
+
+* ``tensor_scale(w)`` -> (s2, amax), FP32 tensors of one element
+* ``quantize(w, m=None, q=None, s2=None, dequant=True)``
+  -> ``Quantized(codes, scales, w_deq, s2)``
+* ``dequantize(codes, scales, s2)`` -> BF16 tensor
+* ``quantize_act_per_token(x, dequant=False)``
+  -> ``Quantized(codes, scales, x_deq, s2 [tokens])``
+
+BF16 inputs are ``torch.bfloat16`` tensors; codes and scales are ``uint8``
+([rows, cols/2] with element 2j in the low nibble, and [rows, cols/16] E4M3
+bytes).
+"""
+from __future__ import annotations
+
+from typing import NamedTuple, Optional
+
+import torch
+
+from . import _lib
+from ._lib import FocusError, FocusLibraryMissing, library_path  # noqa: F401
+
+__all__ = ["tensor_scale", "quantize", "dequantize", "quantize_act_per_token", "Quantized",
+           "FocusError", "FocusLibraryMissing", "abi_version", "library_path"]
+
+
+class Quantized(NamedTuple):
+    codes: torch.Tensor
+    scales: torch.Tensor
+    deq: Optional[torch.Tensor]
+    s2: torch.Tensor
+
+
+def abi_version() -> int:
+    return _lib.lib().focus_abi_version()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check_dev(name, t, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+
+
+def _p(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def tensor_scale(w: torch.Tensor, s2_out: Optional[torch.Tensor] = None,
+                 amax_out: Optional[torch.Tensor] = None):
+    """s2 = amax|W| / (6*448) (and amax) as one-element FP32 device tensors."""
+    _check_dev("w", w, torch.bfloat16)
+    dev = w.device
+    if s2_out is None:
+        s2_out = torch.empty(1, dtype=torch.float32, device=dev)
+    if amax_out is None:
+        amax_out = torch.empty(1, dtype=torch.float32, device=dev)
+    _check_dev("s2_out", s2_out, torch.float32, dev)
+    _check_dev("amax_out", amax_out, torch.float32, dev)
+    _lib.check(_lib.lib().focus_tensor_scale(_p(w), w.numel(), _p(s2_out), _p(amax_out),
+                                             _stream(w)))
+    return s2_out, amax_out
+
+
+def quantize(w: torch.Tensor, m: Optional[torch.Tensor] = None, q: Optional[torch.Tensor] = None,
+             s2: Optional[torch.Tensor] = None, dequant: bool = True,
+             out: Optional[Quantized] = None) -> Quantized:
+    """FOCUS quantizer of W [rows, cols] (BF16); m [rows, cols/16] FP32 or None
+    (m = 1); q [rows, cols/8] FP32 or None (sigmoid = 1); s2 a one-element FP32
+    device tensor, computed with ``tensor_scale`` when None."""
+    _check_dev("w", w, torch.bfloat16)
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [rows, cols]")
+    rows, cols = w.shape
+    dev = w.device
+    if cols % 16:
+        raise ValueError("cols must be a multiple of 16")
+    if m is not None:
+        _check_dev("m", m, torch.float32, dev)
+        if tuple(m.shape) != (rows, cols // 16):
+            raise ValueError(f"m must be [{rows}, {cols // 16}]")
+    if q is not None:
+        _check_dev("q", q, torch.float32, dev)
+        if tuple(q.shape) != (rows, cols // 8):
+            raise ValueError(f"q must be [{rows}, {cols // 8}]")
+    if s2 is None:
+        s2, _ = tensor_scale(w)
+    _check_dev("s2", s2, torch.float32, dev)
+    if s2.numel() < 1:
+        raise ValueError("s2 must hold one float")
+    if out is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+        deq = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) if dequant else None
+    else:
+        codes, scales, deq = out.codes, out.scales, (out.deq if dequant else None)
+        _check_dev("codes", codes, torch.uint8, dev)
+        _check_dev("scales", scales, torch.uint8, dev)
+        if codes.numel() != rows * cols // 2 or scales.numel() != rows * cols // 16:
+            raise ValueError("output buffers have the wrong size")
+        if deq is not None:
+            _check_dev("deq", deq, torch.bfloat16, dev)
+            if deq.numel() != rows * cols:
+                raise ValueError("deq buffer has the wrong size")
+    _lib.check(_lib.lib().focus_quantize(_p(w), rows, cols, _p(m), _p(q), _p(s2), _p(codes),
+                                         _p(scales), _p(deq), _stream(w)))
+    return Quantized(codes, scales, deq, s2)
+
+
+def dequantize(codes: torch.Tensor, scales: torch.Tensor, s2: torch.Tensor,
+               s2_per_row: bool = False, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """BF16 [rows, cols] = (c * S) * s2 from stored codes and scale bytes."""
+    _check_dev("codes", codes, torch.uint8)
+    dev = codes.device
+    _check_dev("scales", scales, torch.uint8, dev)
+    _check_dev("s2", s2, torch.float32, dev)
+    rows, half = codes.shape
+    cols = 2 * half
+    if tuple(scales.shape) != (rows, cols // 16):
+        raise ValueError(f"scales must be [{rows}, {cols // 16}]")
+    if s2.numel() < (rows if s2_per_row else 1):
+        raise ValueError("s2 too small")
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    _check_dev("out", out, torch.bfloat16, dev)
+    _lib.check(_lib.lib().focus_dequantize(_p(codes), _p(scales), _p(s2), 1 if s2_per_row else 0,
+                                           rows, cols, _p(out), _stream(codes)))
+    return out
+
+
+def quantize_act_per_token(x: torch.Tensor, dequant: bool = False,
+                           out: Optional[Quantized] = None) -> Quantized:
+    """Per-token NVFP4 of activations X [tokens, hidden] (one s2 per row)."""
+    _check_dev("x", x, torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [tokens, hidden]")
+    t, h = x.shape
+    if h % 16:
+        raise ValueError("hidden must be a multiple of 16")
+    dev = x.device
+    if out is None:
+        codes = torch.empty((t, h // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((t, h // 16), dtype=torch.uint8, device=dev)
+        s2 = torch.empty((t,), dtype=torch.float32, device=dev)
+        deq = torch.empty((t, h), dtype=torch.bfloat16, device=dev) if dequant else None
+    else:
+        codes, scales, s2, deq = out.codes, out.scales, out.s2, (out.deq if dequant else None)
+    _lib.check(_lib.lib().focus_quantize_act_per_token(_p(x), t, h, _p(codes), _p(scales), _p(s2),
+                                                       _p(deq), _stream(x)))
+    return Quantized(codes, scales, deq, s2)

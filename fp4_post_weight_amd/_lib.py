@@ -1,0 +1,65 @@
+"""ctypes loader of libfocus_nvfp4.so (built in-tree by ``build.py``).
+
+The C signatures mirror include/focus_nvfp4.h: device pointers and sizes as
+integers, the stream as a ``hipStream_t`` handle (``void*``).  There is no
+fallback: a missing library raises ``FocusLibraryMissing``.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfocus_nvfp4.so")
+
+_VP = ct.c_void_p
+_I64 = ct.c_int64
+_INT = ct.c_int
+
+_SIGNATURES = {
+    "focus_abi_version": (_INT, []),
+    "focus_status_string": (ct.c_char_p, [_INT]),
+    "focus_tensor_scale": (_INT, [_VP, _I64, _VP, _VP, _VP]),
+    "focus_quantize": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "focus_dequantize": (_INT, [_VP, _VP, _VP, _INT, _I64, _I64, _VP, _VP]),
+    "focus_quantize_act_per_token": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
+}
+
+EXPORTED = tuple(_SIGNATURES)
+
+_lib = None
+
+
+class FocusLibraryMissing(RuntimeError):
+    pass
+
+
+class FocusError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libfocus_nvfp4 status {status}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FocusLibraryMissing(
+                f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+        handle = ct.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != 0:
+        msg = lib().focus_status_string(status).decode()
+        raise FocusError(status, msg)

@@ -1,0 +1,131 @@
+"""The C ABI: the library loads, exports every symbol include/*.h declares,
+and rejects bad arguments on the host before any HIP call (CPU only: no
+call here reaches a kernel launch)."""
+import ctypes as ct
+import glob
+import os
+import re
+
+import pytest
+
+from fp4_post_weight_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# status codes of include/focus_nvfp4.h
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_HIP, ERR_RANGE = 0, 1, 2, 3, 4, 5
+
+FAKE = 0x10000  # a 64 KiB-aligned address that is never dereferenced
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(focus_[a-z0-9_]+)\s*\(", text, re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libfocus_nvfp4.so is not built (run __graft_entry__.build())")
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"focus_tensor_scale", "focus_quantize", "focus_dequantize",
+            "focus_quantize_act_per_token"} <= names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared but not exported"
+    assert names <= set(_lib.EXPORTED), "binding does not wrap every declared call"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.focus_abi_version() == 1
+    for s in range(6):
+        assert lib.focus_status_string(s)
+    assert lib.focus_status_string(99) == b"unknown status"
+
+
+def test_quantize_validation(lib):
+    q = lib.focus_quantize
+    # null required pointers
+    assert q(None, 4, 32, None, None, FAKE, FAKE, FAKE, None, None) == ERR_NULL
+    assert q(FAKE, 4, 32, None, None, None, FAKE, FAKE, None, None) == ERR_NULL
+    assert q(FAKE, 4, 32, None, None, FAKE, None, FAKE, None, None) == ERR_NULL
+    assert q(FAKE, 4, 32, None, None, FAKE, FAKE, None, None, None) == ERR_NULL
+    # shapes
+    assert q(FAKE, 4, 24, None, None, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
+    assert q(FAKE, -1, 32, None, None, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
+    assert q(FAKE, 4, -16, None, None, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
+    assert q(FAKE, 1 << 40, 1 << 40, None, None, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
+    # alignment
+    assert q(FAKE + 2, 4, 32, None, None, FAKE, FAKE, FAKE, None, None) == ERR_ALIGN
+    assert q(FAKE, 4, 32, FAKE + 2, None, FAKE, FAKE, FAKE, None, None) == ERR_ALIGN
+    assert q(FAKE, 4, 32, None, FAKE + 4, FAKE, FAKE, FAKE, None, None) == ERR_ALIGN
+    assert q(FAKE, 4, 32, None, None, FAKE + 1, FAKE, FAKE, None, None) == ERR_ALIGN
+    assert q(FAKE, 4, 32, None, None, FAKE, FAKE + 4, FAKE, None, None) == ERR_ALIGN
+    assert q(FAKE, 4, 32, None, None, FAKE, FAKE, FAKE, FAKE + 8, None) == ERR_ALIGN
+    # empty tensors are a no-op, even with null pointers
+    assert q(None, 0, 32, None, None, None, None, None, None, None) == OK
+    assert q(None, 5, 0, None, None, None, None, None, None, None) == OK
+
+
+def test_dequantize_validation(lib):
+    d = lib.focus_dequantize
+    assert d(None, FAKE, FAKE, 0, 2, 32, FAKE, None) == ERR_NULL
+    assert d(FAKE, None, FAKE, 0, 2, 32, FAKE, None) == ERR_NULL
+    assert d(FAKE, FAKE, None, 0, 2, 32, FAKE, None) == ERR_NULL
+    assert d(FAKE, FAKE, FAKE, 0, 2, 32, None, None) == ERR_NULL
+    assert d(FAKE, FAKE, FAKE, 0, 2, 40, FAKE, None) == ERR_SHAPE
+    assert d(FAKE, FAKE, FAKE, 2, 2, 32, FAKE, None) == ERR_RANGE
+    assert d(FAKE + 4, FAKE, FAKE, 0, 2, 32, FAKE, None) == ERR_ALIGN
+    assert d(FAKE, FAKE, FAKE, 0, 2, 32, FAKE + 8, None) == ERR_ALIGN
+    assert d(None, None, None, 0, 0, 32, None, None) == OK
+
+
+def test_tensor_scale_validation(lib):
+    t = lib.focus_tensor_scale
+    assert t(FAKE, 10, None, None, None) == ERR_NULL
+    assert t(None, 10, FAKE, None, None) == ERR_NULL
+    assert t(FAKE, -1, FAKE, None, None) == ERR_SHAPE
+    assert t(FAKE + 8, 10, FAKE, None, None) == ERR_ALIGN
+    assert t(FAKE, 10, FAKE + 2, None, None) == ERR_ALIGN
+    assert t(FAKE, 10, FAKE, FAKE + 1, None) == ERR_ALIGN
+
+
+def test_act_validation(lib):
+    a = lib.focus_quantize_act_per_token
+    assert a(None, 4, 64, FAKE, FAKE, FAKE, None, None) == ERR_NULL
+    assert a(FAKE, 4, 64, None, FAKE, FAKE, None, None) == ERR_NULL
+    assert a(FAKE, 4, 64, FAKE, None, FAKE, None, None) == ERR_NULL
+    assert a(FAKE, 4, 64, FAKE, FAKE, None, None, None) == ERR_NULL
+    assert a(FAKE, 4, 60, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
+    assert a(FAKE, 1 << 32, 16, FAKE, FAKE, FAKE, None, None) == ERR_RANGE
+    assert a(FAKE, 4, 64, FAKE + 4, FAKE, FAKE, None, None) == ERR_ALIGN
+    assert a(FAKE, 4, 64, FAKE, FAKE, FAKE, FAKE + 8, None) == ERR_ALIGN
+    assert a(None, 0, 64, None, None, None, None, None) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    import fp4_post_weight_amd as focus
+    w = torch.zeros((4, 32), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        focus.quantize(w)
+    with pytest.raises(TypeError):
+        focus.tensor_scale(torch.zeros(4, dtype=torch.float32))
+
+
+def test_product_path_does_not_reach_the_oracle():
+    """The package and its sources never import or load the oracle."""
+    pkg = os.path.join(ROOT, "fp4_post_weight_amd")
+    for path in glob.glob(os.path.join(pkg, "**", "*"), recursive=True):
+        if path.endswith((".py", ".hip", ".h", ".cpp")):
+            text = open(path).read()
+            assert "oracle" not in text.replace("Oracle", "").lower().replace("no oracle", ""), path

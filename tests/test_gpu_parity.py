@@ -1,0 +1,284 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, element by
+element, on the same seeded inputs.  Runs on an MI355X only (marker gpu).
+
+Sizes: the full single linear and per-token activation cases; ragged shapes
+that span several 256-lane tiles with a partial tail; edge cases (zero
+blocks, signed zeros, an all-zero tensor, extreme magnitudes, subnormal
+scales, extreme logits); and every linear shape of the 8B and 70B weight
+sets at full size, launched exactly as the benchmark launches them and
+checked on sampled rows (plus the full tensor scale).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle_pins as pins
+import parity
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def focus():
+    import fp4_post_weight_amd as f
+    f._lib.lib()  # raises if the library is not built: no fallback
+    assert torch.cuda.is_available()
+    return f
+
+
+def np_bits(t):
+    return synth.bits(t)
+
+
+def run_weights(focus, w, m, q, dequant=True, s2=None):
+    wd = w.to(DEV)
+    md = None if m is None else m.to(DEV)
+    qd = None if q is None else q.to(DEV)
+    if s2 is None:
+        s2d, amaxd = focus.tensor_scale(wd)
+    else:
+        s2d, amaxd = torch.tensor([s2], dtype=torch.float32, device=DEV), None
+    res = focus.quantize(wd, md, qd, s2d, dequant=dequant)
+    torch.cuda.synchronize()
+    return (res.codes.cpu().numpy(), res.scales.cpu().numpy(),
+            None if res.deq is None else np_bits(res.deq), np.float32(s2d.item()),
+            None if amaxd is None else np.float32(amaxd.item()))
+
+
+def check_case(focus, orc, w, m, q, dequant=True, label=""):
+    wb = np_bits(w)
+    mn = None if m is None else m.numpy()
+    qn = None if q is None else q.numpy()
+    codes, scales, deq, s2, amax = run_weights(focus, w, m, q, dequant)
+    s2_o, amax_o = orc.tensor_scale(wb)
+    assert s2.view(np.uint32) == s2_o.view(np.uint32), f"{label}: s2 {s2} vs {s2_o}"
+    assert amax.view(np.uint32) == amax_o.view(np.uint32), label
+    return parity.check_quantized(orc, wb, mn, qn, s2_o, codes, scales, deq, label=label)
+
+
+# ---------------------------------------------------------------------------
+# the single linear, ragged shapes, variants
+# ---------------------------------------------------------------------------
+
+def test_single_linear(focus, orc):
+    w, m, q = synth.make_single()
+    st = check_case(focus, orc, w, m, q, True, "single [256,1024]")
+    assert st["code_mismatches"] == 0
+
+
+RAGGED = [(1, 16), (3, 48), (7, 112), (33, 4112), (5, 2064), (129, 1040), (1, 65536 + 16)]
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("variant", ["m_q_dq", "m_q", "q_only", "m_only", "plain_dq"])
+def test_ragged_shapes(focus, orc, shape, variant):
+    rows, cols = shape
+    seed = rows * 7919 + cols
+    w = synth.weights(shape, seed=seed, tensor_id=1, zero_block_p=0.02)
+    m = synth.block_factor_lognormal((rows, cols // 16), seed=seed, tensor_id=2) \
+        if "m" in variant.split("_") else None
+    q = synth.logits((rows, cols // 8), seed=seed, tensor_id=3) if "q" in variant else None
+    check_case(focus, orc, w, m, q, dequant=variant.endswith("dq"), label=f"{shape} {variant}")
+
+
+def test_fixed_points_and_closed_forms(focus, orc):
+    """The constructed blocks of the oracle pins, through the GPU."""
+    rng = np.random.default_rng(21)
+    sbytes, S, codes, wb = pins._fixed_point_case(rng, n_rows=111, nb=5)
+    w = torch.from_numpy(wb.view(np.int16).copy()).view(torch.bfloat16)
+    m2 = rng.integers(0, 2, (111, 5)).astype(bool)
+    m = torch.from_numpy(np.where(m2, 2.0, 1.0).astype(np.float32))
+    half = rng.integers(0, 2, (111, 10)).astype(bool)
+    q = torch.from_numpy(np.where(half, 0.0, np.inf).astype(np.float32))
+    for mm, qq in [(None, None), (m, None), (None, q), (m, q)]:
+        g = run_weights(focus, w, mm, qq, True, s2=float(pins.S2_POW2))
+        ref = orc.quantize(wb, None if mm is None else mm.numpy(), None if qq is None else qq.numpy(),
+                           pins.S2_POW2, True)
+        assert np.array_equal(g[0], ref[0]) and np.array_equal(g[1], ref[1])
+        assert np.array_equal(g[2], ref[2])
+
+
+def test_zero_blocks_and_signed_zeros(focus, orc):
+    rng = np.random.default_rng(22)
+    x = (rng.standard_normal((40, 512)) * 0.02).astype(np.float32)
+    wb = pins.torch_bf16_bits(x)
+    wb[0, :] = 0
+    wb[1, :] = 0x8000
+    wb[2, 16:32] = 0x8000
+    wb[3, ::2] = 0x8000
+    wb[3, 1::2] = 0
+    w = torch.from_numpy(wb.view(np.int16).copy()).view(torch.bfloat16)
+    m = torch.ones((40, 32))
+    m[5, 3] = 0.0
+    q = synth.logits((40, 64), seed=3, tensor_id=0)
+    st = check_case(focus, orc, w, m, q, True, "zero blocks")
+    assert st["code_mismatches"] == 0
+
+
+def test_all_zero_tensor(focus, orc):
+    wb = np.zeros((8, 64), np.uint16)
+    wb[2, 7] = 0x8000
+    w = torch.from_numpy(wb.view(np.int16).copy()).view(torch.bfloat16)
+    codes, scales, deq, s2, amax = run_weights(focus, w, None, synth.logits((8, 8), seed=1, tensor_id=0))
+    assert s2 == 0 and amax == 0
+    assert np.all(scales == 0x38)
+    ref = orc.quantize(wb, None, None, np.float32(0))
+    assert np.array_equal(codes, ref[0]) and np.array_equal(deq, ref[2])
+
+
+def test_extreme_magnitudes(focus, orc):
+    """Near-largest BF16 values, subnormal BF16 weights, mixed scales."""
+    rng = np.random.default_rng(23)
+    rows, cols = 64, 256
+    e = rng.integers(-140, 127, (rows, cols)).astype(np.float64)
+    x = (rng.standard_normal((rows, cols)) * np.exp2(e)).astype(np.float32)
+    x[0, 0] = 3.3e38
+    wb = pins.torch_bf16_bits(x)
+    w = torch.from_numpy(wb.view(np.int16).copy()).view(torch.bfloat16)
+    q = synth.logits((rows, cols // 8), seed=4, tensor_id=0)
+    m = synth.block_factor_lognormal((rows, cols // 16), seed=4, tensor_id=1)
+    check_case(focus, orc, w, m, q, True, "extreme magnitudes")
+
+
+@pytest.mark.parametrize("amax_exp", [-133, -126, -120, -100])
+def test_tiny_tensor_subnormal_scales(focus, orc, amax_exp):
+    """amax near the bottom of the BF16 range: s2 and the denominators
+    (S*sigmoid)*s2 are binary32 subnormals or underflow to 0 (the literal
+    binary32 division path)."""
+    rng = np.random.default_rng(100 - amax_exp)
+    rows, cols = 16, 128
+    x = (rng.uniform(-1, 1, (rows, cols)) * 2.0 ** amax_exp).astype(np.float32)
+    wb = pins.torch_bf16_bits(x)
+    w = torch.from_numpy(wb.view(np.int16).copy()).view(torch.bfloat16)
+    q = torch.from_numpy(rng.uniform(-5, 20, (rows, cols // 8)).astype(np.float32))
+    check_case(focus, orc, w, None, q, True, f"tiny 2^{amax_exp}")
+
+
+def test_extreme_logits(focus, orc):
+    rows, cols = 32, 512
+    w = synth.weights((rows, cols), seed=5, tensor_id=1)
+    vals = np.array([np.inf, 100.0, 17.0, 16.0, 6.0, 0.0, -0.0, -1.0, -10.0, -20.0, -40.0],
+                    np.float32)
+    rng = np.random.default_rng(24)
+    q = torch.from_numpy(vals[rng.integers(0, len(vals), (rows, cols // 8))])
+    check_case(focus, orc, w, None, q, True, "extreme logits")
+
+
+# ---------------------------------------------------------------------------
+# tensor scale, dequantize, round trip, determinism, streams
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("numel", [0, 1, 7, 8, 9, 15, 16, 17, 4093, 1_000_003, (1 << 22) + 5])
+def test_tensor_scale_sizes(focus, orc, numel):
+    rng = np.random.default_rng(numel)
+    x = (rng.standard_normal(numel) * 0.02).astype(np.float32)
+    if numel > 3:
+        x[numel // 3] = -7.5  # the maximum magnitude is negative
+    wb = pins.torch_bf16_bits(x)
+    w = torch.from_numpy(wb.view(np.int16).copy()).view(torch.bfloat16).to(DEV)
+    s2, amax = focus.tensor_scale(w)
+    s2_o, amax_o = orc.tensor_scale(wb)
+    assert s2.item() == float(s2_o) and amax.item() == float(amax_o)
+
+
+def test_dequantize_every_scale_byte(focus, orc):
+    rows, cols = 254, 64
+    rng = np.random.default_rng(25)
+    codes = rng.integers(0, 256, (rows, cols // 2)).astype(np.uint8)
+    sb = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)
+    scales = np.repeat(sb[:, None], cols // 16, axis=1)
+    scales[:, 1] = sb[::-1]
+    s2t = np.float32(0.0123)
+    s2r = rng.uniform(1e-6, 3.0, rows).astype(np.float32)
+    cd, sd = torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV)
+    out_t = focus.dequantize(cd, sd, torch.tensor([s2t], device=DEV))
+    out_r = focus.dequantize(cd, sd, torch.from_numpy(s2r).to(DEV), s2_per_row=True)
+    assert np.array_equal(np_bits(out_t), orc.dequantize(codes, scales, s2t))
+    assert np.array_equal(np_bits(out_r), orc.dequantize(codes, scales, s2r, s2_per_row=True))
+
+
+def test_roundtrip_determinism_and_stream(focus, orc):
+    w, m, q = synth.make_single(seed=7)
+    wd, md, qd = w.to(DEV), m.to(DEV), q.to(DEV)
+    r1 = focus.quantize(wd, md, qd, None, dequant=True)
+    r2 = focus.quantize(wd, md, qd, None, dequant=True)
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.stream(side):
+        r3 = focus.quantize(wd, md, qd, None, dequant=True)
+        back = focus.dequantize(r3.codes, r3.scales, r3.s2)
+    torch.cuda.current_stream(DEV).wait_stream(side)
+    torch.cuda.synchronize()
+    for r in (r2, r3):
+        assert torch.equal(r.codes, r1.codes) and torch.equal(r.scales, r1.scales)
+        assert torch.equal(r.deq.view(torch.int16), r1.deq.view(torch.int16))
+    assert torch.equal(back.view(torch.int16), r1.deq.view(torch.int16))
+    r4 = focus.quantize(wd, md, qd, r1.s2, dequant=False)
+    assert r4.deq is None and torch.equal(r4.codes, r1.codes)
+
+
+# ---------------------------------------------------------------------------
+# per-token activations
+# ---------------------------------------------------------------------------
+
+def check_act(focus, orc, x, dequant, label):
+    res = focus.quantize_act_per_token(x.to(DEV), dequant=dequant)
+    torch.cuda.synchronize()
+    xb = np_bits(x)
+    c, s, s2, xd = parity.oracle_act_rows(orc, xb, dequant)
+    assert np.array_equal(res.s2.cpu().numpy().view(np.uint32), s2.view(np.uint32)), label
+    assert np.array_equal(res.scales.cpu().numpy(), s), label
+    assert np.array_equal(res.codes.cpu().numpy(), c), label
+    if dequant:
+        assert np.array_equal(np_bits(res.deq), xd), label
+
+
+def test_act_per_token_full(focus, orc):
+    """The activation case: X [8192, 4096], N(0,1) with 2 % outlier channels."""
+    check_act(focus, orc, synth.make_activations(), False, "act [8192,4096]")
+
+
+@pytest.mark.parametrize("shape", [(1, 16), (5, 1024), (6, 2048), (7, 4096), (9, 8192), (3, 16400),
+                                   (13, 48), (2, 4112)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_act_per_token_shapes(focus, orc, shape):
+    x = synth.activations(shape, seed=shape[0] * 31 + shape[1], tensor_id=0)
+    x[0, :16] = 0.0
+    if shape[0] > 2:
+        x[2] = 0.0  # an all-zero token: s2 = 0
+    check_act(focus, orc, x, True, f"act {shape}")
+
+
+# ---------------------------------------------------------------------------
+# full-size linears, sampled rows
+# ---------------------------------------------------------------------------
+
+FULL = [("8B", s) for s in sorted(set(synth.LLAMA_8B.layer_shapes()))] + \
+       [("70B", (28672, 8192)), ("70B", (8192, 28672)), ("70B", (1024, 8192))]
+
+
+@pytest.mark.parametrize("ws_name,shape", FULL, ids=lambda v: v if isinstance(v, str) else f"{v[0]}x{v[1]}")
+@pytest.mark.parametrize("dequant", [False, True], ids=["codes", "codes+deq"])
+def test_full_size_sampled(focus, orc, ws_name, shape, dequant):
+    ws = synth.LLAMA_8B if ws_name == "8B" else synth.LLAMA_70B
+    lin = next(l for l in ws.linears() if (l.rows, l.cols) == shape)
+    w, m, q = synth.make_linear(ws, lin, device=DEV)
+    s2d, amaxd = focus.tensor_scale(w)
+    res = focus.quantize(w, m, q, s2d, dequant=dequant)
+    torch.cuda.synchronize()
+    rows, cols = shape
+    rng = np.random.default_rng(rows + cols)
+    idx = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 46)]))
+    it = torch.from_numpy(idx).to(DEV)
+    wb_full = np_bits(w)
+    s2_o, amax_o = orc.tensor_scale(wb_full)
+    assert s2d.item() == float(s2_o) and amaxd.item() == float(amax_o)
+    wb = wb_full[idx]
+    mn, qn = m[it].cpu().numpy(), q[it].cpu().numpy()
+    st = parity.check_quantized(orc, wb, mn, qn, s2_o, res.codes[it].cpu().numpy(),
+                                res.scales[it].cpu().numpy(),
+                                np_bits(res.deq[it]) if dequant else None,
+                                label=f"{ws_name} {shape}")
+    print(f"{ws_name} {shape} dequant={dequant}: {st}", flush=True)
