@@ -1,0 +1,325 @@
+"""Benchmark of the FOCUS NVFP4 quantizer on one MI355X.
+
+One step is one pass of the whole path over the Llama-3.1-8B-shaped weight
+set (224 linears, 6,979,321,856 weights) plus one batch of activations:
+
+  1. focus_tensor_scale     for every linear (s2 = amax|W| / 2688)
+  2. focus_quantize         for every linear, codes + scale bytes + fused w'
+  3. focus_dequantize       for every linear (codes + scales -> BF16)
+  4. focus_quantize_act_per_token on X [8192, 4096]
+
+Phases run in this order so that each kernel streams its operands from HBM
+(the set is 23 GB, far beyond the 256 MB last-level cache).  Inputs are
+generated on the GPU before the timed region (seeded, synthetic; see
+``synth``) and stay resident in HBM.
+
+``value`` is whole-step throughput in Gweights/s (weights of the set per
+second of step time).  ``roofline`` reports the dominant kernel,
+focus_quantize with w', against the 8 TB/s HBM peak: algorithmic bytes
+(5.3125 B per weight) / mean launch duration, every launch bracketed by HIP
+events on the stream it runs on.  ``rows`` breaks the step down per call and
+adds the codes-only quantize (3.3125 B per weight) timed after the steps.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload on the host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8b|1b]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Gweights/s + achieved HBM GB/s (% of peak), FOCUS NVFP4 quantize+pack, 8B set"
+HBM_PEAK_GBS = 8000.0
+
+# algorithmic bytes per weight (per element for activations)
+B_TENSOR_SCALE = 2.0
+B_QUANT = 2.0 + 0.25 + 0.5 + 0.5 + 0.0625          # W, m, q, codes, scales
+B_QUANT_DQ = B_QUANT + 2.0                          # + w'
+B_DEQUANT = 0.5 + 0.0625 + 2.0                      # codes, scales, out
+B_ACT = 2.0 + 0.5 + 0.0625                          # X, codes, scales (+4 B per token)
+
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "quantize_8b_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", choices=["8b", "1b"], default="8b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows-fraction", type=float, default=0.5,
+                    help="fraction of the rows of layer 0 the CPU oracle quantizes")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp4_post_weight_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """Per-launch HBM traffic of the dominant kernel from the committed
+    rocprofv3 counter summary, or None when it is absent or was taken on
+    other kernel sources."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the quantizer is measured on one MI355X "
+              "(multi-GPU sharding is a design note only). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp4_post_weight_amd as focus
+    import synth
+
+    focus._lib.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ws = synth.LLAMA_8B if args.workload == "8b" else synth.LLAMA_1B
+    lins = ws.linears()
+    n_weights = sum(l.numel for l in lins)
+
+    # ---- inputs (resident in HBM) and outputs ----------------------------
+    t0 = time.time()
+    W, M, Q = [], [], []
+    for lin in lins:
+        w, m, q = synth.make_linear(ws, lin, device=dev)
+        W.append(w)
+        M.append(m)
+        Q.append(q)
+    X = synth.make_activations(device=dev)
+    S2 = torch.empty((len(lins), 1), dtype=torch.float32, device=dev)
+    AMAX = torch.empty((len(lins), 1), dtype=torch.float32, device=dev)
+    OUT = [focus.Quantized(torch.empty((l.rows, l.cols // 2), dtype=torch.uint8, device=dev),
+                           torch.empty((l.rows, l.cols // 16), dtype=torch.uint8, device=dev),
+                           torch.empty((l.rows, l.cols), dtype=torch.bfloat16, device=dev),
+                           S2[i]) for i, l in enumerate(lins)]
+    DEQ = [torch.empty((l.rows, l.cols), dtype=torch.bfloat16, device=dev) for l in lins]
+    ACT = focus.quantize_act_per_token(X)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    print(f"# generated {ws.name}: {n_weights} weights in {gen_s:.1f} s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+    nlin = len(lins)
+
+    # Prepared batched calls, 32 linears each: every quantize / dequantize
+    # batch is exactly one kernel launch, every tensor-scale batch three.
+    chunks = [list(range(i, min(i + 32, nlin))) for i in range(0, nlin, 32)]
+    TS = [focus.tensor_scale_many([W[i] for i in c], S2[c[0]:c[-1] + 1], AMAX[c[0]:c[-1] + 1], run=False)
+          for c in chunks]
+    QB = [focus.quantize_many([W[i] for i in c], [M[i] for i in c], [Q[i] for i in c], [S2[i] for i in c],
+                              outs=[OUT[i] for i in c], dequant=True, run=False) for c in chunks]
+    QB_nodq = [focus.quantize_many([W[i] for i in c], [M[i] for i in c], [Q[i] for i in c],
+                                   [S2[i] for i in c], outs=[OUT[i] for i in c], dequant=False, run=False)
+               for c in chunks]
+    DB = [focus.dequantize_many([OUT[i].codes for i in c], [OUT[i].scales for i in c], [S2[i] for i in c],
+                                outs=[DEQ[i] for i in c], run=False) for c in chunks]
+    nq = len(QB)
+
+    # events of one step: [0] start, [1] tensor scales done, a pair around
+    # each quantize launch, quantize phase done, dequantize done, act done
+    n_ev = 5 + 2 * nq
+    E_TS, E_Q0, E_QEND, E_DQ, E_ACT = 1, 2, 2 + 2 * nq, 3 + 2 * nq, 4 + 2 * nq
+
+    def step(ev=None):
+        rec = (lambda j: ev[j].record(stream)) if ev is not None else (lambda j: None)
+        rec(0)
+        for b in TS:
+            b.run()
+        rec(E_TS)
+        for i, b in enumerate(QB):
+            rec(E_Q0 + 2 * i)
+            b.run()
+            rec(E_Q0 + 2 * i + 1)
+        rec(E_QEND)
+        for b in DB:
+            b.run()
+        rec(E_DQ)
+        focus.quantize_act_per_token(X, out=ACT)
+        rec(E_ACT)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region -------------------------------------------------------
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    gpu_ms = events[0][0].elapsed_time(events[-1][E_ACT])
+    ms_step = max(gpu_ms, wall * 1e3) / args.steps
+
+    q_launch_ms = []
+    phase = {"tensor_scale": 0.0, "quantize_dq": 0.0, "dequantize": 0.0, "act": 0.0}
+    for k in range(args.steps):
+        ev = events[k]
+        for i in range(nq):
+            q_launch_ms.append(ev[E_Q0 + 2 * i].elapsed_time(ev[E_Q0 + 2 * i + 1]))
+        phase["tensor_scale"] += ev[0].elapsed_time(ev[E_TS])
+        phase["quantize_dq"] += ev[E_TS].elapsed_time(ev[E_QEND])
+        phase["dequantize"] += ev[E_QEND].elapsed_time(ev[E_DQ])
+        phase["act"] += ev[E_DQ].elapsed_time(ev[E_ACT])
+    phase = {k: v / args.steps for k, v in phase.items()}
+    mean_launch_ms = float(np.mean(q_launch_ms))
+    bytes_per_launch = B_QUANT_DQ * n_weights / nq
+    achieved = bytes_per_launch / (mean_launch_ms * 1e-3) / 1e9
+
+    # ---- per-call rows outside the steps: each call alone, same buffers ----
+    def time_calls(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_q = time_calls(lambda: [b.run() for b in QB_nodq])
+    torch.cuda.synchronize()
+
+    def row(ms, nbytes, units):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"ms": round(ms, 4), "GB_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                "Gunits_s": round(units / (ms * 1e-3) / 1e9, 2)}
+
+    rows = {
+        "tensor_scale (step phase)": row(phase["tensor_scale"], B_TENSOR_SCALE * n_weights, n_weights),
+        "quantize + w' (step phase)": row(phase["quantize_dq"], B_QUANT_DQ * n_weights, n_weights),
+        "dequantize (step phase)": row(phase["dequantize"], B_DEQUANT * n_weights, n_weights),
+        "act per token [8192,4096] (step phase)": row(phase["act"], B_ACT * X.numel() + 4 * X.shape[0],
+                                                      X.numel()),
+        "quantize codes only (after the steps)": row(t_q, B_QUANT * n_weights, n_weights),
+    }
+
+    # ---- CPU baseline: the oracle on a bounded sample ----------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(lins, W, M, Q, X, args.cpu_rows_fraction)
+
+    line = {
+        "metric": METRIC,
+        "value": round(n_weights / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "Gweights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{ws.name}: {n_weights} BF16 weights; per step tensor_scale + quantize "
+                        f"(codes, E4M3 scales, BF16 w') + dequantize for every linear, and per-token "
+                        f"activations X [8192, 4096]",
+            "weights": n_weights,
+            "linears": nlin,
+            "m": "LogNormal(0, 0.1)", "q": "N(6, 2)", "W": "N(0, %g) + 0.1%% outliers x20" % ws.std,
+        },
+        "roofline": {
+            "kernel": "focus_quantize (codes + scales + w')",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(),
+            "bytes_per_weight": B_QUANT_DQ,
+            "mean_launch_ms": round(mean_launch_ms, 5),
+            "launches": len(q_launch_ms),
+            "launches_per_step": nq,
+        },
+        "cpu_baseline": cpu,
+        "rows": rows,
+        "wall_s_timed": round(wall, 3),
+        "gpu_ms_timed": round(gpu_ms, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(lins, W, M, Q, X, frac):
+    """The oracle, unchanged, on layer 0 of the set: s2 of each full tensor,
+    then quantize (+ w') and dequantize of the first `frac` of its rows, and
+    per-token activations of the first 512 tokens; row chunks run on the
+    host's cores through ctypes (which releases the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+    import synth
+
+    o = oracle.default()
+    try:
+        n_thr = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n_thr = os.cpu_count() or 1
+    n_thr = max(1, min(n_thr, 64))
+    layer0 = [i for i, l in enumerate(lins) if l.layer == 0]
+    host = []
+    for i in layer0:
+        wb = synth.bits(W[i])
+        r = max(1, int(lins[i].rows * frac))
+        host.append((wb, M[i][:r].cpu().numpy(), Q[i][:r].cpu().numpy(), r))
+    xb = synth.bits(X[:512])
+    weights = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(n_thr) as ex:
+        for wb, m, q, r in host:
+            s2, _ = o.tensor_scale(wb)
+            bounds = np.linspace(0, r, n_thr + 1).astype(int)
+
+            def work(k, wb=wb, m=m, q=q, s2=s2, bounds=bounds):
+                a, b = bounds[k], bounds[k + 1]
+                if b <= a:
+                    return 0
+                codes, scales, _ = o.quantize(wb[a:b], m[a:b], q[a:b], s2, True)
+                o.dequantize(codes, scales, s2)
+                return (b - a) * wb.shape[1]
+
+            weights += sum(ex.map(work, range(n_thr)))
+        tb = np.linspace(0, xb.shape[0], n_thr + 1).astype(int)
+        list(ex.map(lambda k: o.quantize_act_per_token(xb[tb[k]:tb[k + 1]]), range(n_thr)))
+    dt = time.perf_counter() - t0
+    return {"value": round(weights / dt / 1e9, 5), "unit": "Gweights/s", "cores": n_thr,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"layer 0 of the set: full-tensor s2, then quantize (+w') and dequantize of the "
+                      f"first {frac:g} of the rows of its 7 linears ({weights} weights), and per-token "
+                      f"activations of 512 x 4096"}
+
+
+if __name__ == "__main__":
+    main()

@@ -15,6 +15,10 @@ Calls (same names as the C ABI, without the ``focus_`` prefix):
 * ``dequantize(codes, scales, s2)`` -> BF16 tensor
 * ``quantize_act_per_token(x, dequant=False)``
   -> ``Quantized(codes, scales, x_deq, s2 [tokens])``
+* ``tensor_scale_many``, ``quantize_many``, ``dequantize_many``: the batched
+  calls (one launch per run of up to 32 tensors).  Each returns a ``Batch``
+  whose descriptor array is built once; calling it again re-launches the same
+  work on the current stream without rebuilding anything.
 
 BF16 inputs are ``torch.bfloat16`` tensors; codes and scales are ``uint8``
 ([rows, cols/2] with element 2j in the low nibble, and [rows, cols/16] E4M3
@@ -30,6 +34,7 @@ from . import _lib
 from ._lib import FocusError, FocusLibraryMissing, library_path  # noqa: F401
 
 __all__ = ["tensor_scale", "quantize", "dequantize", "quantize_act_per_token", "Quantized",
+           "tensor_scale_many", "quantize_many", "dequantize_many", "Batch",
            "FocusError", "FocusLibraryMissing", "abi_version", "library_path"]
 
 
@@ -167,3 +172,119 @@ def quantize_act_per_token(x: torch.Tensor, dequant: bool = False,
     _lib.check(_lib.lib().focus_quantize_act_per_token(_p(x), t, h, _p(codes), _p(scales), _p(s2),
                                                        _p(deq), _stream(x)))
     return Quantized(codes, scales, deq, s2)
+
+
+# ---------------------------------------------------------------------------
+# batched calls
+# ---------------------------------------------------------------------------
+
+class Batch:
+    """A prepared batched call: the descriptor array is built once (device
+    pointers of the given tensors, which must stay alive), and ``run()``
+    launches it on the current stream of ``device``."""
+
+    def __init__(self, fn_name: str, descs, keep, device):
+        self._fn = getattr(_lib.lib(), fn_name)
+        self._descs = descs
+        self._n = len(descs)
+        self._keep = keep  # keep the tensors alive while the batch exists
+        self.device = device
+
+    def run(self):
+        if self._n:
+            _lib.check(self._fn(self._descs, self._n, torch.cuda.current_stream(self.device).cuda_stream))
+        return self
+
+    __call__ = run
+
+
+def tensor_scale_many(ws, s2_out=None, amax_out=None, run: bool = True) -> Batch:
+    """Tensor scales of several BF16 tensors.  s2_out / amax_out: FP32 tensors
+    with one element per input (e.g. an [n, 1] tensor), allocated if None."""
+    n = len(ws)
+    if n == 0:
+        raise ValueError("no tensors")
+    dev = ws[0].device
+    for i, w in enumerate(ws):
+        _check_dev(f"ws[{i}]", w, torch.bfloat16, dev)
+    if s2_out is None:
+        s2_out = torch.empty((n, 1), dtype=torch.float32, device=dev)
+    if amax_out is None:
+        amax_out = torch.empty((n, 1), dtype=torch.float32, device=dev)
+    _check_dev("s2_out", s2_out, torch.float32, dev)
+    _check_dev("amax_out", amax_out, torch.float32, dev)
+    if s2_out.numel() < n or amax_out.numel() < n:
+        raise ValueError("s2_out / amax_out need one element per tensor")
+    arr = (_lib.ScaleDesc * n)()
+    s2f, amf = s2_out.view(-1), amax_out.view(-1)
+    for i, w in enumerate(ws):
+        arr[i] = _lib.ScaleDesc(_p(w), w.numel(), s2f[i].data_ptr(), amf[i].data_ptr())
+    b = Batch("focus_tensor_scale_many", arr, (list(ws), s2_out, amax_out), dev)
+    b.s2, b.amax = s2_out, amax_out
+    return b.run() if run else b
+
+
+def quantize_many(ws, ms, qs, s2s, outs=None, dequant: bool = True, run: bool = True) -> Batch:
+    """FOCUS quantizer over several linears in as few launches as possible.
+    ms / qs: lists (entries may be None); s2s: one-element FP32 tensors (for
+    example the rows of ``tensor_scale_many(...).s2``); outs: list of
+    ``Quantized`` output buffers, allocated if None.  The result's ``outs``
+    holds the outputs."""
+    n = len(ws)
+    if not (len(ms) == len(qs) == len(s2s) == n):
+        raise ValueError("ws, ms, qs, s2s must have the same length")
+    dev = ws[0].device
+    arr = (_lib.QuantDesc * n)()
+    res = []
+    for i in range(n):
+        w, m, q, s2 = ws[i], ms[i], qs[i], s2s[i]
+        _check_dev(f"ws[{i}]", w, torch.bfloat16, dev)
+        rows, cols = w.shape
+        if m is not None:
+            _check_dev(f"ms[{i}]", m, torch.float32, dev)
+            assert tuple(m.shape) == (rows, cols // 16)
+        if q is not None:
+            _check_dev(f"qs[{i}]", q, torch.float32, dev)
+            assert tuple(q.shape) == (rows, cols // 8)
+        _check_dev(f"s2s[{i}]", s2, torch.float32, dev)
+        if outs is None:
+            o = Quantized(torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+                          torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
+                          torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) if dequant else None,
+                          s2)
+        else:
+            o = outs[i]
+            if o.codes.numel() != rows * cols // 2 or o.scales.numel() != rows * cols // 16:
+                raise ValueError(f"outs[{i}] has the wrong size")
+        deq = o.deq if dequant else None
+        res.append(Quantized(o.codes, o.scales, deq, s2))
+        arr[i] = _lib.QuantDesc(_p(w), rows, cols, _p(m), _p(q), _p(s2), _p(o.codes), _p(o.scales),
+                                _p(deq))
+    b = Batch("focus_quantize_many", arr, (list(ws), list(ms), list(qs), list(s2s), res), dev)
+    b.outs = res
+    return b.run() if run else b
+
+
+def dequantize_many(codes, scales, s2s, outs=None, s2_per_row=None, run: bool = True) -> Batch:
+    """Dequantize several stored tensors; the result's ``outs`` holds them."""
+    n = len(codes)
+    dev = codes[0].device
+    arr = (_lib.DequantDesc * n)()
+    res = []
+    for i in range(n):
+        c, s, s2 = codes[i], scales[i], s2s[i]
+        _check_dev(f"codes[{i}]", c, torch.uint8, dev)
+        _check_dev(f"scales[{i}]", s, torch.uint8, dev)
+        _check_dev(f"s2s[{i}]", s2, torch.float32, dev)
+        rows, half = c.shape
+        cols = 2 * half
+        pr = bool(s2_per_row[i]) if s2_per_row is not None else False
+        if s2.numel() < (rows if pr else 1):
+            raise ValueError(f"s2s[{i}] too small")
+        o = outs[i] if outs is not None else torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+        _check_dev(f"outs[{i}]", o, torch.bfloat16, dev)
+        res.append(o)
+        arr[i] = _lib.DequantDesc(_p(c), _p(s), _p(s2), 1 if pr else 0, rows, cols, _p(o))
+    b = Batch("focus_dequantize_many", arr, (list(codes), list(scales), list(s2s), res), dev)
+    b.outs = res
+    return b.run() if run else b

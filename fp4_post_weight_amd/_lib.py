@@ -16,6 +16,20 @@ _VP = ct.c_void_p
 _I64 = ct.c_int64
 _INT = ct.c_int
 
+class ScaleDesc(ct.Structure):
+    _fields_ = [("w_bf16", _VP), ("numel", _I64), ("s2_out", _VP), ("amax_out", _VP)]
+
+
+class QuantDesc(ct.Structure):
+    _fields_ = [("w_bf16", _VP), ("rows", _I64), ("cols", _I64), ("m", _VP), ("q", _VP),
+                ("s2", _VP), ("codes", _VP), ("scales", _VP), ("w_deq", _VP)]
+
+
+class DequantDesc(ct.Structure):
+    _fields_ = [("codes", _VP), ("scales", _VP), ("s2", _VP), ("s2_per_row", _INT),
+                ("rows", _I64), ("cols", _I64), ("out", _VP)]
+
+
 _SIGNATURES = {
     "focus_abi_version": (_INT, []),
     "focus_status_string": (ct.c_char_p, [_INT]),
@@ -23,6 +37,9 @@ _SIGNATURES = {
     "focus_quantize": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "focus_dequantize": (_INT, [_VP, _VP, _VP, _INT, _I64, _I64, _VP, _VP]),
     "focus_quantize_act_per_token": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
+    "focus_tensor_scale_many": (_INT, [ct.POINTER(ScaleDesc), _INT, _VP]),
+    "focus_quantize_many": (_INT, [ct.POINTER(QuantDesc), _INT, _VP]),
+    "focus_dequantize_many": (_INT, [ct.POINTER(DequantDesc), _INT, _VP]),
 }
 
 EXPORTED = tuple(_SIGNATURES)

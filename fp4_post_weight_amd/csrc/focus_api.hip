@@ -1,18 +1,21 @@
 // focus_api.hip -- the extern "C" boundary of libfocus_nvfp4.
 //
-// Every entry point validates its arguments on the host before the first
-// HIP call (so every error path runs without a GPU), then launches the
-// kernels of focus_kernels.hip on the caller's stream.  Nothing is
-// allocated and no state is kept.  The declarations, with the meaning,
-// layout and ownership of each argument, are in include/focus_nvfp4.h.
+// Every entry point validates all of its arguments on the host before the
+// first HIP call (so every error path runs without a GPU), then launches the
+// kernels of focus_kernels.hip on the caller's stream.  Nothing is allocated
+// and no state is kept.  Batched calls read their descriptor arrays during
+// the call only and launch one kernel (one per phase for the tensor scale)
+// per run of up to focus::kBatch tensors.  The declarations, with the
+// meaning, layout and ownership of each argument, are in
+// include/focus_nvfp4.h.
 
 #include "focus_nvfp4.h"
 #include "focus_internal.h"
 
 namespace {
 
-// Sizes are bounded so that every byte offset (elements * 2) fits int64
-// and every grid stays within HIP's limits.
+// Sizes are bounded so that every byte offset (elements * 2) fits int64 and
+// every grid stays within HIP's limits.
 constexpr int64_t kMaxElems = (int64_t)1 << 60;
 constexpr int64_t kMaxTokens = (int64_t)1 << 31;
 
@@ -26,6 +29,115 @@ inline int shape_2d(int64_t rows, int64_t cols) {
 }
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? FOCUS_OK : FOCUS_ERR_HIP; }
+
+int check_quant(const focus_quant_desc& d) {
+    int st = shape_2d(d.rows, d.cols);
+    if (st != FOCUS_OK) return st;
+    if (d.rows == 0 || d.cols == 0) return FOCUS_OK;
+    if (!d.w_bf16 || !d.s2 || !d.codes || !d.scales) return FOCUS_ERR_NULL;
+    if (!aligned(d.w_bf16, 16) || !aligned(d.m, 4) || !aligned(d.q, 8) || !aligned(d.s2, 4) ||
+        !aligned(d.codes, 8) || !aligned(d.w_deq, 16))
+        return FOCUS_ERR_ALIGN;
+    return FOCUS_OK;
+}
+
+int check_dequant(const focus_dequant_desc& d) {
+    int st = shape_2d(d.rows, d.cols);
+    if (st != FOCUS_OK) return st;
+    if (d.s2_per_row != 0 && d.s2_per_row != 1) return FOCUS_ERR_RANGE;
+    if (d.rows == 0 || d.cols == 0) return FOCUS_OK;
+    if (!d.codes || !d.scales || !d.s2 || !d.out) return FOCUS_ERR_NULL;
+    if (!aligned(d.codes, 8) || !aligned(d.s2, 4) || !aligned(d.out, 16)) return FOCUS_ERR_ALIGN;
+    return FOCUS_OK;
+}
+
+int check_scale(const focus_scale_desc& d) {
+    if (!d.s2_out || (d.numel > 0 && !d.w_bf16)) return FOCUS_ERR_NULL;
+    if (d.numel < 0 || d.numel > kMaxElems) return FOCUS_ERR_SHAPE;
+    if (!aligned(d.w_bf16, 16) || !aligned(d.s2_out, 4) || !aligned(d.amax_out, 4))
+        return FOCUS_ERR_ALIGN;
+    return FOCUS_OK;
+}
+
+int quant_key(const focus_quant_desc& d) {
+    return (d.m ? 4 : 0) | (d.q ? 2 : 0) | (d.w_deq ? 1 : 0);
+}
+
+int run_quantize(const focus_quant_desc* descs, int n, hipStream_t stream) {
+    focus::QuantBatch bt;
+    int key = -1;
+    bt.n = 0;
+    for (int i = 0; i <= n; ++i) {
+        const bool end = (i == n);
+        const bool skip = !end && (descs[i].rows == 0 || descs[i].cols == 0);
+        if (skip) continue;
+        const int k = end ? -1 : quant_key(descs[i]);
+        if (bt.n > 0 && (end || k != key || bt.n == focus::kBatch)) {
+            int st = hip_status(focus::launch_quantize(bt, key, stream));
+            if (st != FOCUS_OK) return st;
+            bt.n = 0;
+        }
+        if (end) break;
+        const focus_quant_desc& d = descs[i];
+        key = k;
+        const int j = bt.n++;
+        bt.w[j] = reinterpret_cast<const uint4*>(d.w_bf16);
+        bt.m[j] = d.m;
+        bt.q[j] = reinterpret_cast<const float2*>(d.q);
+        bt.s2[j] = d.s2;
+        bt.codes[j] = reinterpret_cast<uint2*>(d.codes);
+        bt.scales[j] = d.scales;
+        bt.wdeq[j] = reinterpret_cast<uint4*>(d.w_deq);
+        bt.nblk[j] = d.rows * (d.cols / 16);
+    }
+    return FOCUS_OK;
+}
+
+int run_dequantize(const focus_dequant_desc* descs, int n, hipStream_t stream) {
+    focus::DequantBatch bt;
+    bt.n = 0;
+    for (int i = 0; i <= n; ++i) {
+        const bool end = (i == n);
+        if (!end && (descs[i].rows == 0 || descs[i].cols == 0)) continue;
+        if (bt.n > 0 && (end || bt.n == focus::kBatch)) {
+            int st = hip_status(focus::launch_dequantize(bt, stream));
+            if (st != FOCUS_OK) return st;
+            bt.n = 0;
+        }
+        if (end) break;
+        const focus_dequant_desc& d = descs[i];
+        const int j = bt.n++;
+        bt.codes[j] = reinterpret_cast<const uint2*>(d.codes);
+        bt.scales[j] = d.scales;
+        bt.s2[j] = d.s2;
+        bt.out[j] = reinterpret_cast<uint4*>(d.out);
+        bt.nb_row[j] = d.cols / 16;
+        bt.nblk[j] = d.rows * (d.cols / 16);
+        bt.per_row[j] = d.s2_per_row;
+    }
+    return FOCUS_OK;
+}
+
+int run_tensor_scale(const focus_scale_desc* descs, int n, hipStream_t stream) {
+    focus::ScaleBatch bt;
+    bt.n = 0;
+    for (int i = 0; i <= n; ++i) {
+        const bool end = (i == n);
+        if (bt.n > 0 && (end || bt.n == focus::kBatch)) {
+            int st = hip_status(focus::launch_tensor_scale(bt, stream));
+            if (st != FOCUS_OK) return st;
+            bt.n = 0;
+        }
+        if (end) break;
+        const focus_scale_desc& d = descs[i];
+        const int j = bt.n++;
+        bt.w[j] = d.w_bf16;
+        bt.s2[j] = d.s2_out;
+        bt.amax[j] = d.amax_out;
+        bt.numel[j] = d.numel;
+    }
+    return FOCUS_OK;
+}
 
 }  // namespace
 
@@ -47,37 +159,57 @@ const char* focus_status_string(int status) {
 
 int focus_tensor_scale(const uint16_t* w_bf16, int64_t numel, float* s2_out, float* amax_out,
                        void* stream) {
-    if (!s2_out || (numel > 0 && !w_bf16)) return FOCUS_ERR_NULL;
-    if (numel < 0 || numel > kMaxElems) return FOCUS_ERR_SHAPE;
-    if (!aligned(w_bf16, 16) || !aligned(s2_out, 4) || !aligned(amax_out, 4)) return FOCUS_ERR_ALIGN;
-    return hip_status(focus::launch_tensor_scale(w_bf16, numel, s2_out, amax_out,
-                                                 (hipStream_t)stream));
+    const focus_scale_desc d = {w_bf16, numel, s2_out, amax_out};
+    int st = check_scale(d);
+    if (st != FOCUS_OK) return st;
+    return run_tensor_scale(&d, 1, (hipStream_t)stream);
+}
+
+int focus_tensor_scale_many(const focus_scale_desc* descs, int n, void* stream) {
+    if (n < 0) return FOCUS_ERR_RANGE;
+    if (n > 0 && !descs) return FOCUS_ERR_NULL;
+    for (int i = 0; i < n; ++i) {
+        int st = check_scale(descs[i]);
+        if (st != FOCUS_OK) return st;
+    }
+    return run_tensor_scale(descs, n, (hipStream_t)stream);
 }
 
 int focus_quantize(const uint16_t* w_bf16, int64_t rows, int64_t cols, const float* m,
                    const float* q, const float* s2, uint8_t* codes, uint8_t* scales,
                    uint16_t* w_deq, void* stream) {
-    int st = shape_2d(rows, cols);
+    const focus_quant_desc d = {w_bf16, rows, cols, m, q, s2, codes, scales, w_deq};
+    int st = check_quant(d);
     if (st != FOCUS_OK) return st;
-    if (rows == 0 || cols == 0) return FOCUS_OK;
-    if (!w_bf16 || !s2 || !codes || !scales) return FOCUS_ERR_NULL;
-    if (!aligned(w_bf16, 16) || !aligned(m, 4) || !aligned(q, 8) || !aligned(s2, 4) ||
-        !aligned(codes, 8) || !aligned(w_deq, 16))
-        return FOCUS_ERR_ALIGN;
-    return hip_status(focus::launch_quantize(w_bf16, rows, cols, m, q, s2, codes, scales, w_deq,
-                                             (hipStream_t)stream));
+    return run_quantize(&d, 1, (hipStream_t)stream);
+}
+
+int focus_quantize_many(const focus_quant_desc* descs, int n, void* stream) {
+    if (n < 0) return FOCUS_ERR_RANGE;
+    if (n > 0 && !descs) return FOCUS_ERR_NULL;
+    for (int i = 0; i < n; ++i) {
+        int st = check_quant(descs[i]);
+        if (st != FOCUS_OK) return st;
+    }
+    return run_quantize(descs, n, (hipStream_t)stream);
 }
 
 int focus_dequantize(const uint8_t* codes, const uint8_t* scales, const float* s2, int s2_per_row,
                      int64_t rows, int64_t cols, uint16_t* out, void* stream) {
-    int st = shape_2d(rows, cols);
+    const focus_dequant_desc d = {codes, scales, s2, s2_per_row, rows, cols, out};
+    int st = check_dequant(d);
     if (st != FOCUS_OK) return st;
-    if (s2_per_row != 0 && s2_per_row != 1) return FOCUS_ERR_RANGE;
-    if (rows == 0 || cols == 0) return FOCUS_OK;
-    if (!codes || !scales || !s2 || !out) return FOCUS_ERR_NULL;
-    if (!aligned(codes, 8) || !aligned(s2, 4) || !aligned(out, 16)) return FOCUS_ERR_ALIGN;
-    return hip_status(focus::launch_dequantize(codes, scales, s2, s2_per_row, rows, cols, out,
-                                               (hipStream_t)stream));
+    return run_dequantize(&d, 1, (hipStream_t)stream);
+}
+
+int focus_dequantize_many(const focus_dequant_desc* descs, int n, void* stream) {
+    if (n < 0) return FOCUS_ERR_RANGE;
+    if (n > 0 && !descs) return FOCUS_ERR_NULL;
+    for (int i = 0; i < n; ++i) {
+        int st = check_dequant(descs[i]);
+        if (st != FOCUS_OK) return st;
+    }
+    return run_dequantize(descs, n, (hipStream_t)stream);
 }
 
 int focus_quantize_act_per_token(const uint16_t* x_bf16, int64_t tokens, int64_t hidden,

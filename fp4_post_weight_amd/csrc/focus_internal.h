@@ -1,19 +1,55 @@
-// focus_internal.h -- launchers shared by the kernel file and the C ABI.
-// Arguments reaching these functions have been validated on the host.
+// focus_internal.h -- batch descriptors and launchers shared by the kernel
+// file and the C ABI.  Arguments reaching these functions have been
+// validated on the host.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace focus {
 
-hipError_t launch_tensor_scale(const uint16_t* w, int64_t numel, float* s2_out, float* amax_out,
-                               hipStream_t stream);
-hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t cols, const float* m,
-                           const float* q, const float* s2, uint8_t* codes, uint8_t* scales,
-                           uint16_t* wdeq, hipStream_t stream);
-hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* s2,
-                             int s2_per_row, int64_t rows, int64_t cols, uint16_t* out,
-                             hipStream_t stream);
+// Tensors per launch.  A batch travels by value in the kernel argument
+// segment (structure of arrays, at most about 2.3 KB).
+constexpr int kBatch = 32;
+
+struct QuantBatch {
+    const uint4* w[kBatch];
+    const float* m[kBatch];
+    const float2* q[kBatch];
+    const float* s2[kBatch];
+    uint2* codes[kBatch];
+    uint8_t* scales[kBatch];
+    uint4* wdeq[kBatch];
+    int64_t nblk[kBatch];
+    int64_t tile_start[kBatch + 1];
+    int n;
+};
+
+struct DequantBatch {
+    const uint2* codes[kBatch];
+    const uint8_t* scales[kBatch];
+    const float* s2[kBatch];
+    uint4* out[kBatch];
+    int64_t nblk[kBatch];
+    int64_t nb_row[kBatch];
+    int64_t tile_start[kBatch + 1];
+    int32_t per_row[kBatch];
+    int n;
+};
+
+struct ScaleBatch {
+    const uint16_t* w[kBatch];
+    float* s2[kBatch];
+    float* amax[kBatch];
+    int64_t numel[kBatch];
+    int64_t tile_start[kBatch + 1];
+    int n;
+};
+
+// key: bit 2 = m present, bit 1 = q present, bit 0 = w' written; every
+// tensor of one batch shares the key.
+hipError_t launch_quantize(QuantBatch& bt, int key, hipStream_t stream);
+hipError_t launch_dequantize(DequantBatch& bt, hipStream_t stream);
+hipError_t launch_tensor_scale(ScaleBatch& bt, hipStream_t stream);
 hipError_t launch_act_per_token(const uint16_t* x, int64_t tokens, int64_t hidden, uint8_t* codes,
                                 uint8_t* scales, float* s2_out, uint16_t* xdeq,
                                 hipStream_t stream);

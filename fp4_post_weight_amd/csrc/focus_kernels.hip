@@ -17,7 +17,8 @@
 //    wavefront streams 2 KB of contiguous weights; m (4 B/lane) and q
 //    (8 B/lane) are read coalesced beside it; codes leave as 8 B/lane and
 //    w' as two 16-byte stores.  No LDS is needed: nothing is shared.
-//  * Block maximum: binary32 max of |w| (exact).
+//  * Block maximum: integer maximum of the BF16 magnitude bits (exact; the
+//    bit patterns of non-negative floats order like their values).
 //  * t and sigmoid use IEEE binary32 division (the compiler's correctly
 //    rounded sequence).  expf is evaluated as the binary64 exp rounded once
 //    to binary32, which is the correctly rounded binary32 exponential except
@@ -133,6 +134,25 @@ __device__ __forceinline__ uint4 dequant8(uint32_t codes, float S, float s2) {
     return o;
 }
 
+// Block maximum of 16 BF16 values as a binary32: integer maximum of the
+// magnitude bits (exact, and cheaper than a float max that must quiet NaNs).
+__device__ __forceinline__ float block_amax_bits(uint4 a, uint4 b) {
+    const uint32_t mask = 0x7FFF7FFFu;
+    u16x2 m0 = __builtin_bit_cast(u16x2, a.x & mask);
+    u16x2 m1 = __builtin_bit_cast(u16x2, a.y & mask);
+    u16x2 m2 = __builtin_bit_cast(u16x2, a.z & mask);
+    u16x2 m3 = __builtin_bit_cast(u16x2, a.w & mask);
+    u16x2 m4 = __builtin_bit_cast(u16x2, b.x & mask);
+    u16x2 m5 = __builtin_bit_cast(u16x2, b.y & mask);
+    u16x2 m6 = __builtin_bit_cast(u16x2, b.z & mask);
+    u16x2 m7 = __builtin_bit_cast(u16x2, b.w & mask);
+    m0 = __builtin_elementwise_max(__builtin_elementwise_max(m0, m1), __builtin_elementwise_max(m2, m3));
+    m4 = __builtin_elementwise_max(__builtin_elementwise_max(m4, m5), __builtin_elementwise_max(m6, m7));
+    m0 = __builtin_elementwise_max(m0, m4);
+    const uint32_t mx = max((uint32_t)m0[0], (uint32_t)m0[1]);
+    return __uint_as_float(mx << 16);
+}
+
 // Codes of 8 elements f[0..7] for the denominator d of their sub-block.
 __device__ __forceinline__ uint32_t encode8(const float* f, float d) {
     float x[8];
@@ -183,9 +203,7 @@ __device__ __forceinline__ void quantize_block(uint4 a, uint4 b, float mb, float
         }
         return;
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) amax = fmaxf(amax, fmaxf(fabsf(f[i]), fabsf(f[i + 1])));
+    const float amax = block_amax_bits(a, b);
     const uint32_t sb = e4m3_byte_normal(block_t(amax, mb, den));
     const float S = e4m3_normal_value(sb);
     float sig0 = 1.0f, sig1 = 1.0f;
@@ -206,52 +224,103 @@ __device__ __forceinline__ void quantize_block(uint4 a, uint4 b, float mb, float
 }
 
 // ---------------------------------------------------------------------------
-// focus_quantize: one lane per 16-element block, grid-stride over blocks
+// batches: up to kBatch tensors per launch, described in the kernel argument
+// segment (structure of arrays, about 2.3 KB).  Work is cut into tiles of
+// kThreads * U blocks; tile_start[j] is the first tile of tensor j, so a
+// workgroup finds its tensor by a binary search over scalar loads.
 // ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int find_tensor(const int64_t* tile_start, int n, int64_t tile) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tile_start[mid] <= tile) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// ---------------------------------------------------------------------------
+// focus_quantize(_many): one lane per 16-element block, U blocks per lane
+// per tile with all loads issued before any arithmetic
+// ---------------------------------------------------------------------------
+
+constexpr int kQuantU = 2;
+constexpr int64_t kQuantTile = (int64_t)kThreads * kQuantU;
 
 template <bool HAS_M, bool HAS_Q, bool DEQ>
-__global__ __launch_bounds__(kThreads) void k_quantize(
-    const uint4* __restrict__ w, const float* __restrict__ m, const float2* __restrict__ q,
-    const float* __restrict__ s2p, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
-    uint4* __restrict__ wdeq, int64_t nblk) {
-    const float s2 = *s2p;
-    const float den = 6.0f * s2;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblk; blk += stride) {
-        const uint4 a = w[2 * blk];
-        const uint4 b = w[2 * blk + 1];
-        const float mb = HAS_M ? m[blk] : 1.0f;
-        float2 qq = make_float2(0.0f, 0.0f);
-        if (HAS_Q) qq = q[blk];
-        quantize_block<HAS_Q, DEQ>(a, b, mb, qq.x, qq.y, s2, den, codes + blk, scales + blk,
-                                   DEQ ? wdeq + 2 * blk : nullptr);
+__global__ __launch_bounds__(kThreads) void k_quantize(QuantBatch bt, int64_t ntiles) {
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int j = find_tensor(bt.tile_start, bt.n, tile);
+        const uint4* __restrict__ w = bt.w[j];
+        const float* __restrict__ m = bt.m[j];
+        const float2* __restrict__ q = bt.q[j];
+        const float s2 = *bt.s2[j];
+        const float den = 6.0f * s2;
+        const int64_t nblk = bt.nblk[j];
+        const int64_t base = (tile - bt.tile_start[j]) * kQuantTile + threadIdx.x;
+        uint4 va[kQuantU], vb[kQuantU];
+        float mb[kQuantU];
+        float2 qq[kQuantU];
+#pragma unroll
+        for (int k = 0; k < kQuantU; ++k) {
+            const int64_t blk = base + (int64_t)k * kThreads;
+            if (blk < nblk) {
+                va[k] = w[2 * blk];
+                vb[k] = w[2 * blk + 1];
+                mb[k] = HAS_M ? m[blk] : 1.0f;
+                qq[k] = HAS_Q ? q[blk] : make_float2(0.0f, 0.0f);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kQuantU; ++k) {
+            const int64_t blk = base + (int64_t)k * kThreads;
+            if (blk < nblk)
+                quantize_block<HAS_Q, DEQ>(va[k], vb[k], mb[k], qq[k].x, qq[k].y, s2, den,
+                                           bt.codes[j] + blk, bt.scales[j] + blk,
+                                           DEQ ? bt.wdeq[j] + 2 * blk : nullptr);
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
-// focus_dequantize: one lane per block
+// focus_dequantize(_many): one lane per block
 // ---------------------------------------------------------------------------
 
-template <bool PER_ROW>
-__global__ __launch_bounds__(kThreads) void k_dequantize(
-    const uint2* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const float* __restrict__ s2p, int64_t nblk, int64_t nb_row, uint4* __restrict__ out) {
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    const float s2u = PER_ROW ? 0.0f : *s2p;
-    for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblk; blk += stride) {
-        const uint2 c = codes[blk];
-        const float S = e4m3_any_value(scales[blk]);
-        const float s2 = PER_ROW ? s2p[blk / nb_row] : s2u;
-        out[2 * blk] = dequant8(c.x, S, s2);
-        out[2 * blk + 1] = dequant8(c.y, S, s2);
+constexpr int64_t kDeqTile = (int64_t)kThreads * 2;
+
+__global__ __launch_bounds__(kThreads) void k_dequantize(DequantBatch bt, int64_t ntiles) {
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int j = find_tensor(bt.tile_start, bt.n, tile);
+        const uint2* __restrict__ codes = bt.codes[j];
+        const uint8_t* __restrict__ scales = bt.scales[j];
+        const float* __restrict__ s2p = bt.s2[j];
+        const int64_t nblk = bt.nblk[j], nb_row = bt.nb_row[j];
+        const bool per_row = bt.per_row[j] != 0;
+        const int64_t base = (tile - bt.tile_start[j]) * kDeqTile + threadIdx.x;
+        const float s2u = per_row ? 0.0f : *s2p;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int64_t blk = base + (int64_t)k * kThreads;
+            if (blk < nblk) {
+                const uint2 c = codes[blk];
+                const float S = e4m3_any_value(scales[blk]);
+                const float s2 = per_row ? s2p[blk / nb_row] : s2u;
+                bt.out[j][2 * blk] = dequant8(c.x, S, s2);
+                bt.out[j][2 * blk + 1] = dequant8(c.y, S, s2);
+            }
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
-// focus_tensor_scale: clear, reduce (max of BF16 magnitude bits), finalize
+// focus_tensor_scale(_many): clear, reduce (max of BF16 magnitude bits),
+// finalize
 // ---------------------------------------------------------------------------
 
-__global__ void k_fill_u32(uint32_t* p, uint32_t v) { *p = v; }
+__global__ void k_clear_acc(ScaleBatch bt) {
+    if ((int)threadIdx.x < bt.n) *reinterpret_cast<uint32_t*>(bt.s2[threadIdx.x]) = 0u;
+}
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
@@ -259,42 +328,65 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
-// acc: the bits of a non-negative binary32 (the BF16 magnitude shifted up),
-// combined with an integer atomic max, which orders such floats exactly.
-__global__ __launch_bounds__(kThreads) void k_amax(const uint4* __restrict__ w, int64_t nvec,
-                                                   const uint16_t* __restrict__ tail, int ntail,
-                                                   uint32_t* __restrict__ acc) {
-    u16x2 mx = {0, 0};
-    const uint32_t mask = 0x7FFF7FFFu;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride) {
-        const uint4 v = w[i];
-        u16x2 a = __builtin_bit_cast(u16x2, v.x & mask);
-        u16x2 b = __builtin_bit_cast(u16x2, v.y & mask);
-        u16x2 c = __builtin_bit_cast(u16x2, v.z & mask);
-        u16x2 d = __builtin_bit_cast(u16x2, v.w & mask);
-        mx = __builtin_elementwise_max(mx, __builtin_elementwise_max(__builtin_elementwise_max(a, b),
-                                                                     __builtin_elementwise_max(c, d)));
-    }
-    uint32_t m = max((uint32_t)mx[0], (uint32_t)mx[1]);
-    if (blockIdx.x == 0 && (int)threadIdx.x < ntail) m = max(m, (uint32_t)(tail[threadIdx.x] & 0x7FFFu));
-    m = wave_max_u32(m);
+constexpr int kAmaxVecPerThread = 8;  // 8 x 16 B per lane per tile
+constexpr int64_t kAmaxTile = (int64_t)kThreads * kAmaxVecPerThread;  // in 16-byte vectors
+
+// The accumulator is the s2 slot itself, holding the bits of a non-negative
+// binary32 (the BF16 magnitude shifted up); an integer atomic max orders such
+// floats exactly.  Each tile covers kAmaxTile 16-byte vectors of one tensor;
+// the last partial vector of a tensor is read element by element.
+__global__ __launch_bounds__(kThreads) void k_amax(ScaleBatch bt, int64_t ntiles) {
     __shared__ uint32_t part[kThreads / 64];
-    const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) part[wave] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t r = part[0];
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int j = find_tensor(bt.tile_start, bt.n, tile);
+        const uint16_t* __restrict__ w16 = bt.w[j];
+        const uint4* __restrict__ w = reinterpret_cast<const uint4*>(w16);
+        const int64_t numel = bt.numel[j];
+        const int64_t nvec = numel / 8;
+        const int64_t base = (tile - bt.tile_start[j]) * kAmaxTile + threadIdx.x;
+        u16x2 mx = {0, 0};
+        const uint32_t mask = 0x7FFF7FFFu;
+        uint4 v[kAmaxVecPerThread];
 #pragma unroll
-        for (int k = 1; k < kThreads / 64; ++k) r = max(r, part[k]);
-        atomicMax(acc, r << 16);
+        for (int k = 0; k < kAmaxVecPerThread; ++k) {
+            const int64_t i = base + (int64_t)k * kThreads;
+            v[k] = i < nvec ? w[i] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < kAmaxVecPerThread; ++k) {
+            u16x2 a = __builtin_bit_cast(u16x2, v[k].x & mask);
+            u16x2 b = __builtin_bit_cast(u16x2, v[k].y & mask);
+            u16x2 c = __builtin_bit_cast(u16x2, v[k].z & mask);
+            u16x2 d = __builtin_bit_cast(u16x2, v[k].w & mask);
+            mx = __builtin_elementwise_max(mx, __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                                                         __builtin_elementwise_max(c, d)));
+        }
+        uint32_t mm = max((uint32_t)mx[0], (uint32_t)mx[1]);
+        // the tail (numel % 8 elements) belongs to the tile holding vector nvec
+        const int64_t tail_vec_tile = nvec / kAmaxTile;
+        if (tile - bt.tile_start[j] == tail_vec_tile && (int)threadIdx.x < (int)(numel - nvec * 8))
+            mm = max(mm, (uint32_t)(w16[nvec * 8 + threadIdx.x] & 0x7FFFu));
+        mm = wave_max_u32(mm);
+        const int wave = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) part[wave] = mm;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t r = part[0];
+#pragma unroll
+            for (int k = 1; k < kThreads / 64; ++k) r = max(r, part[k]);
+            atomicMax(reinterpret_cast<uint32_t*>(bt.s2[j]), r << 16);
+        }
+        __syncthreads();
     }
 }
 
-__global__ void k_finalize_s2(uint32_t* acc_s2, float* amax_out) {
-    const float amax = __uint_as_float(*acc_s2);
-    *reinterpret_cast<float*>(acc_s2) = amax / 2688.0f;
-    if (amax_out) *amax_out = amax;
+__global__ void k_finalize_s2(ScaleBatch bt) {
+    const int j = threadIdx.x;
+    if (j >= bt.n) return;
+    uint32_t* acc = reinterpret_cast<uint32_t*>(bt.s2[j]);
+    const float amax = __uint_as_float(*acc);
+    *bt.s2[j] = amax / 2688.0f;
+    if (bt.amax[j]) *bt.amax[j] = amax;
 }
 
 // ---------------------------------------------------------------------------
@@ -304,14 +396,6 @@ __global__ void k_finalize_s2(uint32_t* acc_s2, float* amax_out) {
 __device__ __forceinline__ float wave_max_f32(float v) {
     // non-negative binary32: integer order equals value order
     return __uint_as_float(wave_max_u32(__float_as_uint(v)));
-}
-
-__device__ __forceinline__ float block_amax(uint4 a, uint4 b) {
-    const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[i])), fabsf(bf16_hi(v[i]))));
-    return m;
 }
 
 // RB > 0: lane keeps up to RB blocks of the row in registers (rows of at most
@@ -337,12 +421,12 @@ __global__ __launch_bounds__(kThreads) void k_act(const uint4* __restrict__ x, i
             if (j < nb) {
                 va[k] = x[2 * (base + j)];
                 vb[k] = x[2 * (base + j) + 1];
-                amax = fmaxf(amax, block_amax(va[k], vb[k]));
+                amax = fmaxf(amax, block_amax_bits(va[k], vb[k]));
             }
         }
     } else {
         for (int64_t j = lane; j < nb; j += 64)
-            amax = fmaxf(amax, block_amax(x[2 * (base + j)], x[2 * (base + j) + 1]));
+            amax = fmaxf(amax, block_amax_bits(x[2 * (base + j)], x[2 * (base + j) + 1]));
     }
     amax = wave_max_f32(amax);
     const float s2 = amax / 2688.0f;
@@ -368,45 +452,38 @@ __global__ __launch_bounds__(kThreads) void k_act(const uint4* __restrict__ x, i
 // launchers (arguments already validated by the C ABI layer)
 // ---------------------------------------------------------------------------
 
-static inline unsigned grid_for(int64_t items) {
-    int64_t g = (items + kThreads - 1) / kThreads;
-    if (g < 1) g = 1;
+static inline unsigned grid_for_tiles(int64_t ntiles) {
+    int64_t g = ntiles < 1 ? 1 : ntiles;
     if (g > kMaxGrid) g = kMaxGrid;
     return (unsigned)g;
 }
 
-hipError_t launch_tensor_scale(const uint16_t* w, int64_t numel, float* s2_out, float* amax_out,
-                               hipStream_t stream) {
-    uint32_t* acc = reinterpret_cast<uint32_t*>(s2_out);
-    hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(1), 0, stream, acc, 0u);
-    const int64_t nvec = numel / 8;
-    const int ntail = (int)(numel - nvec * 8);
-    if (numel > 0) {
-        int64_t g = (nvec + kThreads - 1) / kThreads;
-        if (g > 2048) g = 2048;
-        if (g < 1) g = 1;
-        hipLaunchKernelGGL(k_amax, dim3((unsigned)g), dim3(kThreads), 0, stream,
-                           reinterpret_cast<const uint4*>(w), nvec, w + nvec * 8, ntail, acc);
+hipError_t launch_tensor_scale(ScaleBatch& bt, hipStream_t stream) {
+    int64_t t = 0;
+    for (int j = 0; j < bt.n; ++j) {
+        bt.tile_start[j] = t;
+        const int64_t nvec = bt.numel[j] / 8;
+        t += nvec / kAmaxTile + 1;  // the +1 tile holds the partial vector tail
     }
-    hipLaunchKernelGGL(k_finalize_s2, dim3(1), dim3(1), 0, stream, acc, amax_out);
+    bt.tile_start[bt.n] = t;
+    hipLaunchKernelGGL(k_clear_acc, dim3(1), dim3(kBatch), 0, stream, bt);
+    hipLaunchKernelGGL(k_amax, dim3(grid_for_tiles(t)), dim3(kThreads), 0, stream, bt, t);
+    hipLaunchKernelGGL(k_finalize_s2, dim3(1), dim3(kBatch), 0, stream, bt);
     return hipGetLastError();
 }
 
-hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t cols, const float* m,
-                           const float* q, const float* s2, uint8_t* codes, uint8_t* scales,
-                           uint16_t* wdeq, hipStream_t stream) {
-    const int64_t nblk = rows * (cols / 16);
-    const dim3 grid(grid_for(nblk)), block(kThreads);
-    auto W = reinterpret_cast<const uint4*>(w);
-    auto Q = reinterpret_cast<const float2*>(q);
-    auto C = reinterpret_cast<uint2*>(codes);
-    auto D = reinterpret_cast<uint4*>(wdeq);
-    const int key = (m ? 4 : 0) | (q ? 2 : 0) | (wdeq ? 1 : 0);
+hipError_t launch_quantize(QuantBatch& bt, int key, hipStream_t stream) {
+    int64_t t = 0;
+    for (int j = 0; j < bt.n; ++j) {
+        bt.tile_start[j] = t;
+        t += (bt.nblk[j] + kQuantTile - 1) / kQuantTile;
+    }
+    bt.tile_start[bt.n] = t;
+    const dim3 grid(grid_for_tiles(t)), block(kThreads);
     switch (key) {
-#define FOCUS_Q_CASE(K, HM, HQ, DQ)                                                             \
-    case K:                                                                                     \
-        hipLaunchKernelGGL((k_quantize<HM, HQ, DQ>), grid, block, 0, stream, W, m, Q, s2, C,   \
-                           scales, D, nblk);                                                    \
+#define FOCUS_Q_CASE(K, HM, HQ, DQ)                                                            \
+    case K:                                                                                    \
+        hipLaunchKernelGGL((k_quantize<HM, HQ, DQ>), grid, block, 0, stream, bt, t);          \
         break;
         FOCUS_Q_CASE(0, false, false, false)
         FOCUS_Q_CASE(1, false, false, true)
@@ -421,17 +498,14 @@ hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t cols, const 
     return hipGetLastError();
 }
 
-hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* s2,
-                             int s2_per_row, int64_t rows, int64_t cols, uint16_t* out,
-                             hipStream_t stream) {
-    const int64_t nb = cols / 16, nblk = rows * nb;
-    const dim3 grid(grid_for(nblk)), block(kThreads);
-    auto C = reinterpret_cast<const uint2*>(codes);
-    auto O = reinterpret_cast<uint4*>(out);
-    if (s2_per_row)
-        hipLaunchKernelGGL(k_dequantize<true>, grid, block, 0, stream, C, scales, s2, nblk, nb, O);
-    else
-        hipLaunchKernelGGL(k_dequantize<false>, grid, block, 0, stream, C, scales, s2, nblk, nb, O);
+hipError_t launch_dequantize(DequantBatch& bt, hipStream_t stream) {
+    int64_t t = 0;
+    for (int j = 0; j < bt.n; ++j) {
+        bt.tile_start[j] = t;
+        t += (bt.nblk[j] + kDeqTile - 1) / kDeqTile;
+    }
+    bt.tile_start[bt.n] = t;
+    hipLaunchKernelGGL(k_dequantize, dim3(grid_for_tiles(t)), dim3(kThreads), 0, stream, bt, t);
     return hipGetLastError();
 }
 

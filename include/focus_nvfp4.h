@@ -131,6 +131,50 @@ int focus_quantize_act_per_token(const uint16_t* x_bf16, int64_t tokens, int64_t
                                  uint8_t* codes, uint8_t* scales, float* s2_out,
                                  uint16_t* x_deq, void* stream);
 
+/*
+ * Batched calls.  A model holds many linears (112, 224 or 560 for the Llama
+ * sets); one launch per tensor leaves the GPU idle between short kernels.
+ * These calls take a HOST array of descriptors (read during the call only,
+ * so it may be freed on return) and launch one kernel per run of up to 32
+ * tensors (three small kernels per run for the tensor scale).  Each
+ * descriptor follows the rules of the matching single call; all descriptors
+ * are validated before anything is launched, and the first invalid one
+ * decides the returned status.  n == 0 is a no-op.  Output buffers of
+ * different descriptors must not overlap.
+ */
+typedef struct focus_scale_desc {
+    const uint16_t* w_bf16;  /* [numel] BF16, 16-byte aligned */
+    int64_t numel;
+    float* s2_out;           /* one float; also the reduction accumulator */
+    float* amax_out;         /* one float or NULL */
+} focus_scale_desc;
+
+int focus_tensor_scale_many(const focus_scale_desc* descs, int n, void* stream);
+
+typedef struct focus_quant_desc {
+    const uint16_t* w_bf16;  /* [rows, cols] BF16 */
+    int64_t rows, cols;
+    const float* m;          /* [rows, cols/16] or NULL */
+    const float* q;          /* [rows, cols/8] or NULL */
+    const float* s2;         /* one float */
+    uint8_t* codes;          /* [rows, cols/2] */
+    uint8_t* scales;         /* [rows, cols/16] */
+    uint16_t* w_deq;         /* [rows, cols] or NULL */
+} focus_quant_desc;
+
+int focus_quantize_many(const focus_quant_desc* descs, int n, void* stream);
+
+typedef struct focus_dequant_desc {
+    const uint8_t* codes;    /* [rows, cols/2] */
+    const uint8_t* scales;   /* [rows, cols/16] */
+    const float* s2;         /* one float, or [rows] when s2_per_row == 1 */
+    int s2_per_row;
+    int64_t rows, cols;
+    uint16_t* out;           /* [rows, cols] BF16 */
+} focus_dequant_desc;
+
+int focus_dequantize_many(const focus_dequant_desc* descs, int n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -129,3 +129,33 @@ def test_product_path_does_not_reach_the_oracle():
         if path.endswith((".py", ".hip", ".h", ".cpp")):
             text = open(path).read()
             assert "oracle" not in text.replace("Oracle", "").lower().replace("no oracle", ""), path
+
+
+def test_batched_validation(lib):
+    QD, SD, DD = _lib.QuantDesc, _lib.ScaleDesc, _lib.DequantDesc
+    assert lib.focus_quantize_many(None, 0, None) == OK
+    assert lib.focus_quantize_many(None, 2, None) == ERR_NULL
+    assert lib.focus_quantize_many((QD * 1)(), -1, None) == ERR_RANGE
+    good = QD(FAKE, 4, 32, None, None, FAKE, FAKE, FAKE, None)
+    bad_shape = QD(FAKE, 4, 24, None, None, FAKE, FAKE, FAKE, None)
+    bad_align = QD(FAKE, 4, 32, None, None, FAKE, FAKE + 4, FAKE, None)
+    empty = QD(None, 0, 32, None, None, None, None, None, None)
+    # every descriptor is checked before anything is launched
+    assert lib.focus_quantize_many((QD * 3)(good, empty, bad_shape), 3, None) == ERR_SHAPE
+    assert lib.focus_quantize_many((QD * 2)(bad_align, good), 2, None) == ERR_ALIGN
+    assert lib.focus_quantize_many((QD * 2)(empty, empty), 2, None) == OK
+    assert lib.focus_tensor_scale_many(None, 1, None) == ERR_NULL
+    assert lib.focus_tensor_scale_many((SD * 2)(SD(FAKE, 8, FAKE, None), SD(FAKE, 8, None, None)), 2,
+                                       None) == ERR_NULL
+    assert lib.focus_tensor_scale_many((SD * 1)(SD(FAKE, -3, FAKE, None)), 1, None) == ERR_SHAPE
+    assert lib.focus_dequantize_many((DD * 1)(DD(FAKE, FAKE, FAKE, 3, 2, 32, FAKE)), 1, None) == ERR_RANGE
+    assert lib.focus_dequantize_many((DD * 1)(DD(FAKE, FAKE, FAKE, 0, 2, 32, FAKE + 2)), 1, None) == ERR_ALIGN
+    assert lib.focus_dequantize_many(None, 0, None) == OK
+
+
+def test_descriptor_layout():
+    """ctypes mirrors of the C descriptor structs (LP64 layout)."""
+    assert ct.sizeof(_lib.QuantDesc) == 9 * 8
+    assert ct.sizeof(_lib.ScaleDesc) == 4 * 8
+    assert ct.sizeof(_lib.DequantDesc) == 7 * 8
+    assert _lib.DequantDesc.rows.offset == 32

@@ -282,3 +282,96 @@ def test_full_size_sampled(focus, orc, ws_name, shape, dequant):
                                 np_bits(res.deq[it]) if dequant else None,
                                 label=f"{ws_name} {shape}")
     print(f"{ws_name} {shape} dequant={dequant}: {st}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# batched calls: identical to the single calls, and to the oracle
+# ---------------------------------------------------------------------------
+
+def _mixed_set(n, seed):
+    rng = np.random.default_rng(seed)
+    shapes = [(int(rng.integers(1, 70)), 16 * int(rng.integers(1, 90))) for _ in range(n)]
+    shapes[3] = (0, 64)          # empty
+    shapes[5] = (300, 4096)      # several tiles
+    items = []
+    for i, (r, c) in enumerate(shapes):
+        w = synth.weights((r, c), seed=seed, tensor_id=4 * i, zero_block_p=0.01).to(DEV)
+        m = synth.block_factor_lognormal((r, c // 16), seed=seed, tensor_id=4 * i + 1).to(DEV) \
+            if i % 3 else None
+        q = synth.logits((r, c // 8), seed=seed, tensor_id=4 * i + 2).to(DEV) if i % 4 else None
+        items.append((w, m, q))
+    return items
+
+
+@pytest.mark.parametrize("n", [1, 7, 32, 33, 70])
+def test_batched_calls_match_single_calls(focus, orc, n):
+    items = _mixed_set(max(n, 6), seed=900 + n)[:n] if n >= 6 else _mixed_set(6, 900 + n)[:n]
+    ws = [w for w, _, _ in items]
+    ts = focus.tensor_scale_many(ws)
+    # alternate the dequant flag to split the batch into several runs
+    deq_flags = [bool(i % 5) for i in range(n)]
+    outs = []
+    for i, (w, m, q) in enumerate(items):
+        r, c = w.shape
+        outs.append(focus.Quantized(torch.empty((r, c // 2), dtype=torch.uint8, device=DEV),
+                                    torch.empty((r, c // 16), dtype=torch.uint8, device=DEV),
+                                    torch.empty((r, c), dtype=torch.bfloat16, device=DEV) if deq_flags[i] else None,
+                                    ts.s2[i]))
+    qb = focus.quantize_many(ws, [m for _, m, _ in items], [q for _, _, q in items],
+                             [ts.s2[i] for i in range(n)], outs=outs, dequant=True)
+    dq = focus.dequantize_many([o.codes for o in qb.outs], [o.scales for o in qb.outs],
+                               [ts.s2[i] for i in range(n)])
+    torch.cuda.synchronize()
+    for i, (w, m, q) in enumerate(items):
+        s2, amax = focus.tensor_scale(w)
+        single = focus.quantize(w, m, q, s2, dequant=deq_flags[i])
+        torch.cuda.synchronize()
+        assert ts.s2[i].item() == s2.item() and ts.amax[i].item() == amax.item()
+        assert torch.equal(qb.outs[i].codes, single.codes), i
+        assert torch.equal(qb.outs[i].scales, single.scales), i
+        if deq_flags[i]:
+            assert torch.equal(qb.outs[i].deq.view(torch.int16), single.deq.view(torch.int16)), i
+            assert torch.equal(dq.outs[i].view(torch.int16), single.deq.view(torch.int16)), i
+        if i < 8 and w.numel():
+            wb = np_bits(w)
+            s2_o, _ = orc.tensor_scale(wb)
+            parity.check_quantized(orc, wb, None if m is None else m.cpu().numpy(),
+                                   None if q is None else q.cpu().numpy(), s2_o,
+                                   single.codes.cpu().numpy(), single.scales.cpu().numpy(),
+                                   np_bits(single.deq) if deq_flags[i] else None, label=f"batch item {i}")
+
+
+def test_tensor_scale_many_sizes(focus, orc):
+    sizes = [0, 1, 7, 8, 9, 4093, 65536 * 8 + 3, 16, 1_000_003] * 5
+    rng = np.random.default_rng(31)
+    host, ws = [], []
+    for k, n in enumerate(sizes):
+        x = (rng.standard_normal(n) * (k + 1)).astype(np.float32)
+        wb = pins.torch_bf16_bits(x)
+        host.append(wb)
+        ws.append(torch.from_numpy(wb.view(np.int16).copy()).view(torch.bfloat16).to(DEV))
+    ts = focus.tensor_scale_many(ws)
+    torch.cuda.synchronize()
+    for k, wb in enumerate(host):
+        s2_o, amax_o = orc.tensor_scale(wb)
+        assert ts.s2[k].item() == float(s2_o) and ts.amax[k].item() == float(amax_o), k
+
+
+def test_dequantize_many_per_row_mix(focus, orc):
+    rng = np.random.default_rng(32)
+    codes, scales, s2s, flags, host = [], [], [], [], []
+    for k in range(40):
+        r, c = int(rng.integers(1, 50)), 16 * int(rng.integers(1, 40))
+        cd = rng.integers(0, 256, (r, c // 2)).astype(np.uint8)
+        sc = rng.integers(0x08, 0x7F, (r, c // 16)).astype(np.uint8)
+        pr = bool(k % 2)
+        s2 = rng.uniform(1e-5, 1.0, r if pr else 1).astype(np.float32)
+        host.append((cd, sc, s2, pr))
+        codes.append(torch.from_numpy(cd).to(DEV))
+        scales.append(torch.from_numpy(sc).to(DEV))
+        s2s.append(torch.from_numpy(s2).to(DEV))
+        flags.append(pr)
+    dq = focus.dequantize_many(codes, scales, s2s, s2_per_row=flags)
+    torch.cuda.synchronize()
+    for k, (cd, sc, s2, pr) in enumerate(host):
+        assert np.array_equal(np_bits(dq.outs[k]), orc.dequantize(cd, sc, s2, s2_per_row=pr)), k
