@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows-fraction", type=float, default=0.5,
                     help="fraction of the rows of layer 0 the CPU oracle quantizes")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="before the steps, copy a buffer of BYTES bytes three times (a plain copy "
+                         "kernel of known traffic, to scale hardware byte counters)")
     return ap.parse_args()
 
 
@@ -123,6 +126,13 @@ def main():
     ACT = focus.quantize_act_per_token(X)
     torch.cuda.synchronize()
     gen_s = time.time() - t0
+    if args.copy_calibration > 0:
+        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(f"# generated {ws.name}: {n_weights} weights in {gen_s:.1f} s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)

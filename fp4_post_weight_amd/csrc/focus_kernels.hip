@@ -559,7 +559,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 constexpr int kAmaxVecPerThread = 8;                                  // 16-byte vectors per lane per tile
 constexpr int64_t kAmaxTile = (int64_t)kThreads * kAmaxVecPerThread;  // vectors per tile (32 KB)
-constexpr int64_t kAmaxGrid = 2048;                                   // workgroups per launch (at most)
+constexpr int64_t kAmaxGrid = 1024;                                   // workgroups per launch (at most)
 
 __device__ __forceinline__ u16x2 max_mag2(u16x2 acc, uint32_t v) {
     return __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2, v & 0x7FFF7FFFu));
