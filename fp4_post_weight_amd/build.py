@@ -51,5 +51,25 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+SELFTEST_SRC = os.path.join(ROOT, "tests", "hip", "focus_selftest.hip")
+SELFTEST_LIB = os.path.join(ROOT, "tests", "hip", "libfocus_selftest.so")
+
+
+def build_selftest(verbose: bool = False) -> str:
+    """The test-only helper library (tests/hip), built from the same numerics
+    header as the product kernels."""
+    out = SELFTEST_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, f"-I{CSRC}", SELFTEST_SRC, "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stderr)
+        raise RuntimeError("hipcc failed (selftest)")
+    os.replace(out, SELFTEST_LIB)
+    return SELFTEST_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_selftest(verbose=True)

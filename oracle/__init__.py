@@ -47,6 +47,7 @@ _SIGNATURES = {
     "oracle_e4m3_round_n": (None, [_f32p, _i64, _u8p]),
     "oracle_bf16_round_n": (None, [_f32p, _i64, _u16p]),
     "oracle_sigmoid_n": (None, [_f32p, _i64, _f32p]),
+    "oracle_expf_n": (None, [_f32p, _i64, _f32p]),
 }
 
 
@@ -132,6 +133,12 @@ class Oracle:
         q = _as(q, _np.float32).ravel()
         out = _np.empty(q.size, _np.float32)
         self.lib.oracle_sigmoid_n(_ptr(q, _f32p), q.size, _ptr(out, _f32p))
+        return out
+
+    def expf_array(self, x):
+        x = _as(x, _np.float32).ravel()
+        out = _np.empty(x.size, _np.float32)
+        self.lib.oracle_expf_n(_ptr(x, _f32p), x.size, _ptr(out, _f32p))
         return out
 
     def subblock_codes(self, w_bits, S, sig, s2):

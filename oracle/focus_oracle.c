@@ -320,3 +320,8 @@ void oracle_sigmoid_n(const float* q, int64_t n, float* out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_sigmoid(q[i]);
 }
+
+void oracle_expf_n(const float* x, int64_t n, float* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_expf(x[i]);
+}
