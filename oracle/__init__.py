@@ -48,6 +48,9 @@ _SIGNATURES = {
     "oracle_bf16_round_n": (None, [_f32p, _i64, _u16p]),
     "oracle_sigmoid_n": (None, [_f32p, _i64, _f32p]),
     "oracle_expf_n": (None, [_f32p, _i64, _f32p]),
+    "oracle_fo6_block": (_ct.c_uint, [_u16p, _f, _u8p]),
+    "oracle_fo6_quantize": (None, [_u16p, _i64, _i64, _f32p, _ct.c_int, _u8p, _u8p, _u16p]),
+    "oracle_fo6_quantize_act_per_token": (None, [_u16p, _i64, _i64, _u8p, _u8p, _f32p, _u16p]),
 }
 
 
@@ -202,6 +205,36 @@ class Oracle:
         self.lib.oracle_quantize_act_per_token(_ptr(x_bits, _u16p), t, h, _ptr(codes, _u8p),
                                                _ptr(scales, _u8p), _ptr(s2, _f32p),
                                                _ptr(xdeq, _u16p))
+        return codes, scales, s2, xdeq
+
+
+    # ---- FourOverSix -------------------------------------------------------------
+    def fo6_quantize(self, w_bits, s2, s2_per_row=False, dequant=True):
+        """FourOverSix RTN of [rows, cols]: one s2 (weights) or s2 per row."""
+        w_bits = _as(w_bits, _np.uint16)
+        rows, cols = w_bits.shape
+        assert cols % 16 == 0
+        s2 = _np.ascontiguousarray(_np.atleast_1d(_np.asarray(s2, _np.float32)))
+        assert s2.size >= (rows if s2_per_row else 1)
+        codes = _np.empty((rows, cols // 2), _np.uint8)
+        scales = _np.empty((rows, cols // 16), _np.uint8)
+        wdeq = _np.empty((rows, cols), _np.uint16) if dequant else None
+        self.lib.oracle_fo6_quantize(_ptr(w_bits, _u16p), rows, cols, _ptr(s2, _f32p),
+                                     1 if s2_per_row else 0, _ptr(codes, _u8p),
+                                     _ptr(scales, _u8p), _ptr(wdeq, _u16p))
+        return codes, scales, wdeq
+
+    def fo6_quantize_act_per_token(self, x_bits, dequant=False):
+        x_bits = _as(x_bits, _np.uint16)
+        t, h = x_bits.shape
+        assert h % 16 == 0
+        codes = _np.empty((t, h // 2), _np.uint8)
+        scales = _np.empty((t, h // 16), _np.uint8)
+        s2 = _np.empty(t, _np.float32)
+        xdeq = _np.empty((t, h), _np.uint16) if dequant else None
+        self.lib.oracle_fo6_quantize_act_per_token(_ptr(x_bits, _u16p), t, h, _ptr(codes, _u8p),
+                                                   _ptr(scales, _u8p), _ptr(s2, _f32p),
+                                                   _ptr(xdeq, _u16p))
         return codes, scales, s2, xdeq
 
 

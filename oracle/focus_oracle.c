@@ -325,3 +325,94 @@ void oracle_expf_n(const float* x, int64_t n, float* out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_expf(x[i]);
 }
+
+/* ---------- FourOverSix (RTN weights, per-token activations) ----------- */
+
+/* FourOverSix, as the FOCUS page describes its evaluation activations
+ * ("FOCUS NVFP4 scales for Llama-3.2-1B-Instruct (our reproduction)",
+ * section "Calibration", the differences from the paper) and its
+ * FourOverSix baseline rows (section "Perplexity"): plain NVFP4 (m = 1, no
+ * relaxation) in which each 16-element block's scale maps the block maximum
+ * either to 6 or to 4, whichever quantizes the block with the lower error.
+ * Readings where the page is silent:
+ *   - candidate k in {6, 4}: t_k = a / (k * s2) (one binary32 division of
+ *     the block maximum by the rounded product k*s2), zero -> 1, clamp to
+ *     [2^-6, 448], E4M3; codes E2M1(clamp(w / (S_k * s2), -6, 6));
+ *   - error of a candidate: sum over the 16 elements, in element order, of
+ *     e*e with e = w - (c*S_k)*s2, every operation binary32;
+ *   - the 4-candidate is taken only when its error is strictly lower
+ *     (ties keep 6); s2 = amax / (6*448) as for NVFP4;
+ *   - s2 == 0: every block is a zero block (scale byte 0x38, signed zeros). */
+
+static void fo6_candidate(const uint16_t* wb, float a, float k, float s2,
+                          unsigned* sb_out, unsigned c[16], float* err_out)
+{
+    float t = a / (k * s2);
+    if (t == 0.0f) t = 1.0f;
+    t = fminf(fmaxf(t, 0x1p-6f), 448.0f);
+    unsigned sb = oracle_e4m3_round(t);
+    float S = oracle_e4m3_value(sb);
+    float err = 0.0f;
+    for (int i = 0; i < 16; ++i) {
+        c[i] = oracle_element_code(wb[i], S, 1.0f, s2);
+        float v = (oracle_e2m1_value(c[i]) * S) * s2;
+        float e = oracle_bf16_value(wb[i]) - v;
+        err = err + e * e;
+    }
+    *sb_out = sb;
+    *err_out = err;
+}
+
+/* One block: returns the scale byte, fills the 16 codes. */
+unsigned oracle_fo6_block(const uint16_t* wb, float s2, uint8_t* codes16)
+{
+    unsigned c6[16], c4[16], sb6, sb4;
+    float e6, e4;
+    if (s2 == 0.0f) {
+        for (int i = 0; i < 16; ++i) codes16[i] = (uint8_t)(((uint32_t)wb[i] >> 15) << 3);
+        return 0x38;
+    }
+    float a = 0.0f;
+    for (int i = 0; i < 16; ++i) {
+        float v = fabsf(oracle_bf16_value(wb[i]));
+        if (v > a) a = v;
+    }
+    fo6_candidate(wb, a, 6.0f, s2, &sb6, c6, &e6);
+    fo6_candidate(wb, a, 4.0f, s2, &sb4, c4, &e4);
+    const int four = e4 < e6;
+    for (int i = 0; i < 16; ++i) codes16[i] = (uint8_t)(four ? c4[i] : c6[i]);
+    return four ? sb4 : sb6;
+}
+
+/* W [rows, cols] with one s2 for the tensor (weights) or, when s2_per_row,
+ * s2[r] for row r (activations).  Outputs as oracle_quantize. */
+void oracle_fo6_quantize(const uint16_t* w, int64_t rows, int64_t cols, const float* s2,
+                         int s2_per_row, uint8_t* codes, uint8_t* scales, uint16_t* wdeq)
+{
+    int64_t nb = cols / 16;
+    for (int64_t r = 0; r < rows; ++r) {
+        float s = s2_per_row ? s2[r] : s2[0];
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint16_t* wb = w + r * cols + b * 16;
+            uint8_t c[16];
+            unsigned sb = oracle_fo6_block(wb, s, c);
+            float S = oracle_e4m3_value(sb);
+            scales[r * nb + b] = (uint8_t)sb;
+            for (int j = 0; j < 8; ++j)
+                codes[r * (cols / 2) + b * 8 + j] = (uint8_t)(c[2 * j] | (c[2 * j + 1] << 4));
+            if (wdeq)
+                for (int i = 0; i < 16; ++i)
+                    wdeq[r * cols + b * 16 + i] = oracle_dequant_value(c[i], S, s);
+        }
+    }
+}
+
+/* Per-token FourOverSix activations: s2_t = amax|x_t| / 2688 per row. */
+void oracle_fo6_quantize_act_per_token(const uint16_t* x, int64_t tokens, int64_t hidden,
+                                       uint8_t* codes, uint8_t* scales, float* s2_out,
+                                       uint16_t* xdeq)
+{
+    for (int64_t t = 0; t < tokens; ++t)
+        s2_out[t] = oracle_tensor_scale(x + t * hidden, hidden, NULL);
+    oracle_fo6_quantize(x, tokens, hidden, s2_out, 1, codes, scales, xdeq);
+}

@@ -526,10 +526,119 @@ def check_act_per_token(o):
         assert np.array_equal(d1[0], xd[t])
 
 
+# ---------------------------------------------------------------------------
+# FourOverSix
+# ---------------------------------------------------------------------------
+
+def _fo6_four_case(rng, n_blocks=300):
+    """Blocks w = c * S * s2 with S a power of two in [2^-6, 2^8], codes of
+    magnitude <= 4 and one element of magnitude exactly 4.  The 4-candidate
+    has t = a/(4*s2) = S exactly, so it reproduces the block with zero error;
+    the 6-candidate's scale is E4M3(2S/3), which for a power of two S is not
+    2S/3 (no E4M3 value is), so its maximum element is off: FourOverSix must
+    choose the 4-candidate and return (S, c)."""
+    exps = rng.integers(-6, 9, n_blocks)
+    S = np.exp2(exps).astype(np.float64)
+    mags = rng.integers(0, 7, (n_blocks, 16))          # codes 0..6 (values <= 4)
+    signs = rng.integers(0, 2, (n_blocks, 16)) << 3
+    pos = rng.integers(0, 16, n_blocks)
+    mags[np.arange(n_blocks), pos] = 6                 # value 4
+    codes = (mags | signs).astype(np.uint8)
+    w = code_value(codes) * S[:, None] * float(S2_POW2)
+    wb = torch_bf16_bits(w.astype(np.float32))
+    assert np.array_equal(bf16_float(wb).astype(np.float64), w)
+    wb = np.where(codes == 8, np.uint16(0x8000), wb).astype(np.uint16)
+    sbytes = torch_e4m3_bytes(S.astype(np.float32))
+    return sbytes, codes, wb.reshape(n_blocks // 4, 64), codes.reshape(n_blocks // 4, 64)
+
+
+def check_fo6_four_fixed_points(o):
+    rng = np.random.default_rng(60)
+    sbytes, _, wb, codes = _fo6_four_case(rng)
+    pc, sc, wd = o.fo6_quantize(wb, S2_POW2)
+    assert np.array_equal(sc.ravel(), sbytes)
+    assert np.array_equal(unpack_codes(pc), codes)
+    assert np.array_equal(wd, wb)
+
+
+def check_fo6_six_fixed_points(o):
+    """Blocks with |c| = 6 at the maximum reproduce exactly under the
+    6-candidate (error 0), so FourOverSix keeps it."""
+    rng = np.random.default_rng(61)
+    sbytes, S, codes, wb = _fixed_point_case(rng, n_rows=119, nb=3)
+    pc, sc, wd = o.fo6_quantize(wb, S2_POW2)
+    assert np.all(sc == sbytes[:, None])
+    assert np.array_equal(unpack_codes(pc), codes)
+    assert np.array_equal(wd, wb)
+
+
+def check_fo6_ties_keep_six(o):
+    """Ties: codes from {0, +-1.5, +-3, +-6} with one +-6 and S = 2^k
+    (k = -6..8) are reproduced exactly by both candidates (the 4-candidate's
+    scale 1.5*S is an E4M3 value and c/1.5 is an E2M1 value), so both errors
+    are 0 and the 6-candidate, scale byte of S with codes c, must be kept."""
+    rng = np.random.default_rng(64)
+    n = 300
+    S = np.exp2(rng.integers(-6, 9, n)).astype(np.float64)
+    mags = np.array([0, 3, 5, 7], np.uint8)[rng.integers(0, 4, (n, 16))]
+    mags[np.arange(n), rng.integers(0, 16, n)] = 7
+    codes = (mags | (rng.integers(0, 2, (n, 16)) << 3)).astype(np.uint8)
+    w = code_value(codes) * S[:, None] * float(S2_POW2)
+    wb = torch_bf16_bits(w.astype(np.float32))
+    wb = np.where(codes == 8, np.uint16(0x8000), wb).astype(np.uint16).reshape(n // 4, 64)
+    pc, sc, wd = o.fo6_quantize(wb, S2_POW2)
+    assert np.array_equal(sc.ravel(), torch_e4m3_bytes(S.astype(np.float32)))
+    assert np.array_equal(unpack_codes(pc), codes.reshape(n // 4, 64))
+
+
+def check_fo6_never_worse_than_rtn(o):
+    """Per block, FourOverSix's squared error is at most plain NVFP4
+    round-to-nearest's (it takes the 4-candidate only when that is lower),
+    and the amax block keeps byte 0x7E (t = 672 clamps to 448 = the
+    6-candidate's scale, a tie)."""
+    wb, _, _ = _random_case(62)
+    s2, _ = o.tensor_scale(wb)
+    pc, sc, wd = o.fo6_quantize(wb, s2)
+    pr, sr, wr = o.quantize(wb, None, None, s2)
+    w = bf16_float(wb).astype(np.float64).reshape(-1, 16)
+    def block_err(pcodes, sbytes):
+        v = code_value(unpack_codes(pcodes)).reshape(-1, 16) * \
+            torch_e4m3_value(sbytes).astype(np.float64).reshape(-1, 1) * float(s2)
+        return ((w - v) ** 2).sum(axis=1)
+    e_fo6, e_rtn = block_err(pc, sc), block_err(pr, sr)
+    assert np.all(e_fo6 <= e_rtn * (1 + 1e-5) + 1e-30)
+    changed = sc.ravel() != sr.ravel()
+    assert changed.any() and np.all(e_fo6[changed] < e_rtn[changed] * (1 + 1e-5))
+    mag = np.abs(bf16_float(wb))
+    r, col = np.unravel_index(np.argmax(mag), mag.shape)
+    assert sc[r, col // 16] == 0x7E
+
+
+def check_fo6_zero_and_act(o):
+    """Zero blocks and an all-zero token take byte 0x38; each token equals the
+    per-tensor FourOverSix of that row with s2_t = amax|x_t| / 2688."""
+    rng = np.random.default_rng(63)
+    x = rng.standard_normal((12, 128)).astype(np.float32)
+    x[:, rng.random(128) < 0.05] *= 30
+    x[3] = 0.0
+    x[5, 16:32] = 0.0
+    xb = torch_bf16_bits(x)
+    pc, sc, s2, xd = o.fo6_quantize_act_per_token(xb, dequant=True)
+    assert np.all(sc[3] == 0x38) and sc[5, 1] == 0x38
+    amax = np.abs(bf16_float(xb)).max(axis=1)
+    assert np.array_equal(s2, (amax / np.float32(2688.0)).astype(np.float32))
+    for t in (0, 5, 11):
+        c1, s1, d1 = o.fo6_quantize(xb[t:t + 1], s2[t])
+        assert np.array_equal(c1[0], pc[t]) and np.array_equal(s1[0], sc[t]) and np.array_equal(d1[0], xd[t])
+
+
 ALL_CHECKS = [
     check_e2m1_table, check_e2m1_nearest_dense, check_e4m3_vs_torch, check_e4m3_decode_vs_torch,
     check_bf16_vs_torch, check_sigmoid, check_expf_correctly_rounded, check_tensor_scale,
     check_fixed_points, check_block_factor_m, check_subblock_logits, check_zero_blocks, check_clamps,
     check_s2_zero, check_amax_block_closed_form, check_error_bound, check_monotone,
     check_plain_rtn_reduction, check_dequantize_roundtrip, check_act_per_token,
+    check_fo6_four_fixed_points, check_fo6_six_fixed_points, check_fo6_ties_keep_six,
+    check_fo6_never_worse_than_rtn,
+    check_fo6_zero_and_act,
 ]

@@ -45,6 +45,13 @@ MUTATIONS = [
     ("s2 == 0 drops the code sign", "return ((uint32_t)w >> 15) << 3;", "return 0;"),
     ("per-token scale from the first row only", "oracle_tensor_scale(x + t * hidden, hidden, NULL)",
      "oracle_tensor_scale(x, hidden, NULL)"),
+    ("FourOverSix prefers 4 on ties", "const int four = e4 < e6;", "const int four = e4 <= e6;"),
+    ("FourOverSix never picks 4", "const int four = e4 < e6;", "const int four = 0;"),
+    ("FourOverSix 4-candidate maps the max to 6", "fo6_candidate(wb, a, 4.0f, s2, &sb4, c4, &e4);",
+     "fo6_candidate(wb, a, 6.0f, s2, &sb4, c4, &e4);"),
+    ("FourOverSix error without the square", "err = err + e * e;", "err = err + fabsf(e);"),
+    ("FourOverSix per-token scale from row 0", "s2_out[t] = oracle_tensor_scale(x + t * hidden, hidden, NULL);",
+     "s2_out[t] = oracle_tensor_scale(x, hidden, NULL);"),
     ("block max over the first sub-block only", "for (int i = 0; i < 16; ++i) {\n                float v = fabsf",
      "for (int i = 0; i < 8; ++i) {\n                float v = fabsf"),
 ]
