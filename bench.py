@@ -148,6 +148,8 @@ def main():
     QB_nodq = [focus.quantize_many([W[i] for i in c], [M[i] for i in c], [Q[i] for i in c],
                                    [S2[i] for i in c], outs=[OUT[i] for i in c], dequant=False, run=False)
                for c in chunks]
+    FB = [focus.quantize_fo6_many([W[i] for i in c], [S2[i] for i in c], outs=[OUT[i] for i in c],
+                                  dequant=False, run=False) for c in chunks]
     DB = [focus.dequantize_many([OUT[i].codes for i in c], [OUT[i].scales for i in c], [S2[i] for i in c],
                                 outs=[DEQ[i] for i in c], run=False) for c in chunks]
     nq = len(QB)
@@ -217,6 +219,9 @@ def main():
         return a.elapsed_time(b) / reps
 
     t_q = time_calls(lambda: [b.run() for b in QB_nodq])
+    t_f6 = time_calls(lambda: [b.run() for b in FB])
+    ACT6 = focus.quantize_act_per_token_fo6(X)
+    t_a6 = time_calls(lambda: focus.quantize_act_per_token_fo6(X, out=ACT6), reps=20)
     torch.cuda.synchronize()
 
     def row(ms, nbytes, units):
@@ -231,6 +236,9 @@ def main():
         "act per token [8192,4096] (step phase)": row(phase["act"], B_ACT * X.numel() + 4 * X.shape[0],
                                                       X.numel()),
         "quantize codes only (after the steps)": row(t_q, B_QUANT * n_weights, n_weights),
+        "FourOverSix weights, codes only (after the steps)": row(t_f6, B_ACT * n_weights, n_weights),
+        "FourOverSix act per token [8192,4096] (after the steps, cache-resident)":
+            row(t_a6, B_ACT * X.numel() + 4 * X.shape[0], X.numel()),
     }
 
     # ---- CPU baseline: the oracle on a bounded sample ----------------------

@@ -34,6 +34,7 @@ from . import _lib
 from ._lib import FocusError, FocusLibraryMissing, library_path  # noqa: F401
 
 __all__ = ["tensor_scale", "quantize", "dequantize", "quantize_act_per_token", "Quantized",
+           "quantize_fo6", "quantize_act_per_token_fo6", "quantize_fo6_many",
            "tensor_scale_many", "quantize_many", "dequantize_many", "Batch",
            "FocusError", "FocusLibraryMissing", "abi_version", "library_path"]
 
@@ -175,6 +176,56 @@ def quantize_act_per_token(x: torch.Tensor, dequant: bool = False,
 
 
 # ---------------------------------------------------------------------------
+# FourOverSix
+# ---------------------------------------------------------------------------
+
+def quantize_fo6(w: torch.Tensor, s2: Optional[torch.Tensor] = None, dequant: bool = True,
+                 out: Optional[Quantized] = None) -> Quantized:
+    """FourOverSix round-to-nearest NVFP4 of W [rows, cols] (per-tensor s2,
+    computed with ``tensor_scale`` when None)."""
+    _check_dev("w", w, torch.bfloat16)
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [rows, cols]")
+    rows, cols = w.shape
+    dev = w.device
+    if cols % 16:
+        raise ValueError("cols must be a multiple of 16")
+    if s2 is None:
+        s2, _ = tensor_scale(w)
+    _check_dev("s2", s2, torch.float32, dev)
+    if out is None:
+        out = Quantized(torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+                        torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
+                        torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) if dequant else None,
+                        s2)
+    deq = out.deq if dequant else None
+    _lib.check(_lib.lib().focus_quantize_fo6(_p(w), rows, cols, _p(s2), _p(out.codes), _p(out.scales),
+                                             _p(deq), _stream(w)))
+    return Quantized(out.codes, out.scales, deq, s2)
+
+
+def quantize_act_per_token_fo6(x: torch.Tensor, dequant: bool = False,
+                               out: Optional[Quantized] = None) -> Quantized:
+    """Per-token FourOverSix NVFP4 of activations X [tokens, hidden]."""
+    _check_dev("x", x, torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [tokens, hidden]")
+    t, h = x.shape
+    if h % 16:
+        raise ValueError("hidden must be a multiple of 16")
+    dev = x.device
+    if out is None:
+        out = Quantized(torch.empty((t, h // 2), dtype=torch.uint8, device=dev),
+                        torch.empty((t, h // 16), dtype=torch.uint8, device=dev),
+                        torch.empty((t, h), dtype=torch.bfloat16, device=dev) if dequant else None,
+                        torch.empty((t,), dtype=torch.float32, device=dev))
+    deq = out.deq if dequant else None
+    _lib.check(_lib.lib().focus_quantize_act_per_token_fo6(_p(x), t, h, _p(out.codes), _p(out.scales),
+                                                           _p(out.s2), _p(deq), _stream(x)))
+    return Quantized(out.codes, out.scales, deq, out.s2)
+
+
+# ---------------------------------------------------------------------------
 # batched calls
 # ---------------------------------------------------------------------------
 
@@ -221,6 +272,13 @@ def tensor_scale_many(ws, s2_out=None, amax_out=None, run: bool = True) -> Batch
         arr[i] = _lib.ScaleDesc(_p(w), w.numel(), s2f[i].data_ptr(), amf[i].data_ptr())
     b = Batch("focus_tensor_scale_many", arr, (list(ws), s2_out, amax_out), dev)
     b.s2, b.amax = s2_out, amax_out
+    return b.run() if run else b
+
+
+def quantize_fo6_many(ws, s2s, outs=None, dequant: bool = True, run: bool = True) -> Batch:
+    """Batched FourOverSix of several weight tensors (see ``quantize_many``)."""
+    b = quantize_many(ws, [None] * len(ws), [None] * len(ws), s2s, outs=outs, dequant=dequant, run=False)
+    b._fn = _lib.lib().focus_quantize_fo6_many
     return b.run() if run else b
 
 

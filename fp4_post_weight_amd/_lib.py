@@ -37,9 +37,12 @@ _SIGNATURES = {
     "focus_quantize": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "focus_dequantize": (_INT, [_VP, _VP, _VP, _INT, _I64, _I64, _VP, _VP]),
     "focus_quantize_act_per_token": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
+    "focus_quantize_fo6": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
+    "focus_quantize_act_per_token_fo6": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP]),
     "focus_tensor_scale_many": (_INT, [ct.POINTER(ScaleDesc), _INT, _VP]),
     "focus_quantize_many": (_INT, [ct.POINTER(QuantDesc), _INT, _VP]),
     "focus_dequantize_many": (_INT, [ct.POINTER(DequantDesc), _INT, _VP]),
+    "focus_quantize_fo6_many": (_INT, [ct.POINTER(QuantDesc), _INT, _VP]),
 }
 
 EXPORTED = tuple(_SIGNATURES)

@@ -63,7 +63,7 @@ int quant_key(const focus_quant_desc& d) {
     return (d.m ? 4 : 0) | (d.q ? 2 : 0) | (d.w_deq ? 1 : 0);
 }
 
-int run_quantize(const focus_quant_desc* descs, int n, hipStream_t stream) {
+int run_quantize(const focus_quant_desc* descs, int n, hipStream_t stream, bool fo6 = false) {
     focus::QuantBatch bt;
     int key = -1;
     bt.n = 0;
@@ -71,7 +71,7 @@ int run_quantize(const focus_quant_desc* descs, int n, hipStream_t stream) {
         const bool end = (i == n);
         const bool skip = !end && (descs[i].rows == 0 || descs[i].cols == 0);
         if (skip) continue;
-        const int k = end ? -1 : quant_key(descs[i]);
+        const int k = end ? -1 : (fo6 ? 8 | (descs[i].w_deq ? 1 : 0) : quant_key(descs[i]));
         if (bt.n > 0 && (end || k != key || bt.n == focus::kBatch)) {
             int st = hip_status(focus::launch_quantize(bt, key, stream));
             if (st != FOCUS_OK) return st;
@@ -223,7 +223,40 @@ int focus_quantize_act_per_token(const uint16_t* x_bf16, int64_t tokens, int64_t
     if (!aligned(x_bf16, 16) || !aligned(codes, 8) || !aligned(s2_out, 4) || !aligned(x_deq, 16))
         return FOCUS_ERR_ALIGN;
     return hip_status(focus::launch_act_per_token(x_bf16, tokens, hidden, codes, scales, s2_out,
-                                                  x_deq, (hipStream_t)stream));
+                                                  x_deq, false, (hipStream_t)stream));
+}
+
+int focus_quantize_fo6(const uint16_t* w_bf16, int64_t rows, int64_t cols, const float* s2,
+                       uint8_t* codes, uint8_t* scales, uint16_t* w_deq, void* stream) {
+    const focus_quant_desc d = {w_bf16, rows, cols, nullptr, nullptr, s2, codes, scales, w_deq};
+    int st = check_quant(d);
+    if (st != FOCUS_OK) return st;
+    return run_quantize(&d, 1, (hipStream_t)stream, true);
+}
+
+int focus_quantize_fo6_many(const focus_quant_desc* descs, int n, void* stream) {
+    if (n < 0) return FOCUS_ERR_RANGE;
+    if (n > 0 && !descs) return FOCUS_ERR_NULL;
+    for (int i = 0; i < n; ++i) {
+        int st = check_quant(descs[i]);
+        if (st != FOCUS_OK) return st;
+        if (descs[i].m || descs[i].q) return FOCUS_ERR_RANGE;
+    }
+    return run_quantize(descs, n, (hipStream_t)stream, true);
+}
+
+int focus_quantize_act_per_token_fo6(const uint16_t* x_bf16, int64_t tokens, int64_t hidden,
+                                     uint8_t* codes, uint8_t* scales, float* s2_out,
+                                     uint16_t* x_deq, void* stream) {
+    int st = shape_2d(tokens, hidden);
+    if (st != FOCUS_OK) return st;
+    if (tokens > kMaxTokens) return FOCUS_ERR_RANGE;
+    if (tokens == 0 || hidden == 0) return FOCUS_OK;
+    if (!x_bf16 || !codes || !scales || !s2_out) return FOCUS_ERR_NULL;
+    if (!aligned(x_bf16, 16) || !aligned(codes, 8) || !aligned(s2_out, 4) || !aligned(x_deq, 16))
+        return FOCUS_ERR_ALIGN;
+    return hip_status(focus::launch_act_per_token(x_bf16, tokens, hidden, codes, scales, s2_out,
+                                                  x_deq, true, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -192,6 +192,45 @@ __device__ __forceinline__ void quantize_block(uint4 a, uint4 b, float mb, float
     }
 }
 
+// FourOverSix for one block; same interface as quantize_block (rden6 and
+// rden4 are RN64(1/RN32(6*s2)) and RN64(1/RN32(4*s2))).
+template <bool DEQ>
+__device__ __forceinline__ void fo6_block(uint4 a, uint4 b, float s2, double rden6, double rden4,
+                                          uint2* codes_out, uint8_t* scale_out, uint4& deq0,
+                                          uint4& deq1) {
+    const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float f[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        f[2 * i] = bf16_lo(v[i]);
+        f[2 * i + 1] = bf16_hi(v[i]);
+    }
+    if (s2 == 0.0f) {
+        *scale_out = 0x38;
+        st8(codes_out, 0, make_uint2(sign_codes8(a), sign_codes8(b)));
+        if (DEQ) {
+            const uint32_t z = 0x80008000u;
+            deq0 = make_uint4(a.x & z, a.y & z, a.z & z, a.w & z);
+            deq1 = make_uint4(b.x & z, b.y & z, b.z & z, b.w & z);
+        }
+        return;
+    }
+    const float amax = block_amax_bits(a, b);
+    uint32_t sb6, sb4, c60, c61, c40, c41;
+    float S6, S4, e6, e4;
+    fo6_candidate(f, amax, rden6, s2, sb6, S6, c60, c61, e6);
+    fo6_candidate(f, amax, rden4, s2, sb4, S4, c40, c41, e4);
+    const bool four = e4 < e6;
+    const uint32_t c0 = four ? c40 : c60, c1 = four ? c41 : c61;
+    const float S = four ? S4 : S6;
+    st8(codes_out, 0, make_uint2(c0, c1));
+    *scale_out = (uint8_t)(four ? sb4 : sb6);
+    if (DEQ) {
+        deq0 = dequant8(c0, S, s2);
+        deq1 = dequant8(c1, S, s2);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // batches: up to kBatch tensors per launch, described in the kernel argument
 // segment (structure of arrays, about 2.3 KB).  Work is cut into tiles of
@@ -217,7 +256,7 @@ __device__ __forceinline__ int find_tensor(const int64_t* tile_start, int n, int
 constexpr int kQuantU = 2;
 constexpr int64_t kQuantTile = (int64_t)kThreads * kQuantU;
 
-template <bool HAS_M, bool HAS_Q, bool DEQ>
+template <bool HAS_M, bool HAS_Q, bool DEQ, bool FO6 = false>
 __global__ __launch_bounds__(kThreads) void k_quantize(QuantBatch bt, int64_t ntiles) {
     __shared__ uint4 xch[DEQ ? kThreads / 64 : 1][128];
     constexpr bool kLdsLoadW = LdsLoadW<DEQ>::value;
@@ -233,6 +272,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QuantBatch bt, int64_t nt
         const float2* __restrict__ q = bt.q[j];
         const float s2 = ld_uniform(bt.s2[j]);
         const double rden = 1.0 / (double)(6.0f * s2);
+        const double rden4 = FO6 ? 1.0 / (double)(4.0f * s2) : 0.0;
         const int64_t nblk = bt.nblk[j];
         const int64_t tile0 = (tile - bt.tile_start[j]) * kQuantTile;
         uint4 va[kQuantU], vb[kQuantU];
@@ -262,9 +302,14 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QuantBatch bt, int64_t nt
             const int64_t blk = first + lane;
             if (kLdsLoadW && first < nblk) wave_gather_blocks(va[k], vb[k], xchw[wave], lane);
             uint4 d0 = make_uint4(0, 0, 0, 0), d1 = d0;
-            if (blk < nblk)
-                quantize_block<HAS_Q, DEQ>(va[k], vb[k], mb[k], qq[k].x, qq[k].y, s2, rden, tab,
-                                           bt.codes[j] + blk, bt.scales[j] + blk, d0, d1);
+            if (blk < nblk) {
+                if (FO6)
+                    fo6_block<DEQ>(va[k], vb[k], s2, rden, rden4, bt.codes[j] + blk,
+                                   bt.scales[j] + blk, d0, d1);
+                else
+                    quantize_block<HAS_Q, DEQ>(va[k], vb[k], mb[k], qq[k].x, qq[k].y, s2, rden, tab,
+                                               bt.codes[j] + blk, bt.scales[j] + blk, d0, d1);
+            }
             if (DEQ && first < nblk)
                 wave_store_blocks(bt.wdeq[j] + 2 * first, d0, d1, xch[DEQ ? wave : 0], lane,
                                   nblk - first);
@@ -434,7 +479,7 @@ __device__ __forceinline__ float wave_max_f32(float v) {
 // RB > 0: lane keeps up to RB blocks of the row in registers (rows of at most
 // 64*RB blocks).  RB == 0: rows of any length, read twice (the second read
 // hits the caches).
-template <int RB, bool DEQ>
+template <int RB, bool DEQ, bool FO6 = false>
 __global__ __launch_bounds__(kThreads) void k_act(const uint4* __restrict__ x, int64_t tokens,
                                                   int64_t nb, uint2* __restrict__ codes,
                                                   uint8_t* __restrict__ scales,
@@ -466,24 +511,36 @@ __global__ __launch_bounds__(kThreads) void k_act(const uint4* __restrict__ x, i
     const float s2 = amax / 2688.0f;
     if (lane == 0) s2out[row] = s2;
     const double rden = 1.0 / (double)(6.0f * s2);
+    const double rden4 = FO6 ? 1.0 / (double)(4.0f * s2) : 0.0;
     uint4* xw = xch[DEQ ? (threadIdx.x >> 6) : 0];
     if (RB > 0) {
 #pragma unroll
         for (int k = 0; k < R; ++k) {
             const int64_t j0 = 64 * k, j = j0 + lane;
             uint4 d0 = make_uint4(0, 0, 0, 0), d1 = d0;
-            if (j < nb)
-                quantize_block<false, DEQ>(va[k], vb[k], 1.0f, 0.0f, 0.0f, s2, rden, nullptr, codes + base + j,
-                                           scales + base + j, d0, d1);
+            if (j < nb) {
+                if (FO6)
+                    fo6_block<DEQ>(va[k], vb[k], s2, rden, rden4, codes + base + j, scales + base + j,
+                                   d0, d1);
+                else
+                    quantize_block<false, DEQ>(va[k], vb[k], 1.0f, 0.0f, 0.0f, s2, rden, nullptr,
+                                               codes + base + j, scales + base + j, d0, d1);
+            }
             if (DEQ && j0 < nb) wave_store_blocks(xdeq + 2 * (base + j0), d0, d1, xw, lane, nb - j0);
         }
     } else {
         for (int64_t j0 = 0; j0 < nb; j0 += 64) {
             const int64_t j = j0 + lane;
             uint4 d0 = make_uint4(0, 0, 0, 0), d1 = d0;
-            if (j < nb)
-                quantize_block<false, DEQ>(x[2 * (base + j)], x[2 * (base + j) + 1], 1.0f, 0.0f, 0.0f,
-                                           s2, rden, nullptr, codes + base + j, scales + base + j, d0, d1);
+            if (j < nb) {
+                if (FO6)
+                    fo6_block<DEQ>(x[2 * (base + j)], x[2 * (base + j) + 1], s2, rden, rden4,
+                                   codes + base + j, scales + base + j, d0, d1);
+                else
+                    quantize_block<false, DEQ>(x[2 * (base + j)], x[2 * (base + j) + 1], 1.0f, 0.0f,
+                                               0.0f, s2, rden, nullptr, codes + base + j,
+                                               scales + base + j, d0, d1);
+            }
             if (DEQ) wave_store_blocks(xdeq + 2 * (base + j0), d0, d1, xw, lane, nb - j0);
         }
     }
@@ -537,6 +594,12 @@ hipError_t launch_quantize(QuantBatch& bt, int key, hipStream_t stream) {
         FOCUS_Q_CASE(6, true, true, false)
         FOCUS_Q_CASE(7, true, true, true)
 #undef FOCUS_Q_CASE
+        case 8:
+            hipLaunchKernelGGL((k_quantize<false, false, false, true>), grid, block, 0, stream, bt, t);
+            break;
+        case 9:
+            hipLaunchKernelGGL((k_quantize<false, false, true, true>), grid, block, 0, stream, bt, t);
+            break;
     }
     return hipGetLastError();
 }
@@ -553,7 +616,7 @@ hipError_t launch_dequantize(DequantBatch& bt, hipStream_t stream) {
 }
 
 hipError_t launch_act_per_token(const uint16_t* x, int64_t tokens, int64_t hidden, uint8_t* codes,
-                                uint8_t* scales, float* s2_out, uint16_t* xdeq,
+                                uint8_t* scales, float* s2_out, uint16_t* xdeq, bool fo6,
                                 hipStream_t stream) {
     const int64_t nb = hidden / 16;
     const int64_t rows_per_wg = kThreads / 64;
@@ -561,14 +624,19 @@ hipError_t launch_act_per_token(const uint16_t* x, int64_t tokens, int64_t hidde
     auto X = reinterpret_cast<const uint4*>(x);
     auto C = reinterpret_cast<uint2*>(codes);
     auto D = reinterpret_cast<uint4*>(xdeq);
-#define FOCUS_ACT(RB)                                                                          \
+#define FOCUS_ACT_F(RB, F)                                                                     \
     do {                                                                                       \
         if (xdeq)                                                                              \
-            hipLaunchKernelGGL((k_act<RB, true>), grid, block, 0, stream, X, tokens, nb, C,    \
+            hipLaunchKernelGGL((k_act<RB, true, F>), grid, block, 0, stream, X, tokens, nb, C, \
                                scales, s2_out, D);                                             \
         else                                                                                   \
-            hipLaunchKernelGGL((k_act<RB, false>), grid, block, 0, stream, X, tokens, nb, C,   \
-                               scales, s2_out, D);                                             \
+            hipLaunchKernelGGL((k_act<RB, false, F>), grid, block, 0, stream, X, tokens, nb,   \
+                               C, scales, s2_out, D);                                          \
+    } while (0)
+#define FOCUS_ACT(RB)                 \
+    do {                              \
+        if (fo6) FOCUS_ACT_F(RB, true);  \
+        else FOCUS_ACT_F(RB, false);     \
     } while (0)
     if (nb <= 64) FOCUS_ACT(1);
     else if (nb <= 128) FOCUS_ACT(2);
@@ -576,6 +644,7 @@ hipError_t launch_act_per_token(const uint16_t* x, int64_t tokens, int64_t hidde
     else if (nb <= 512) FOCUS_ACT(8);
     else FOCUS_ACT(0);
 #undef FOCUS_ACT
+#undef FOCUS_ACT_F
     return hipGetLastError();
 }
 

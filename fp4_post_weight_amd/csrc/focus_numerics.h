@@ -230,4 +230,41 @@ __device__ __forceinline__ uint32_t sign_codes8(uint4 v) {
     return out;
 }
 
+// ---------------------------------------------------------------------------
+// FourOverSix: the block scale maps the block maximum to 6 or to 4, whichever
+// quantizes the block with the lower binary32 squared error (summed in element
+// order; the 4-candidate only when strictly lower).  m = 1, no relaxation.
+// ---------------------------------------------------------------------------
+
+// One candidate: scale byte, codes of both halves, and its error.
+__device__ __forceinline__ void fo6_candidate(const float* f, float amax, double rden, float s2,
+                                              uint32_t& sb, float& S, uint32_t& c0, uint32_t& c1,
+                                              float& err) {
+    sb = e4m3_byte_normal(block_t(amax, 1.0f, rden));
+    S = e4m3_normal_value(sb);
+    const float d = S * s2;
+    c0 = encode8(f, d);
+    c1 = encode8(f + 8, d);
+    float e = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t c = h ? c1 : c0;
+#pragma unroll
+        for (int sel = 0; sel < 4; ++sel) {
+            f32x2 cv;
+            if (sel == 0) cv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+            else if (sel == 1) cv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+            else if (sel == 2) cv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+            else cv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+            const float v0 = (cv[0] * S) * s2;
+            const float v1 = (cv[1] * S) * s2;
+            const float e0 = f[8 * h + 2 * sel] - v0;
+            const float e1 = f[8 * h + 2 * sel + 1] - v1;
+            e = e + e0 * e0;
+            e = e + e1 * e1;
+        }
+    }
+    err = e;
+}
+
 }  // namespace focus

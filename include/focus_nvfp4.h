@@ -132,6 +132,24 @@ int focus_quantize_act_per_token(const uint16_t* x_bf16, int64_t tokens, int64_t
                                  uint16_t* x_deq, void* stream);
 
 /*
+ * FourOverSix (NVFP4 with adaptive block scale), the FOCUS page's activation
+ * protocol and baseline ("FOCUS NVFP4 scales for Llama-3.2-1B-Instruct (our
+ * reproduction)", sections "Calibration" and "Perplexity"): plain NVFP4
+ * (m = 1, no relaxation) in which each 16-element block's scale maps the
+ * block maximum to 6 or to 4, whichever gives the lower error.  Readings
+ * where the page is silent: error = binary32 sum, in element order, of
+ * (w - (c*S)*s2)^2; the 4-candidate only when strictly lower (ties keep 6);
+ * s2 = amax / (6*448) as for NVFP4.  Outputs and rules as focus_quantize /
+ * focus_quantize_act_per_token (codes, E4M3 scale bytes, optional BF16 w').
+ */
+int focus_quantize_fo6(const uint16_t* w_bf16, int64_t rows, int64_t cols, const float* s2,
+                       uint8_t* codes, uint8_t* scales, uint16_t* w_deq, void* stream);
+
+int focus_quantize_act_per_token_fo6(const uint16_t* x_bf16, int64_t tokens, int64_t hidden,
+                                     uint8_t* codes, uint8_t* scales, float* s2_out,
+                                     uint16_t* x_deq, void* stream);
+
+/*
  * Batched calls.  A model holds many linears (112, 224 or 560 for the Llama
  * sets); one launch per tensor leaves the GPU idle between short kernels.
  * These calls take a HOST array of descriptors (read during the call only,
@@ -174,6 +192,10 @@ typedef struct focus_dequant_desc {
 } focus_dequant_desc;
 
 int focus_dequantize_many(const focus_dequant_desc* descs, int n, void* stream);
+
+/* Batched FourOverSix of weights: descriptors as for focus_quantize_many with
+ * m and q NULL (FOCUS_ERR_RANGE otherwise). */
+int focus_quantize_fo6_many(const focus_quant_desc* descs, int n, void* stream);
 
 #ifdef __cplusplus
 }

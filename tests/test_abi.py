@@ -159,3 +159,14 @@ def test_descriptor_layout():
     assert ct.sizeof(_lib.ScaleDesc) == 4 * 8
     assert ct.sizeof(_lib.DequantDesc) == 7 * 8
     assert _lib.DequantDesc.rows.offset == 32
+
+
+def test_fo6_validation(lib):
+    QD = _lib.QuantDesc
+    assert lib.focus_quantize_fo6(None, 4, 32, FAKE, FAKE, FAKE, None, None) == ERR_NULL
+    assert lib.focus_quantize_fo6(FAKE, 4, 30, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
+    assert lib.focus_quantize_fo6(FAKE, 0, 32, None, None, None, None, None) == OK
+    with_m = QD(FAKE, 4, 32, FAKE, None, FAKE, FAKE, FAKE, None)
+    assert lib.focus_quantize_fo6_many((QD * 1)(with_m), 1, None) == ERR_RANGE
+    assert lib.focus_quantize_act_per_token_fo6(FAKE, 4, 64, None, FAKE, FAKE, None, None) == ERR_NULL
+    assert lib.focus_quantize_act_per_token_fo6(FAKE + 2, 4, 64, FAKE, FAKE, FAKE, None, None) == ERR_ALIGN

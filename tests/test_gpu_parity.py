@@ -375,3 +375,131 @@ def test_dequantize_many_per_row_mix(focus, orc):
     torch.cuda.synchronize()
     for k, (cd, sc, s2, pr) in enumerate(host):
         assert np.array_equal(np_bits(dq.outs[k]), orc.dequantize(cd, sc, s2, s2_per_row=pr)), k
+
+
+# ---------------------------------------------------------------------------
+# FourOverSix (weights per tensor, activations per token)
+# ---------------------------------------------------------------------------
+
+def run_fo6(focus, wb, s2=None, dequant=True):
+    w = torch.from_numpy(np.ascontiguousarray(wb).view(np.int16).copy()).view(torch.bfloat16).to(DEV)
+    s2d = None if s2 is None else torch.tensor([s2], dtype=torch.float32, device=DEV)
+    res = focus.quantize_fo6(w, s2d, dequant=dequant)
+    torch.cuda.synchronize()
+    return (res.codes.cpu().numpy(), res.scales.cpu().numpy(),
+            None if res.deq is None else np_bits(res.deq), np.float32(res.s2.item()))
+
+
+def check_fo6(focus, orc, wb, dequant=True, s2=None, label=""):
+    codes, scales, deq, s2g = run_fo6(focus, wb, s2, dequant)
+    if s2 is None:
+        s2_o, _ = orc.tensor_scale(wb)
+        assert s2g == s2_o, label
+    else:
+        s2_o = np.float32(s2)
+    c, sc, d = orc.fo6_quantize(wb, s2_o, dequant=dequant)
+    assert np.array_equal(scales, sc), f"{label}: {np.count_nonzero(scales != sc)} scale bytes differ"
+    assert np.array_equal(codes, c), f"{label}: {np.count_nonzero(codes != c)} code bytes differ"
+    if dequant:
+        assert np.array_equal(deq, d), label
+    return np.count_nonzero(sc != orc.quantize(wb, None, None, s2_o, dequant=False)[1])
+
+
+def test_fo6_single_linear_and_ragged(focus, orc):
+    w, _, _ = synth.make_single()
+    n4 = check_fo6(focus, orc, np_bits(w), label="fo6 single [256,1024]")
+    assert n4 > 1000  # a large share of Gaussian blocks prefer the 4-candidate
+    for shape in RAGGED:
+        wr = synth.weights(shape, seed=shape[0] + 7 * shape[1], tensor_id=9, zero_block_p=0.02)
+        check_fo6(focus, orc, np_bits(wr), dequant=shape[0] % 2 == 1, label=f"fo6 {shape}")
+
+
+def test_fo6_constructed_cases(focus, orc):
+    rng = np.random.default_rng(70)
+    _, _, wb4, _ = pins._fo6_four_case(rng)
+    check_fo6(focus, orc, wb4, s2=float(pins.S2_POW2), label="fo6 four fixed points")
+    _, _, _, wb6 = pins._fixed_point_case(rng, n_rows=119, nb=3)
+    check_fo6(focus, orc, wb6, s2=float(pins.S2_POW2), label="fo6 six fixed points")
+    wz = np.zeros((4, 64), np.uint16)
+    wz[1, 3] = 0x8000
+    check_fo6(focus, orc, wz, label="fo6 all zero")
+
+
+def test_fo6_extreme_magnitudes(focus, orc):
+    rng = np.random.default_rng(71)
+    e = rng.integers(-140, 127, (64, 256)).astype(np.float64)
+    x = (rng.standard_normal((64, 256)) * np.exp2(e)).astype(np.float32)
+    x[0, 0] = 3.3e38
+    check_fo6(focus, orc, pins.torch_bf16_bits(x), label="fo6 extreme")
+    for amax_exp in (-133, -120):
+        y = (rng.uniform(-1, 1, (16, 128)) * 2.0 ** amax_exp).astype(np.float32)
+        check_fo6(focus, orc, pins.torch_bf16_bits(y), label=f"fo6 tiny 2^{amax_exp}")
+
+
+@pytest.mark.parametrize("shape", sorted(set(synth.LLAMA_8B.layer_shapes())), ids=lambda s: f"{s[0]}x{s[1]}")
+def test_fo6_full_size_sampled(focus, orc, shape):
+    lin = next(l for l in synth.LLAMA_8B.linears() if (l.rows, l.cols) == shape)
+    w, _, _ = synth.make_linear(synth.LLAMA_8B, lin, device=DEV, with_m=False, with_q=False)
+    res = focus.quantize_fo6(w, dequant=True)
+    torch.cuda.synchronize()
+    wb = np_bits(w)
+    s2_o, _ = orc.tensor_scale(wb)
+    assert res.s2.item() == float(s2_o)
+    rows = shape[0]
+    idx = np.unique(np.concatenate([[0, rows - 1], np.random.default_rng(rows).integers(0, rows, 30)]))
+    it = torch.from_numpy(idx).to(DEV)
+    c, sc, d = orc.fo6_quantize(wb[idx], s2_o)
+    assert np.array_equal(res.scales[it].cpu().numpy(), sc)
+    assert np.array_equal(res.codes[it].cpu().numpy(), c)
+    assert np.array_equal(np_bits(res.deq[it]), d)
+
+
+def check_act_fo6(focus, orc, x, dequant, label):
+    res = focus.quantize_act_per_token_fo6(x.to(DEV), dequant=dequant)
+    torch.cuda.synchronize()
+    xb = np_bits(x)
+    rows = xb.shape[0]
+    n = parity.threads()
+    if rows >= 2 * n:
+        from concurrent.futures import ThreadPoolExecutor
+        bounds = np.linspace(0, rows, n + 1).astype(int)
+        with ThreadPoolExecutor(n) as ex:
+            parts = list(ex.map(lambda i: orc.fo6_quantize_act_per_token(xb[bounds[i]:bounds[i + 1]], dequant),
+                                range(n)))
+        c = np.concatenate([p[0] for p in parts])
+        s = np.concatenate([p[1] for p in parts])
+        s2 = np.concatenate([p[2] for p in parts])
+        xd = np.concatenate([p[3] for p in parts]) if dequant else None
+    else:
+        c, s, s2, xd = orc.fo6_quantize_act_per_token(xb, dequant)
+    assert np.array_equal(res.s2.cpu().numpy().view(np.uint32), s2.view(np.uint32)), label
+    assert np.array_equal(res.scales.cpu().numpy(), s), label
+    assert np.array_equal(res.codes.cpu().numpy(), c), label
+    if dequant:
+        assert np.array_equal(np_bits(res.deq), xd), label
+
+
+def test_fo6_act_full(focus, orc):
+    check_act_fo6(focus, orc, synth.make_activations(), False, "fo6 act [8192,4096]")
+
+
+@pytest.mark.parametrize("shape", [(1, 16), (5, 1024), (6, 2048), (7, 4096), (9, 8192), (3, 16400)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
+def test_fo6_act_shapes(focus, orc, shape):
+    x = synth.activations(shape, seed=shape[0] * 13 + shape[1], tensor_id=2)
+    if shape[0] > 2:
+        x[2] = 0.0
+    check_act_fo6(focus, orc, x, True, f"fo6 act {shape}")
+
+
+def test_fo6_many_matches_single(focus, orc):
+    items = _mixed_set(40, seed=77)
+    ws = [w for w, _, _ in items]
+    ts = focus.tensor_scale_many(ws)
+    b = focus.quantize_fo6_many(ws, [ts.s2[i] for i in range(len(ws))], dequant=True)
+    torch.cuda.synchronize()
+    for i, w in enumerate(ws):
+        single = focus.quantize_fo6(w, ts.s2[i], dequant=True)
+        torch.cuda.synchronize()
+        assert torch.equal(b.outs[i].codes, single.codes) and torch.equal(b.outs[i].scales, single.scales)
+        assert torch.equal(b.outs[i].deq.view(torch.int16), single.deq.view(torch.int16))
