@@ -49,6 +49,10 @@ _SIGNATURES = {
     "oracle_sigmoid_n": (None, [_f32p, _i64, _f32p]),
     "oracle_expf_n": (None, [_f32p, _i64, _f32p]),
     "oracle_fo6_block": (_ct.c_uint, [_u16p, _f, _u8p]),
+    "oracle_e8m0_value": (_f, [_ct.c_uint]),
+    "oracle_mx_block_scale": (_ct.c_uint, [_f, _f]),
+    "oracle_mx_quantize": (None, [_u16p, _i64, _i64, _f32p, _f32p, _u8p, _u8p, _u16p]),
+    "oracle_mx_dequantize": (None, [_u8p, _u8p, _i64, _i64, _u16p]),
     "oracle_fo6_quantize": (None, [_u16p, _i64, _i64, _f32p, _ct.c_int, _u8p, _u8p, _u16p]),
     "oracle_fo6_quantize_act_per_token": (None, [_u16p, _i64, _i64, _u8p, _u8p, _f32p, _u16p]),
 }
@@ -236,6 +240,43 @@ class Oracle:
                                                    _ptr(scales, _u8p), _ptr(s2, _f32p),
                                                    _ptr(xdeq, _u16p))
         return codes, scales, s2, xdeq
+
+    # ---- FOCUS on MXFP4 ---------------------------------------------------------
+    def e8m0_value(self, b):
+        return self.lib.oracle_e8m0_value(int(b))
+
+    def mx_block_scale(self, a, mb=1.0):
+        return self.lib.oracle_mx_block_scale(float(a), float(mb))
+
+    def mx_quantize(self, w_bits, m, q, dequant=True):
+        """FOCUS on MXFP4: W [rows, cols] (cols % 32 == 0), m [rows, cols/32] or
+        None, q [rows, cols/8] or None -> (codes, E8M0 scales [rows, cols/32],
+        wdeq or None)."""
+        w_bits = _as(w_bits, _np.uint16)
+        rows, cols = w_bits.shape
+        assert cols % 32 == 0
+        if m is not None:
+            m = _as(m, _np.float32)
+            assert m.shape == (rows, cols // 32)
+        if q is not None:
+            q = _as(q, _np.float32)
+            assert q.shape == (rows, cols // 8)
+        codes = _np.empty((rows, cols // 2), _np.uint8)
+        scales = _np.empty((rows, cols // 32), _np.uint8)
+        wdeq = _np.empty((rows, cols), _np.uint16) if dequant else None
+        self.lib.oracle_mx_quantize(_ptr(w_bits, _u16p), rows, cols, _ptr(m, _f32p), _ptr(q, _f32p),
+                                    _ptr(codes, _u8p), _ptr(scales, _u8p), _ptr(wdeq, _u16p))
+        return codes, scales, wdeq
+
+    def mx_dequantize(self, codes, scales):
+        codes = _as(codes, _np.uint8)
+        scales = _as(scales, _np.uint8)
+        rows, half = codes.shape
+        cols = 2 * half
+        assert scales.shape == (rows, cols // 32)
+        out = _np.empty((rows, cols), _np.uint16)
+        self.lib.oracle_mx_dequantize(_ptr(codes, _u8p), _ptr(scales, _u8p), rows, cols, _ptr(out, _u16p))
+        return out
 
 
 _default = None

@@ -416,3 +416,88 @@ void oracle_fo6_quantize_act_per_token(const uint16_t* x, int64_t tokens, int64_
         s2_out[t] = oracle_tensor_scale(x + t * hidden, hidden, NULL);
     oracle_fo6_quantize(x, tokens, hidden, s2_out, 1, codes, scales, xdeq);
 }
+
+/* ---------- FOCUS on MXFP4 ---------------------------------------------- */
+
+/* The technical summary of the FOCUS paper ("Technische Samenvatting:
+ * FOCUS ...", section "Methodologie", Coupled-Relaxation and Dual-Granularity
+ * Scaling) applies the method to MXFP4 as well: 32-element hardware blocks
+ * with a power-of-two (E8M0) dequantization scale, each block split into
+ * sub-blocks of 8 that are quantized with their own relaxation coefficient,
+ * the stored scale shared by the whole block.  Readings where the pages are
+ * silent (the same shape as the NVFP4 formulas of the FOCUS page):
+ *   - block scale: the OCP Microscaling conversion applied to the scaled
+ *     block maximum t = max|w_b| * m_b (binary32 product): S_b =
+ *     2^(floor(log2 t) - 2) (2 = the exponent of E2M1's largest value 6),
+ *     exponent clamped to [-127, 127] (the E8M0 range); t == 0 -> scale 1;
+ *     byte = exponent + 127;
+ *   - no tensor scale;
+ *   - sub-block k (0..3, elements 8k..8k+7) of block b of row r uses
+ *     q[r, 4b+k]; m is [rows, cols/32];
+ *   - c_i = E2M1(clamp(w_i / (S_b * sigmoid(q_k)), -6, 6)); w' = BF16(c*S_b). */
+
+/* E8M0 value of a byte (0xFF is NaN). */
+float oracle_e8m0_value(unsigned byte)
+{
+    if ((byte & 0xFFu) == 0xFFu) return NAN;
+    return ldexpf(1.0f, (int)(byte & 0xFFu) - 127);
+}
+
+unsigned oracle_mx_block_scale(float a, float mb)
+{
+    float t = a * mb;
+    if (t == 0.0f) return 127u;
+    int e2;
+    (void)frexpf(t, &e2);          /* t = f * 2^e2, f in [0.5, 1) */
+    int e = (e2 - 1) - 2;          /* floor(log2 t) - emax(E2M1) */
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return (unsigned)(e + 127);
+}
+
+/* W [rows, cols] (cols % 32 == 0); m [rows, cols/32] or NULL; q [rows,
+ * cols/8] or NULL.  codes [rows, cols/2] (element 2j low nibble), scales
+ * [rows, cols/32] E8M0 bytes, wdeq [rows, cols] BF16 or NULL. */
+void oracle_mx_quantize(const uint16_t* w, int64_t rows, int64_t cols, const float* m,
+                        const float* q, uint8_t* codes, uint8_t* scales, uint16_t* wdeq)
+{
+    int64_t nb = cols / 32;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint16_t* wb = w + r * cols + b * 32;
+            float a = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                float v = fabsf(oracle_bf16_value(wb[i]));
+                if (v > a) a = v;
+            }
+            float mb = m ? m[r * nb + b] : 1.0f;
+            unsigned sb = oracle_mx_block_scale(a, mb);
+            float S = oracle_e8m0_value(sb);
+            scales[r * nb + b] = (uint8_t)sb;
+            unsigned c[32];
+            for (int k = 0; k < 4; ++k) {
+                float sig = q ? oracle_sigmoid(q[r * (4 * nb) + 4 * b + k]) : 1.0f;
+                for (int i = 0; i < 8; ++i)
+                    c[8 * k + i] = oracle_element_code(wb[8 * k + i], S, sig, 1.0f);
+            }
+            for (int j = 0; j < 16; ++j)
+                codes[r * (cols / 2) + b * 16 + j] = (uint8_t)(c[2 * j] | (c[2 * j + 1] << 4));
+            if (wdeq)
+                for (int i = 0; i < 32; ++i)
+                    wdeq[r * cols + b * 32 + i] = oracle_dequant_value(c[i], S, 1.0f);
+        }
+    }
+}
+
+void oracle_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                          uint16_t* out)
+{
+    int64_t nb = cols / 32;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t i = 0; i < cols; ++i) {
+            uint8_t byte = codes[r * (cols / 2) + i / 2];
+            unsigned code = (i & 1) ? (byte >> 4) : (byte & 15u);
+            float S = oracle_e8m0_value(scales[r * nb + i / 32]);
+            out[r * cols + i] = oracle_dequant_value(code, S, 1.0f);
+        }
+}

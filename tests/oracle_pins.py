@@ -632,6 +632,104 @@ def check_fo6_zero_and_act(o):
         assert np.array_equal(c1[0], pc[t]) and np.array_equal(s1[0], sc[t]) and np.array_equal(d1[0], xd[t])
 
 
+# ---------------------------------------------------------------------------
+# FOCUS on MXFP4
+# ---------------------------------------------------------------------------
+
+def unpack_mx_scales(sb):
+    return np.exp2(sb.astype(np.float64) - 127.0)
+
+
+def check_mx_scale_closed_forms(o):
+    """OCP Microscaling block scale 2^(floor(log2 t) - 2): maxima 6*2^k and
+    4*2^k and 7.99*2^k give 2^k (byte 127 + k), 3.99*2^k gives 2^(k-1); zero
+    gives 1; the exponent clamps to [-127, 127]."""
+    for k in range(-100, 101, 7):
+        for mult, off in ((6.0, 0), (4.0, 0), (7.99, 0), (3.99, -1), (1.0, -2), (0.5, -3)):
+            t = np.float32(mult * 2.0 ** k)
+            assert o.mx_block_scale(t) == 127 + k + off, (mult, k)
+    assert o.mx_block_scale(0.0) == 127
+    assert o.mx_block_scale(2.0 ** -140) == 0
+    assert o.mx_block_scale(1.5 * 2.0 ** 127) == 127 + 125
+    assert o.mx_block_scale(3.0, 2.0) == 127 + 0  # t = a * m = 6
+    for b in range(0, 255):
+        assert o.e8m0_value(b) == np.float32(2.0 ** (b - 127))
+
+
+def _mx_fixed_case(rng, rows=40, nb=4):
+    """Blocks of 32 built as c * 2^k with one |c| in {4, 6}: floor(log2 max)
+    = k + 2, so the scale is 2^k and the codes are c, exactly."""
+    k = rng.integers(-100, 101, (rows, nb))
+    codes = rng.integers(0, 16, (rows, nb * 32)).astype(np.uint8)
+    pos = rng.integers(0, 32, (rows, nb))
+    top = rng.choice(np.array([6, 7], np.uint8), (rows, nb))
+    for r in range(rows):
+        for b in range(nb):
+            i = 32 * b + pos[r, b]
+            codes[r, i] = (codes[r, i] & 8) | top[r, b]
+    S = np.repeat(np.exp2(k.astype(np.float64)), 32, axis=1)
+    w = code_value(codes) * S
+    wb = torch_bf16_bits(w.astype(np.float32))
+    assert np.array_equal(bf16_float(wb).astype(np.float64), w)
+    wb = np.where(codes == 8, np.uint16(0x8000), wb).astype(np.uint16)
+    return (k + 127).astype(np.uint8), codes, wb
+
+
+def check_mx_fixed_points(o):
+    rng = np.random.default_rng(80)
+    sb, codes, wb = _mx_fixed_case(rng)
+    pc, sc, wd = o.mx_quantize(wb, None, None)
+    assert np.array_equal(sc, sb)
+    assert np.array_equal(unpack_codes(pc), codes)
+    assert np.array_equal(wd, wb)
+
+
+def check_mx_factor_and_subblocks(o):
+    """m_b = 2 doubles the scale (byte + 1) and halves the codes (E2M1(c/2),
+    ties to even); q = 0 (sigmoid 1/2) doubles the codes of exactly that
+    8-element sub-block, k = 0..3, through q[r, 4b + k]."""
+    rng = np.random.default_rng(81)
+    sb, codes, wb = _mx_fixed_case(rng, rows=24, nb=5)
+    m2 = rng.integers(0, 2, (24, 5)).astype(bool)
+    m = np.where(m2, 2.0, 1.0).astype(np.float32)
+    pc, sc, _ = o.mx_quantize(wb, m, None, dequant=False)
+    assert np.array_equal(sc, np.where(m2, sb + 1, sb))
+    want = codes.copy()
+    mask = np.repeat(m2, 32, axis=1)
+    want[mask] = ((codes & 8) | HALF_MAP[codes & 7])[mask]
+    assert np.array_equal(unpack_codes(pc), want)
+    half = rng.integers(0, 2, (24, 20)).astype(bool)
+    q = np.where(half, np.float32(0.0), np.float32(np.inf)).astype(np.float32)
+    pc, sc, _ = o.mx_quantize(wb, None, q, dequant=False)
+    assert np.array_equal(sc, sb)
+    mask8 = np.repeat(half, 8, axis=1)
+    want = np.where(mask8, (codes & 8) | DOUBLE_MAP[codes & 7], codes)
+    assert np.array_equal(unpack_codes(pc), want)
+
+
+def check_mx_plain_reduction(o):
+    """m = 1 with no relaxation is plain OCP MXFP4 round-to-nearest, written
+    independently here: shared exponent floor(log2 amax) - 2 from numpy's
+    frexp, elements scaled by an exact power of two, E2M1 by its decision
+    boundaries; dequantize(codes, scales) equals the fused w'."""
+    wb, _, _ = _random_case(82, rows=64, cols=512)
+    wb[3, 32:64] = 0
+    pc, sc, wd = o.mx_quantize(wb, None, None)
+    w = bf16_float(wb).astype(np.float32).reshape(64, 16, 32)
+    a = np.abs(w).max(axis=2)
+    _, e2 = np.frexp(a)
+    e = np.where(a == 0, 0, np.clip(e2 - 1 - 2, -127, 127))
+    x = np.clip(w * np.exp2(-e.astype(np.float64))[..., None], -6, 6).astype(np.float32)
+    ax = np.abs(x)
+    mag = ((ax > 0.25).astype(np.uint8) + (ax >= 0.75) + (ax > 1.25) + (ax >= 1.75)
+           + (ax > 2.5) + (ax >= 3.5) + (ax > 5)).astype(np.uint8)
+    want = ((np.signbit(x).astype(np.uint8) << 3) | mag).reshape(64, 512)
+    assert np.array_equal(sc, (e + 127).astype(np.uint8))
+    assert np.array_equal(unpack_codes(pc), want)
+    assert np.array_equal(o.mx_dequantize(pc, sc), wd)
+    assert np.all(sc[3, 1] == 127) and np.all(unpack_codes(pc)[3, 32:64] == 0)
+
+
 ALL_CHECKS = [
     check_e2m1_table, check_e2m1_nearest_dense, check_e4m3_vs_torch, check_e4m3_decode_vs_torch,
     check_bf16_vs_torch, check_sigmoid, check_expf_correctly_rounded, check_tensor_scale,
@@ -639,6 +737,7 @@ ALL_CHECKS = [
     check_s2_zero, check_amax_block_closed_form, check_error_bound, check_monotone,
     check_plain_rtn_reduction, check_dequantize_roundtrip, check_act_per_token,
     check_fo6_four_fixed_points, check_fo6_six_fixed_points, check_fo6_ties_keep_six,
-    check_fo6_never_worse_than_rtn,
+    check_fo6_never_worse_than_rtn, check_mx_scale_closed_forms, check_mx_fixed_points,
+    check_mx_factor_and_subblocks, check_mx_plain_reduction,
     check_fo6_zero_and_act,
 ]

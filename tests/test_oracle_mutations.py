@@ -52,6 +52,13 @@ MUTATIONS = [
     ("FourOverSix error without the square", "err = err + e * e;", "err = err + fabsf(e);"),
     ("FourOverSix per-token scale from row 0", "s2_out[t] = oracle_tensor_scale(x + t * hidden, hidden, NULL);",
      "s2_out[t] = oracle_tensor_scale(x, hidden, NULL);"),
+    ("MXFP4 scale rounds log2 to nearest", "int e = (e2 - 1) - 2;", "int e = (int)lrintf(log2f(t)) - 2;"),
+    ("MXFP4 scale uses emax 3", "int e = (e2 - 1) - 2;", "int e = (e2 - 1) - 3;"),
+    ("MXFP4 zero block gets byte 0", "if (t == 0.0f) return 127u;", "if (t == 0.0f) return 0u;"),
+    ("MXFP4 ignores m", "unsigned sb = oracle_mx_block_scale(a, mb);", "unsigned sb = oracle_mx_block_scale(a, 1.0f);"),
+    ("MXFP4 q indexed as NVFP4", "q[r * (4 * nb) + 4 * b + k]", "q[r * (4 * nb) + 2 * b + k]"),
+    ("MXFP4 32-block max over 16", "for (int i = 0; i < 32; ++i) {\n                float v = fabsf",
+     "for (int i = 0; i < 16; ++i) {\n                float v = fabsf"),
     ("block max over the first sub-block only", "for (int i = 0; i < 16; ++i) {\n                float v = fabsf",
      "for (int i = 0; i < 8; ++i) {\n                float v = fabsf"),
 ]
