@@ -45,6 +45,7 @@ B_QUANT = 2.0 + 0.25 + 0.5 + 0.5 + 0.0625          # W, m, q, codes, scales
 B_QUANT_DQ = B_QUANT + 2.0                          # + w'
 B_DEQUANT = 0.5 + 0.0625 + 2.0                      # codes, scales, out
 B_ACT = 2.0 + 0.5 + 0.0625                          # X, codes, scales (+4 B per token)
+B_MX = 2.0 + 4.0 / 32 + 0.5 + 0.5 + 1.0 / 32        # W, m per 32, q, codes, E8M0 scales
 
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "quantize_8b_traffic.json")
 
@@ -150,6 +151,17 @@ def main():
                for c in chunks]
     FB = [focus.quantize_fo6_many([W[i] for i in c], [S2[i] for i in c], outs=[OUT[i] for i in c],
                                   dequant=False, run=False) for c in chunks]
+    M32 = [synth.block_factor_lognormal((l.rows, l.cols // 32), seed=42, tensor_id=l.tid(1), device=dev)
+           for l in lins]
+    MXB = [focus.quantize_mx_many([W[i] for i in c], [M32[i] for i in c], [Q[i] for i in c],
+                                  outs=[focus.Quantized(OUT[i].codes, OUT[i].scales.view(-1)[:lins[i].numel // 32]
+                                                        .view(lins[i].rows, lins[i].cols // 32), OUT[i].deq, None)
+                                        for i in c], dequant=True, run=False) for c in chunks]
+    MXB_nodq = [focus.quantize_mx_many([W[i] for i in c], [M32[i] for i in c], [Q[i] for i in c],
+                                       outs=[focus.Quantized(OUT[i].codes,
+                                                             OUT[i].scales.view(-1)[:lins[i].numel // 32]
+                                                             .view(lins[i].rows, lins[i].cols // 32), None, None)
+                                             for i in c], dequant=False, run=False) for c in chunks]
     DB = [focus.dequantize_many([OUT[i].codes for i in c], [OUT[i].scales for i in c], [S2[i] for i in c],
                                 outs=[DEQ[i] for i in c], run=False) for c in chunks]
     nq = len(QB)
@@ -220,6 +232,8 @@ def main():
 
     t_q = time_calls(lambda: [b.run() for b in QB_nodq])
     t_f6 = time_calls(lambda: [b.run() for b in FB])
+    t_mx = time_calls(lambda: [b.run() for b in MXB])
+    t_mxn = time_calls(lambda: [b.run() for b in MXB_nodq])
     ACT6 = focus.quantize_act_per_token_fo6(X)
     t_a6 = time_calls(lambda: focus.quantize_act_per_token_fo6(X, out=ACT6), reps=20)
     torch.cuda.synchronize()
@@ -237,6 +251,8 @@ def main():
                                                       X.numel()),
         "quantize codes only (after the steps)": row(t_q, B_QUANT * n_weights, n_weights),
         "FourOverSix weights, codes only (after the steps)": row(t_f6, B_ACT * n_weights, n_weights),
+        "FOCUS on MXFP4 + w' (after the steps)": row(t_mx, (B_MX + 2.0) * n_weights, n_weights),
+        "FOCUS on MXFP4 codes only (after the steps)": row(t_mxn, B_MX * n_weights, n_weights),
         "FourOverSix act per token [8192,4096] (after the steps, cache-resident)":
             row(t_a6, B_ACT * X.numel() + 4 * X.shape[0], X.numel()),
     }

@@ -35,6 +35,7 @@ from ._lib import FocusError, FocusLibraryMissing, library_path  # noqa: F401
 
 __all__ = ["tensor_scale", "quantize", "dequantize", "quantize_act_per_token", "Quantized",
            "quantize_fo6", "quantize_act_per_token_fo6", "quantize_fo6_many",
+           "quantize_mx", "quantize_mx_many", "dequantize_mx",
            "tensor_scale_many", "quantize_many", "dequantize_many", "Batch",
            "FocusError", "FocusLibraryMissing", "abi_version", "library_path"]
 
@@ -223,6 +224,87 @@ def quantize_act_per_token_fo6(x: torch.Tensor, dequant: bool = False,
     _lib.check(_lib.lib().focus_quantize_act_per_token_fo6(_p(x), t, h, _p(out.codes), _p(out.scales),
                                                            _p(out.s2), _p(deq), _stream(x)))
     return Quantized(out.codes, out.scales, deq, out.s2)
+
+
+# ---------------------------------------------------------------------------
+# FOCUS on MXFP4
+# ---------------------------------------------------------------------------
+
+def _mx_outs(rows, cols, dev, dequant):
+    return Quantized(torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+                     torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev),
+                     torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) if dequant else None,
+                     None)
+
+
+def quantize_mx(w: torch.Tensor, m: Optional[torch.Tensor] = None, q: Optional[torch.Tensor] = None,
+                dequant: bool = True, out: Optional[Quantized] = None) -> Quantized:
+    """FOCUS on MXFP4 of W [rows, cols] (cols % 32 == 0): m [rows, cols/32] or
+    None, q [rows, cols/8] or None.  Returns codes, E8M0 scale bytes
+    [rows, cols/32], optional BF16 w' (s2 is None: MXFP4 has no tensor scale)."""
+    _check_dev("w", w, torch.bfloat16)
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [rows, cols]")
+    rows, cols = w.shape
+    dev = w.device
+    if cols % 32:
+        raise ValueError("cols must be a multiple of 32")
+    if m is not None:
+        _check_dev("m", m, torch.float32, dev)
+        if tuple(m.shape) != (rows, cols // 32):
+            raise ValueError(f"m must be [{rows}, {cols // 32}]")
+    if q is not None:
+        _check_dev("q", q, torch.float32, dev)
+        if tuple(q.shape) != (rows, cols // 8):
+            raise ValueError(f"q must be [{rows}, {cols // 8}]")
+    if out is None:
+        out = _mx_outs(rows, cols, dev, dequant)
+    deq = out.deq if dequant else None
+    _lib.check(_lib.lib().focus_quantize_mx(_p(w), rows, cols, _p(m), _p(q), _p(out.codes),
+                                            _p(out.scales), _p(deq), _stream(w)))
+    return Quantized(out.codes, out.scales, deq, None)
+
+
+def dequantize_mx(codes: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _check_dev("codes", codes, torch.uint8)
+    dev = codes.device
+    _check_dev("scales", scales, torch.uint8, dev)
+    rows, half = codes.shape
+    cols = 2 * half
+    if tuple(scales.shape) != (rows, cols // 32):
+        raise ValueError(f"scales must be [{rows}, {cols // 32}]")
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    _check_dev("out", out, torch.bfloat16, dev)
+    _lib.check(_lib.lib().focus_dequantize_mx(_p(codes), _p(scales), rows, cols, _p(out), _stream(codes)))
+    return out
+
+
+def quantize_mx_many(ws, ms, qs, outs=None, dequant: bool = True, run: bool = True) -> Batch:
+    """Batched FOCUS on MXFP4 (m [rows, cols/32] entries may be None)."""
+    n = len(ws)
+    dev = ws[0].device
+    arr = (_lib.QuantDesc * n)()
+    res = []
+    for i in range(n):
+        w, m, q = ws[i], ms[i], qs[i]
+        _check_dev(f"ws[{i}]", w, torch.bfloat16, dev)
+        rows, cols = w.shape
+        if cols % 32:
+            raise ValueError("cols must be a multiple of 32")
+        if m is not None:
+            _check_dev(f"ms[{i}]", m, torch.float32, dev)
+            assert tuple(m.shape) == (rows, cols // 32)
+        if q is not None:
+            _check_dev(f"qs[{i}]", q, torch.float32, dev)
+            assert tuple(q.shape) == (rows, cols // 8)
+        o = outs[i] if outs is not None else _mx_outs(rows, cols, dev, dequant)
+        deq = o.deq if dequant else None
+        res.append(Quantized(o.codes, o.scales, deq, None))
+        arr[i] = _lib.QuantDesc(_p(w), rows, cols, _p(m), _p(q), 0, _p(o.codes), _p(o.scales), _p(deq))
+    b = Batch("focus_quantize_mx_many", arr, (list(ws), list(ms), list(qs), res), dev)
+    b.outs = res
+    return b.run() if run else b
 
 
 # ---------------------------------------------------------------------------

@@ -43,6 +43,9 @@ _SIGNATURES = {
     "focus_quantize_many": (_INT, [ct.POINTER(QuantDesc), _INT, _VP]),
     "focus_dequantize_many": (_INT, [ct.POINTER(DequantDesc), _INT, _VP]),
     "focus_quantize_fo6_many": (_INT, [ct.POINTER(QuantDesc), _INT, _VP]),
+    "focus_quantize_mx": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "focus_quantize_mx_many": (_INT, [ct.POINTER(QuantDesc), _INT, _VP]),
+    "focus_dequantize_mx": (_INT, [_VP, _VP, _I64, _I64, _VP, _VP]),
 }
 
 EXPORTED = tuple(_SIGNATURES)

@@ -59,11 +59,25 @@ int check_scale(const focus_scale_desc& d) {
     return FOCUS_OK;
 }
 
+// MXFP4: cols % 32 == 0, no tensor scale (s2 is ignored and may be NULL).
+int check_quant_mx(const focus_quant_desc& d) {
+    int st = shape_2d(d.rows, d.cols);
+    if (st != FOCUS_OK) return st;
+    if (d.cols % 32 != 0) return FOCUS_ERR_SHAPE;
+    if (d.rows == 0 || d.cols == 0) return FOCUS_OK;
+    if (!d.w_bf16 || !d.codes || !d.scales) return FOCUS_ERR_NULL;
+    if (!aligned(d.w_bf16, 16) || !aligned(d.m, 4) || !aligned(d.q, 8) || !aligned(d.codes, 8) ||
+        !aligned(d.w_deq, 16))
+        return FOCUS_ERR_ALIGN;
+    return FOCUS_OK;
+}
+
 int quant_key(const focus_quant_desc& d) {
     return (d.m ? 4 : 0) | (d.q ? 2 : 0) | (d.w_deq ? 1 : 0);
 }
 
-int run_quantize(const focus_quant_desc* descs, int n, hipStream_t stream, bool fo6 = false) {
+// mode 0: FOCUS NVFP4, 1: FourOverSix, 2: FOCUS on MXFP4.
+int run_quantize(const focus_quant_desc* descs, int n, hipStream_t stream, int mode = 0) {
     focus::QuantBatch bt;
     int key = -1;
     bt.n = 0;
@@ -71,7 +85,9 @@ int run_quantize(const focus_quant_desc* descs, int n, hipStream_t stream, bool 
         const bool end = (i == n);
         const bool skip = !end && (descs[i].rows == 0 || descs[i].cols == 0);
         if (skip) continue;
-        const int k = end ? -1 : (fo6 ? 8 | (descs[i].w_deq ? 1 : 0) : quant_key(descs[i]));
+        const int k = end ? -1
+                          : (mode == 1 ? 8 | (descs[i].w_deq ? 1 : 0)
+                                       : (mode == 2 ? 16 : 0) | quant_key(descs[i]));
         if (bt.n > 0 && (end || k != key || bt.n == focus::kBatch)) {
             int st = hip_status(focus::launch_quantize(bt, key, stream));
             if (st != FOCUS_OK) return st;
@@ -93,14 +109,14 @@ int run_quantize(const focus_quant_desc* descs, int n, hipStream_t stream, bool 
     return FOCUS_OK;
 }
 
-int run_dequantize(const focus_dequant_desc* descs, int n, hipStream_t stream) {
+int run_dequantize(const focus_dequant_desc* descs, int n, hipStream_t stream, bool mx = false) {
     focus::DequantBatch bt;
     bt.n = 0;
     for (int i = 0; i <= n; ++i) {
         const bool end = (i == n);
         if (!end && (descs[i].rows == 0 || descs[i].cols == 0)) continue;
         if (bt.n > 0 && (end || bt.n == focus::kBatch)) {
-            int st = hip_status(focus::launch_dequantize(bt, stream));
+            int st = hip_status(focus::launch_dequantize(bt, mx, stream));
             if (st != FOCUS_OK) return st;
             bt.n = 0;
         }
@@ -231,7 +247,7 @@ int focus_quantize_fo6(const uint16_t* w_bf16, int64_t rows, int64_t cols, const
     const focus_quant_desc d = {w_bf16, rows, cols, nullptr, nullptr, s2, codes, scales, w_deq};
     int st = check_quant(d);
     if (st != FOCUS_OK) return st;
-    return run_quantize(&d, 1, (hipStream_t)stream, true);
+    return run_quantize(&d, 1, (hipStream_t)stream, 1);
 }
 
 int focus_quantize_fo6_many(const focus_quant_desc* descs, int n, void* stream) {
@@ -242,7 +258,38 @@ int focus_quantize_fo6_many(const focus_quant_desc* descs, int n, void* stream) 
         if (st != FOCUS_OK) return st;
         if (descs[i].m || descs[i].q) return FOCUS_ERR_RANGE;
     }
-    return run_quantize(descs, n, (hipStream_t)stream, true);
+    return run_quantize(descs, n, (hipStream_t)stream, 1);
+}
+
+int focus_quantize_mx(const uint16_t* w_bf16, int64_t rows, int64_t cols, const float* m,
+                      const float* q, uint8_t* codes, uint8_t* scales, uint16_t* w_deq,
+                      void* stream) {
+    const focus_quant_desc d = {w_bf16, rows, cols, m, q, nullptr, codes, scales, w_deq};
+    int st = check_quant_mx(d);
+    if (st != FOCUS_OK) return st;
+    return run_quantize(&d, 1, (hipStream_t)stream, 2);
+}
+
+int focus_quantize_mx_many(const focus_quant_desc* descs, int n, void* stream) {
+    if (n < 0) return FOCUS_ERR_RANGE;
+    if (n > 0 && !descs) return FOCUS_ERR_NULL;
+    for (int i = 0; i < n; ++i) {
+        int st = check_quant_mx(descs[i]);
+        if (st != FOCUS_OK) return st;
+    }
+    return run_quantize(descs, n, (hipStream_t)stream, 2);
+}
+
+int focus_dequantize_mx(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                        uint16_t* out, void* stream) {
+    int st = shape_2d(rows, cols);
+    if (st != FOCUS_OK) return st;
+    if (cols % 32 != 0) return FOCUS_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return FOCUS_OK;
+    if (!codes || !scales || !out) return FOCUS_ERR_NULL;
+    if (!aligned(codes, 8) || !aligned(out, 16)) return FOCUS_ERR_ALIGN;
+    const focus_dequant_desc d = {codes, scales, nullptr, 0, rows, cols, out};
+    return run_dequantize(&d, 1, (hipStream_t)stream, true);
 }
 
 int focus_quantize_act_per_token_fo6(const uint16_t* x_bf16, int64_t tokens, int64_t hidden,

@@ -231,6 +231,41 @@ __device__ __forceinline__ void fo6_block(uint4 a, uint4 b, float s2, double rde
     }
 }
 
+// One 16-element half of an MXFP4 32-block whose scale S (a power of two) is
+// already known: the codes of its two relaxed 8-element sub-blocks (q0, q1),
+// w' = BF16(c*S).  Same interface as quantize_block otherwise.
+template <bool HAS_SIG, bool DEQ>
+__device__ __forceinline__ void mx_half_block(uint4 a, uint4 b, float S, float q0, float q1,
+                                              const double* tab, uint2* codes_out, uint4& deq0,
+                                              uint4& deq1) {
+    const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float f[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        f[2 * i] = bf16_lo(v[i]);
+        f[2 * i + 1] = bf16_hi(v[i]);
+    }
+    float sig0 = 1.0f, sig1 = 1.0f;
+    if (HAS_SIG) {
+        sig0 = sigmoid_cr(q0, tab);
+        sig1 = sigmoid_cr(q1, tab);
+    }
+    const uint32_t c0 = encode8(f, S * sig0);
+    const uint32_t c1 = encode8(f + 8, S * sig1);
+    st8(codes_out, 0, make_uint2(c0, c1));
+    if (DEQ) {
+        deq0 = dequant8(c0, S, 1.0f);
+        deq1 = dequant8(c1, S, 1.0f);
+    }
+}
+
+// Maximum of two lanes' values within each lane pair (2j, 2j+1): DPP
+// quad permutation [1, 0, 3, 2].
+__device__ __forceinline__ uint32_t pair_max_u32(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+    return max(v, o);
+}
+
 // ---------------------------------------------------------------------------
 // batches: up to kBatch tensors per launch, described in the kernel argument
 // segment (structure of arrays, about 2.3 KB).  Work is cut into tiles of
@@ -256,8 +291,12 @@ __device__ __forceinline__ int find_tensor(const int64_t* tile_start, int n, int
 constexpr int kQuantU = 2;
 constexpr int64_t kQuantTile = (int64_t)kThreads * kQuantU;
 
-template <bool HAS_M, bool HAS_Q, bool DEQ, bool FO6 = false>
+// MODE 0: FOCUS NVFP4; 1: FourOverSix (m, q absent); 2: FOCUS on MXFP4 (lanes
+// 2j and 2j+1 share one 32-block: m[blk/2], scale byte stored by the even
+// lane, no tensor scale).
+template <bool HAS_M, bool HAS_Q, bool DEQ, int MODE = 0>
 __global__ __launch_bounds__(kThreads) void k_quantize(QuantBatch bt, int64_t ntiles) {
+    constexpr bool FO6 = MODE == 1, MX = MODE == 2;
     __shared__ uint4 xch[DEQ ? kThreads / 64 : 1][128];
     constexpr bool kLdsLoadW = LdsLoadW<DEQ>::value;
     __shared__ uint4 xchw[kLdsLoadW ? kThreads / 64 : 1][128];
@@ -270,12 +309,12 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QuantBatch bt, int64_t nt
         const uint4* __restrict__ w = bt.w[j];
         const float* __restrict__ m = bt.m[j];
         const float2* __restrict__ q = bt.q[j];
-        const float s2 = ld_uniform(bt.s2[j]);
-        const double rden = 1.0 / (double)(6.0f * s2);
+        const float s2 = MX ? 1.0f : ld_uniform(bt.s2[j]);
+        const double rden = MX ? 0.0 : 1.0 / (double)(6.0f * s2);
         const double rden4 = FO6 ? 1.0 / (double)(4.0f * s2) : 0.0;
         const int64_t nblk = bt.nblk[j];
         const int64_t tile0 = (tile - bt.tile_start[j]) * kQuantTile;
-        uint4 va[kQuantU], vb[kQuantU];
+        uint4 va[kQuantU] = {}, vb[kQuantU] = {};
         float mb[kQuantU];
         float2 qq[kQuantU];
 #pragma unroll
@@ -292,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QuantBatch bt, int64_t nt
                 vb[k] = ld16(w, 2 * blk + 1);
             }
             if (blk < nblk) {
-                mb[k] = HAS_M ? ld4f(m, blk) : 1.0f;
+                mb[k] = HAS_M ? ld4f(m, MX ? blk >> 1 : blk) : 1.0f;
                 qq[k] = HAS_Q ? ld8f(q, blk) : make_float2(0.0f, 0.0f);
             }
         }
@@ -302,8 +341,17 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QuantBatch bt, int64_t nt
             const int64_t blk = first + lane;
             if (kLdsLoadW && first < nblk) wave_gather_blocks(va[k], vb[k], xchw[wave], lane);
             uint4 d0 = make_uint4(0, 0, 0, 0), d1 = d0;
+            uint32_t mx_sb = 0;
+            if (MX) {  // all lanes: the pair exchange needs both partners
+                const uint32_t am = pair_max_u32(__float_as_uint(block_amax_bits(va[k], vb[k])));
+                mx_sb = mx_scale_byte(__uint_as_float(am) * (blk < nblk ? mb[k] : 1.0f));
+            }
             if (blk < nblk) {
-                if (FO6)
+                if (MX) {
+                    mx_half_block<HAS_Q, DEQ>(va[k], vb[k], e8m0_value(mx_sb), qq[k].x, qq[k].y, tab,
+                                              bt.codes[j] + blk, d0, d1);
+                    if ((lane & 1) == 0) bt.scales[j][blk >> 1] = (uint8_t)mx_sb;
+                } else if (FO6)
                     fo6_block<DEQ>(va[k], vb[k], s2, rden, rden4, bt.codes[j] + blk,
                                    bt.scales[j] + blk, d0, d1);
                 else
@@ -323,6 +371,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QuantBatch bt, int64_t nt
 
 constexpr int64_t kDeqTile = (int64_t)kThreads * 2;
 
+// MX: E8M0 scale byte per 32 elements (per pair of 16-element blocks), no s2.
+template <bool MX>
 __global__ __launch_bounds__(kThreads) void k_dequantize(DequantBatch bt, int64_t ntiles) {
     __shared__ uint4 xch[kThreads / 64][128];
     const int lane = threadIdx.x & 63;
@@ -343,10 +393,12 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(DequantBatch bt, int64_
             const int64_t blk = tile0 + (int64_t)k * kThreads + threadIdx.x;
             if (blk < nblk) {
                 c[k] = ld8u(codes, blk);
-                sb[k] = scales[blk];
+                sb[k] = scales[MX ? blk >> 1 : blk];
             }
         }
-        if (per_row) {  // uniform branch: one s2 per row (activations)
+        if (MX) {
+            s2v[0] = s2v[1] = 1.0f;
+        } else if (per_row) {  // uniform branch: one s2 per row (activations)
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 const int64_t blk = tile0 + (int64_t)k * kThreads + threadIdx.x;
@@ -362,7 +414,7 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(DequantBatch bt, int64_
             const int64_t blk = first + lane;
             uint4 d0 = make_uint4(0, 0, 0, 0), d1 = d0;
             if (blk < nblk) {
-                const float S = e4m3_any_value(sb[k]);
+                const float S = MX ? e8m0_value(sb[k]) : e4m3_any_value(sb[k]);
                 d0 = dequant8(c[k].x, S, s2v[k]);
                 d1 = dequant8(c[k].y, S, s2v[k]);
             }
@@ -595,23 +647,39 @@ hipError_t launch_quantize(QuantBatch& bt, int key, hipStream_t stream) {
         FOCUS_Q_CASE(7, true, true, true)
 #undef FOCUS_Q_CASE
         case 8:
-            hipLaunchKernelGGL((k_quantize<false, false, false, true>), grid, block, 0, stream, bt, t);
+            hipLaunchKernelGGL((k_quantize<false, false, false, 1>), grid, block, 0, stream, bt, t);
             break;
         case 9:
-            hipLaunchKernelGGL((k_quantize<false, false, true, true>), grid, block, 0, stream, bt, t);
+            hipLaunchKernelGGL((k_quantize<false, false, true, 1>), grid, block, 0, stream, bt, t);
             break;
+#define FOCUS_MX_CASE(K, HM, HQ, DQ)                                                            \
+    case 16 + K:                                                                                \
+        hipLaunchKernelGGL((k_quantize<HM, HQ, DQ, 2>), grid, block, 0, stream, bt, t);        \
+        break;
+        FOCUS_MX_CASE(0, false, false, false)
+        FOCUS_MX_CASE(1, false, false, true)
+        FOCUS_MX_CASE(2, false, true, false)
+        FOCUS_MX_CASE(3, false, true, true)
+        FOCUS_MX_CASE(4, true, false, false)
+        FOCUS_MX_CASE(5, true, false, true)
+        FOCUS_MX_CASE(6, true, true, false)
+        FOCUS_MX_CASE(7, true, true, true)
+#undef FOCUS_MX_CASE
     }
     return hipGetLastError();
 }
 
-hipError_t launch_dequantize(DequantBatch& bt, hipStream_t stream) {
+hipError_t launch_dequantize(DequantBatch& bt, bool mx, hipStream_t stream) {
     int64_t t = 0;
     for (int j = 0; j < bt.n; ++j) {
         bt.tile_start[j] = t;
         t += (bt.nblk[j] + kDeqTile - 1) / kDeqTile;
     }
     bt.tile_start[bt.n] = t;
-    hipLaunchKernelGGL(k_dequantize, dim3(grid_for_tiles(t)), dim3(kThreads), 0, stream, bt, t);
+    if (mx)
+        hipLaunchKernelGGL(k_dequantize<true>, dim3(grid_for_tiles(t)), dim3(kThreads), 0, stream, bt, t);
+    else
+        hipLaunchKernelGGL(k_dequantize<false>, dim3(grid_for_tiles(t)), dim3(kThreads), 0, stream, bt, t);
     return hipGetLastError();
 }
 

@@ -231,6 +231,26 @@ __device__ __forceinline__ uint32_t sign_codes8(uint4 v) {
 }
 
 // ---------------------------------------------------------------------------
+// MXFP4 (FOCUS on 32-element blocks with an E8M0 scale)
+// ---------------------------------------------------------------------------
+
+// E8M0 byte of the scaled block maximum t = max|w_b| * m_b: the OCP
+// Microscaling rule 2^(floor(log2 t) - 2), exponent clamped to [-127, 127];
+// t == 0 -> 1 (byte 127).  The hardware frexp exponent gives floor(log2 t) + 1
+// for every finite t, subnormals included.
+__device__ __forceinline__ uint32_t mx_scale_byte(float t) {
+    if (t == 0.0f) return 127u;
+    int e = __builtin_amdgcn_frexp_expf(t) - 1 - 2;
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    return (uint32_t)(e + 127);
+}
+
+// Value of an E8M0 byte 0..254 (2^(b-127); 2^-127 is a binary32 subnormal).
+__device__ __forceinline__ float e8m0_value(uint32_t b) {
+    return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+}
+
+// ---------------------------------------------------------------------------
 // FourOverSix: the block scale maps the block maximum to 6 or to 4, whichever
 // quantizes the block with the lower binary32 squared error (summed in element
 // order; the 4-candidate only when strictly lower).  m = 1, no relaxation.

@@ -150,6 +150,29 @@ int focus_quantize_act_per_token_fo6(const uint16_t* x_bf16, int64_t tokens, int
                                      uint16_t* x_deq, void* stream);
 
 /*
+ * FOCUS on MXFP4 (the technical summary of the FOCUS paper, section
+ * "Methodologie": the method on MXFP4's 32-element blocks with an E8M0 scale
+ * and relaxed sub-blocks of 8).  Readings where the pages are silent: block
+ * scale = the OCP Microscaling rule applied to the scaled maximum,
+ * S_b = 2^(floor(log2(max|w_b| * m_b)) - 2), exponent clamped to [-127, 127],
+ * a zero scaled maximum giving 1; no tensor scale;
+ * c_i = E2M1(clamp(w_i / (S_b * sigmoid(q_k)), -6, 6)); w' = BF16(c * S_b).
+ *   w_bf16  [rows, cols] BF16, cols % 32 == 0, 16-byte aligned.
+ *   m       [rows, cols/32] FP32 or NULL;  q [rows, cols/8] FP32 or NULL
+ *           (sub-block k = 0..3 of block b: q[r, 4b + k]).
+ *   codes   [rows, cols/2] (element 2j low nibble);  scales [rows, cols/32]
+ *           E8M0 bytes (exponent + 127);  w_deq [rows, cols] BF16 or NULL.
+ * focus_quantize_mx_many takes focus_quant_desc entries whose s2 is ignored.
+ * focus_dequantize_mx: out = BF16(c * 2^(byte - 127)).
+ */
+int focus_quantize_mx(const uint16_t* w_bf16, int64_t rows, int64_t cols, const float* m,
+                      const float* q, uint8_t* codes, uint8_t* scales, uint16_t* w_deq,
+                      void* stream);
+
+int focus_dequantize_mx(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                        uint16_t* out, void* stream);
+
+/*
  * Batched calls.  A model holds many linears (112, 224 or 560 for the Llama
  * sets); one launch per tensor leaves the GPU idle between short kernels.
  * These calls take a HOST array of descriptors (read during the call only,
@@ -196,6 +219,9 @@ int focus_dequantize_many(const focus_dequant_desc* descs, int n, void* stream);
 /* Batched FourOverSix of weights: descriptors as for focus_quantize_many with
  * m and q NULL (FOCUS_ERR_RANGE otherwise). */
 int focus_quantize_fo6_many(const focus_quant_desc* descs, int n, void* stream);
+
+/* Batched FOCUS on MXFP4 (cols % 32 == 0; s2 ignored). */
+int focus_quantize_mx_many(const focus_quant_desc* descs, int n, void* stream);
 
 #ifdef __cplusplus
 }

@@ -170,3 +170,16 @@ def test_fo6_validation(lib):
     assert lib.focus_quantize_fo6_many((QD * 1)(with_m), 1, None) == ERR_RANGE
     assert lib.focus_quantize_act_per_token_fo6(FAKE, 4, 64, None, FAKE, FAKE, None, None) == ERR_NULL
     assert lib.focus_quantize_act_per_token_fo6(FAKE + 2, 4, 64, FAKE, FAKE, FAKE, None, None) == ERR_ALIGN
+
+
+def test_mx_validation(lib):
+    QD = _lib.QuantDesc
+    q = lib.focus_quantize_mx
+    assert q(FAKE, 4, 48, None, None, FAKE, FAKE, None, None) == ERR_SHAPE  # cols % 32
+    assert q(None, 4, 64, None, None, FAKE, FAKE, None, None) == ERR_NULL
+    assert q(FAKE, 4, 64, None, None, FAKE + 4, FAKE, None, None) == ERR_ALIGN
+    assert q(FAKE, 0, 64, None, None, None, None, None, None) == OK
+    assert lib.focus_quantize_mx_many((QD * 1)(QD(FAKE, 4, 48, None, None, None, FAKE, FAKE, None)), 1,
+                                      None) == ERR_SHAPE
+    assert lib.focus_dequantize_mx(FAKE, FAKE, 2, 48, FAKE, None) == ERR_SHAPE
+    assert lib.focus_dequantize_mx(FAKE, None, 2, 64, FAKE, None) == ERR_NULL

@@ -503,3 +503,104 @@ def test_fo6_many_matches_single(focus, orc):
         torch.cuda.synchronize()
         assert torch.equal(b.outs[i].codes, single.codes) and torch.equal(b.outs[i].scales, single.scales)
         assert torch.equal(b.outs[i].deq.view(torch.int16), single.deq.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# FOCUS on MXFP4
+# ---------------------------------------------------------------------------
+
+def run_mx(focus, wb, m=None, q=None, dequant=True):
+    w = torch.from_numpy(np.ascontiguousarray(wb).view(np.int16).copy()).view(torch.bfloat16).to(DEV)
+    md = None if m is None else torch.from_numpy(np.ascontiguousarray(m)).to(DEV)
+    qd = None if q is None else torch.from_numpy(np.ascontiguousarray(q)).to(DEV)
+    res = focus.quantize_mx(w, md, qd, dequant=dequant)
+    torch.cuda.synchronize()
+    back = focus.dequantize_mx(res.codes, res.scales)
+    torch.cuda.synchronize()
+    return (res.codes.cpu().numpy(), res.scales.cpu().numpy(),
+            None if res.deq is None else np_bits(res.deq), np_bits(back))
+
+
+def check_mx(focus, orc, wb, m=None, q=None, dequant=True, label=""):
+    codes, scales, deq, back = run_mx(focus, wb, m, q, dequant)
+    c, s, d = orc.mx_quantize(wb, m, q, dequant=True)
+    assert np.array_equal(scales, s), f"{label}: {np.count_nonzero(scales != s)} scale bytes differ"
+    nbad = np.count_nonzero(parity.unpack(codes) != parity.unpack(c))
+    assert nbad <= int(1e-6 * wb.size), f"{label}: {nbad} codes differ"
+    if nbad == 0:
+        if dequant:
+            assert np.array_equal(deq, d), label
+        assert np.array_equal(back, d), label
+    return nbad
+
+
+def test_mx_constructed_cases(focus, orc):
+    rng = np.random.default_rng(90)
+    sb, codes, wb = pins._mx_fixed_case(rng)
+    assert check_mx(focus, orc, wb, label="mx fixed points") == 0
+    m = np.where(rng.integers(0, 2, (wb.shape[0], wb.shape[1] // 32)) == 1, 2.0, 1.0).astype(np.float32)
+    qv = np.where(rng.integers(0, 2, (wb.shape[0], wb.shape[1] // 8)) == 1, 0.0, np.inf).astype(np.float32)
+    assert check_mx(focus, orc, wb, m, qv, label="mx m and q maps") == 0
+    wz = np.zeros((4, 64), np.uint16)
+    wz[1, 40] = 0x8000
+    assert check_mx(focus, orc, wz, label="mx zeros") == 0
+
+
+@pytest.mark.parametrize("shape", [(1, 32), (3, 96), (7, 4128), (33, 2080), (129, 1056)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("variant", ["m_q_dq", "m_q", "q_only", "plain_dq"])
+def test_mx_ragged(focus, orc, shape, variant):
+    rows, cols = shape
+    seed = rows * 31 + cols
+    wb = np_bits(synth.weights(shape, seed=seed, tensor_id=11, zero_block_p=0.02))
+    m = synth.block_factor_lognormal((rows, cols // 32), seed=seed, tensor_id=12).numpy() \
+        if "m" in variant.split("_") else None
+    q = synth.logits((rows, cols // 8), seed=seed, tensor_id=13).numpy() if "q" in variant else None
+    check_mx(focus, orc, wb, m, q, dequant=variant.endswith("dq"), label=f"mx {shape} {variant}")
+
+
+def test_mx_extreme(focus, orc):
+    rng = np.random.default_rng(91)
+    e = rng.integers(-140, 127, (32, 256)).astype(np.float64)
+    x = (rng.standard_normal((32, 256)) * np.exp2(e)).astype(np.float32)
+    x[0, 0] = 3.3e38
+    q = rng.uniform(-20, 30, (32, 32)).astype(np.float32)
+    m = np.exp(rng.standard_normal((32, 8)) * 3).astype(np.float32)
+    check_mx(focus, orc, pins.torch_bf16_bits(x), m, q, label="mx extreme")
+
+
+@pytest.mark.parametrize("shape", sorted(set(synth.LLAMA_8B.layer_shapes())), ids=lambda s: f"{s[0]}x{s[1]}")
+def test_mx_full_size_sampled(focus, orc, shape):
+    rows, cols = shape
+    lin = next(l for l in synth.LLAMA_8B.linears() if (l.rows, l.cols) == shape)
+    w = synth.weights(shape, seed=42, tensor_id=lin.tid(0), device=DEV)
+    m = synth.block_factor_lognormal((rows, cols // 32), seed=42, tensor_id=lin.tid(1), device=DEV)
+    q = synth.logits((rows, cols // 8), seed=42, tensor_id=lin.tid(2), device=DEV)
+    res = focus.quantize_mx(w, m, q, dequant=True)
+    torch.cuda.synchronize()
+    idx = np.unique(np.concatenate([[0, rows - 1], np.random.default_rng(rows).integers(0, rows, 30)]))
+    it = torch.from_numpy(idx).to(DEV)
+    c, s, d = orc.mx_quantize(np_bits(w[it]), m[it].cpu().numpy(), q[it].cpu().numpy())
+    assert np.array_equal(res.scales[it].cpu().numpy(), s)
+    gc = parity.unpack(res.codes[it].cpu().numpy())
+    nbad = np.count_nonzero(gc != parity.unpack(c))
+    assert nbad <= int(1e-6 * gc.size)
+    if nbad == 0:
+        assert np.array_equal(np_bits(res.deq[it]), d)
+
+
+def test_mx_many_matches_single(focus, orc):
+    rng = np.random.default_rng(92)
+    ws, ms, qs = [], [], []
+    for i in range(37):
+        r, c = int(rng.integers(1, 60)), 32 * int(rng.integers(1, 40))
+        ws.append(synth.weights((r, c), seed=i, tensor_id=14).to(DEV))
+        ms.append(synth.block_factor_lognormal((r, c // 32), seed=i, tensor_id=15).to(DEV) if i % 3 else None)
+        qs.append(synth.logits((r, c // 8), seed=i, tensor_id=16).to(DEV) if i % 4 else None)
+    b = focus.quantize_mx_many(ws, ms, qs, dequant=True)
+    torch.cuda.synchronize()
+    for i in range(37):
+        single = focus.quantize_mx(ws[i], ms[i], qs[i], dequant=True)
+        torch.cuda.synchronize()
+        assert torch.equal(b.outs[i].codes, single.codes) and torch.equal(b.outs[i].scales, single.scales)
+        assert torch.equal(b.outs[i].deq.view(torch.int16), single.deq.view(torch.int16))
