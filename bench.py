@@ -55,9 +55,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["8b", "1b"], default="8b")
+    ap.add_argument("--workload", choices=["8b", "1b", "70b"], default="8b",
+                    help="8b (default): the Llama-3.1-8B-shaped set; 1b: Llama-3.2-1B-shaped; "
+                         "70b: Llama-3.1-70B-shaped, processed layer by layer with w' and the "
+                         "dequantized copy written to one reused per-layer buffer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows-fraction", type=float, default=0.5,
+    ap.add_argument("--cpu-rows-fraction", type=float, default=None,
                     help="fraction of the rows of layer 0 the CPU oracle quantizes")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="before the steps, copy a buffer of BYTES bytes three times (a plain copy "
@@ -104,7 +107,10 @@ def main():
     focus._lib.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    ws = synth.LLAMA_8B if args.workload == "8b" else synth.LLAMA_1B
+    ws = {"8b": synth.LLAMA_8B, "1b": synth.LLAMA_1B, "70b": synth.LLAMA_70B}[args.workload]
+    layered = args.workload == "70b"
+    if args.cpu_rows_fraction is None:
+        args.cpu_rows_fraction = 0.05 if layered else 0.5
     lins = ws.linears()
     n_weights = sum(l.numel for l in lins)
 
@@ -119,11 +125,24 @@ def main():
     X = synth.make_activations(device=dev)
     S2 = torch.empty((len(lins), 1), dtype=torch.float32, device=dev)
     AMAX = torch.empty((len(lins), 1), dtype=torch.float32, device=dev)
+    if layered:
+        # w' and the dequantized copy of one layer at a time: every layer's
+        # linears are views of one reused buffer each
+        per_layer = max(sum(l.numel for l in lins if l.layer == k) for k in range(ws.layers))
+        wdq_buf = torch.empty(per_layer, dtype=torch.bfloat16, device=dev)
+        deq_buf = torch.empty(per_layer, dtype=torch.bfloat16, device=dev)
+        WDQ, DEQ, off = [], [], {}
+        for l in lins:
+            o = off.get(l.layer, 0)
+            WDQ.append(wdq_buf[o:o + l.numel].view(l.rows, l.cols))
+            DEQ.append(deq_buf[o:o + l.numel].view(l.rows, l.cols))
+            off[l.layer] = o + l.numel
+    else:
+        WDQ = [torch.empty((l.rows, l.cols), dtype=torch.bfloat16, device=dev) for l in lins]
+        DEQ = [torch.empty((l.rows, l.cols), dtype=torch.bfloat16, device=dev) for l in lins]
     OUT = [focus.Quantized(torch.empty((l.rows, l.cols // 2), dtype=torch.uint8, device=dev),
                            torch.empty((l.rows, l.cols // 16), dtype=torch.uint8, device=dev),
-                           torch.empty((l.rows, l.cols), dtype=torch.bfloat16, device=dev),
-                           S2[i]) for i, l in enumerate(lins)]
-    DEQ = [torch.empty((l.rows, l.cols), dtype=torch.bfloat16, device=dev) for l in lins]
+                           WDQ[i], S2[i]) for i, l in enumerate(lins)]
     ACT = focus.quantize_act_per_token(X)
     torch.cuda.synchronize()
     gen_s = time.time() - t0
@@ -141,7 +160,10 @@ def main():
 
     # Prepared batched calls, 32 linears each: every quantize / dequantize
     # batch is exactly one kernel launch, every tensor-scale batch three.
-    chunks = [list(range(i, min(i + 32, nlin))) for i in range(0, nlin, 32)]
+    if layered:
+        chunks = [[i for i, l in enumerate(lins) if l.layer == k] for k in range(ws.layers)]
+    else:
+        chunks = [list(range(i, min(i + 32, nlin))) for i in range(0, nlin, 32)]
     TS = [focus.tensor_scale_many([W[i] for i in c], S2[c[0]:c[-1] + 1], AMAX[c[0]:c[-1] + 1], run=False)
           for c in chunks]
     QB = [focus.quantize_many([W[i] for i in c], [M[i] for i in c], [Q[i] for i in c], [S2[i] for i in c],
@@ -149,15 +171,17 @@ def main():
     QB_nodq = [focus.quantize_many([W[i] for i in c], [M[i] for i in c], [Q[i] for i in c],
                                    [S2[i] for i in c], outs=[OUT[i] for i in c], dequant=False, run=False)
                for c in chunks]
-    FB = [focus.quantize_fo6_many([W[i] for i in c], [S2[i] for i in c], outs=[OUT[i] for i in c],
+    extra_rows = not layered
+    FB = [] if not extra_rows else [focus.quantize_fo6_many([W[i] for i in c], [S2[i] for i in c], outs=[OUT[i] for i in c],
                                   dequant=False, run=False) for c in chunks]
-    M32 = [synth.block_factor_lognormal((l.rows, l.cols // 32), seed=42, tensor_id=l.tid(1), device=dev)
-           for l in lins]
-    MXB = [focus.quantize_mx_many([W[i] for i in c], [M32[i] for i in c], [Q[i] for i in c],
+    M32 = [] if not extra_rows else [
+        synth.block_factor_lognormal((l.rows, l.cols // 32), seed=42, tensor_id=l.tid(1), device=dev)
+        for l in lins]
+    MXB = [] if not extra_rows else [focus.quantize_mx_many([W[i] for i in c], [M32[i] for i in c], [Q[i] for i in c],
                                   outs=[focus.Quantized(OUT[i].codes, OUT[i].scales.view(-1)[:lins[i].numel // 32]
                                                         .view(lins[i].rows, lins[i].cols // 32), OUT[i].deq, None)
                                         for i in c], dequant=True, run=False) for c in chunks]
-    MXB_nodq = [focus.quantize_mx_many([W[i] for i in c], [M32[i] for i in c], [Q[i] for i in c],
+    MXB_nodq = [] if not extra_rows else [focus.quantize_mx_many([W[i] for i in c], [M32[i] for i in c], [Q[i] for i in c],
                                        outs=[focus.Quantized(OUT[i].codes,
                                                              OUT[i].scales.view(-1)[:lins[i].numel // 32]
                                                              .view(lins[i].rows, lins[i].cols // 32), None, None)
@@ -231,11 +255,12 @@ def main():
         return a.elapsed_time(b) / reps
 
     t_q = time_calls(lambda: [b.run() for b in QB_nodq])
-    t_f6 = time_calls(lambda: [b.run() for b in FB])
-    t_mx = time_calls(lambda: [b.run() for b in MXB])
-    t_mxn = time_calls(lambda: [b.run() for b in MXB_nodq])
-    ACT6 = focus.quantize_act_per_token_fo6(X)
-    t_a6 = time_calls(lambda: focus.quantize_act_per_token_fo6(X, out=ACT6), reps=20)
+    if extra_rows:
+        t_f6 = time_calls(lambda: [b.run() for b in FB])
+        t_mx = time_calls(lambda: [b.run() for b in MXB])
+        t_mxn = time_calls(lambda: [b.run() for b in MXB_nodq])
+        ACT6 = focus.quantize_act_per_token_fo6(X)
+        t_a6 = time_calls(lambda: focus.quantize_act_per_token_fo6(X, out=ACT6), reps=20)
     torch.cuda.synchronize()
 
     def row(ms, nbytes, units):
@@ -250,12 +275,15 @@ def main():
         "act per token [8192,4096] (step phase)": row(phase["act"], B_ACT * X.numel() + 4 * X.shape[0],
                                                       X.numel()),
         "quantize codes only (after the steps)": row(t_q, B_QUANT * n_weights, n_weights),
-        "FourOverSix weights, codes only (after the steps)": row(t_f6, B_ACT * n_weights, n_weights),
-        "FOCUS on MXFP4 + w' (after the steps)": row(t_mx, (B_MX + 2.0) * n_weights, n_weights),
-        "FOCUS on MXFP4 codes only (after the steps)": row(t_mxn, B_MX * n_weights, n_weights),
-        "FourOverSix act per token [8192,4096] (after the steps, cache-resident)":
-            row(t_a6, B_ACT * X.numel() + 4 * X.shape[0], X.numel()),
     }
+    if extra_rows:
+        rows.update({
+            "FourOverSix weights, codes only (after the steps)": row(t_f6, B_ACT * n_weights, n_weights),
+            "FOCUS on MXFP4 + w' (after the steps)": row(t_mx, (B_MX + 2.0) * n_weights, n_weights),
+            "FOCUS on MXFP4 codes only (after the steps)": row(t_mxn, B_MX * n_weights, n_weights),
+            "FourOverSix act per token [8192,4096] (after the steps, cache-resident)":
+                row(t_a6, B_ACT * X.numel() + 4 * X.shape[0], X.numel()),
+        })
 
     # ---- CPU baseline: the oracle on a bounded sample ----------------------
     cpu = None
@@ -263,7 +291,7 @@ def main():
         cpu = cpu_baseline(lins, W, M, Q, X, args.cpu_rows_fraction)
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "8b" else METRIC.replace("8B set", f"{args.workload.upper()} set"),
         "value": round(n_weights / (ms_step * 1e-3) / 1e9, 2),
         "unit": "Gweights/s",
         "n_gpus": 1,
@@ -278,7 +306,8 @@ def main():
         "config": {
             "workload": f"{ws.name}: {n_weights} BF16 weights; per step tensor_scale + quantize "
                         f"(codes, E4M3 scales, BF16 w') + dequantize for every linear, and per-token "
-                        f"activations X [8192, 4096]",
+                        f"activations X [8192, 4096]"
+                        + ("; w' and the dequantized copy to one reused per-layer buffer" if layered else ""),
             "weights": n_weights,
             "linears": nlin,
             "m": "LogNormal(0, 0.1)", "q": "N(6, 2)", "W": "N(0, %g) + 0.1%% outliers x20" % ws.std,
@@ -290,7 +319,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(),
+            "traffic": measured_traffic() if args.workload == "8b" else None,
             "bytes_per_weight": B_QUANT_DQ,
             "mean_launch_ms": round(mean_launch_ms, 5),
             "launches": len(q_launch_ms),
