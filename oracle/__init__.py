@@ -50,6 +50,9 @@ _SIGNATURES = {
     "oracle_expf_n": (None, [_f32p, _i64, _f32p]),
     "oracle_fo6_block": (_ct.c_uint, [_u16p, _f, _u8p]),
     "oracle_e8m0_value": (_f, [_ct.c_uint]),
+    "oracle_e0m3_round": (_ct.c_uint, [_f]),
+    "oracle_e0m3_value": (_f, [_ct.c_uint]),
+    "oracle_mixfp4_quantize": (None, [_u16p, _i64, _i64, _f, _u8p, _i64, _i64, _u8p, _u8p, _u16p]),
     "oracle_mx_block_scale": (_ct.c_uint, [_f, _f]),
     "oracle_mx_quantize": (None, [_u16p, _i64, _i64, _f32p, _f32p, _u8p, _u8p, _u16p]),
     "oracle_mx_dequantize": (None, [_u8p, _u8p, _i64, _i64, _u16p]),
@@ -277,6 +280,29 @@ class Oracle:
         out = _np.empty((rows, cols), _np.uint16)
         self.lib.oracle_mx_dequantize(_ptr(codes, _u8p), _ptr(scales, _u8p), rows, cols, _ptr(out, _u16p))
         return out
+
+    # ---- FlipQuant MixFP4 --------------------------------------------------------
+    def e0m3_round(self, x):
+        return self.lib.oracle_e0m3_round(float(x))
+
+    def e0m3_value(self, code):
+        return self.lib.oracle_e0m3_value(int(code))
+
+    def mixfp4_quantize(self, w_bits, s2, tile_map, tile_rows, tile_cols=64, dequant=True):
+        """MixFP4: W [rows, cols], per-tensor s2, tile_map [rows/tile_rows,
+        cols/tile_cols] (nonzero = E0M3 tile, else E2M1 with FourOverSix)."""
+        w_bits = _as(w_bits, _np.uint16)
+        rows, cols = w_bits.shape
+        assert cols % 16 == 0 and rows % tile_rows == 0 and cols % tile_cols == 0
+        tile_map = _as(_np.asarray(tile_map).astype(_np.uint8), _np.uint8)
+        assert tile_map.shape == (rows // tile_rows, cols // tile_cols)
+        codes = _np.empty((rows, cols // 2), _np.uint8)
+        scales = _np.empty((rows, cols // 16), _np.uint8)
+        wdeq = _np.empty((rows, cols), _np.uint16) if dequant else None
+        self.lib.oracle_mixfp4_quantize(_ptr(w_bits, _u16p), rows, cols, float(s2), _ptr(tile_map, _u8p),
+                                        tile_rows, tile_cols, _ptr(codes, _u8p), _ptr(scales, _u8p),
+                                        _ptr(wdeq, _u16p))
+        return codes, scales, wdeq
 
 
 _default = None

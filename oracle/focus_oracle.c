@@ -501,3 +501,91 @@ void oracle_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t r
             out[r * cols + i] = oracle_dequant_value(code, S, 1.0f);
         }
 }
+
+/* ---------- FlipQuant MixFP4 tile maps ---------------------------------- */
+
+/* "Llama-3.1-8B-Instruct FlipQuant MixFP4 maps", section "What this is": a
+ * map holds one bit per weight tile (8x64, 16x64 or 256x64, rows x input
+ * columns); a set bit stores the tile's 4-bit elements as E0M3 (uniform
+ * levels 0..7), a clear bit as E2M1 with FourOverSix; everything else is
+ * NVFP4 (16-element blocks, E4M3 block scale, FP32 tensor scale).  Readings
+ * where the page is silent:
+ *   - an E0M3 block's scale maps the block maximum to 7: t = a / (7*s2),
+ *     zero -> 1, clamp [2^-6, 448], E4M3;
+ *   - E0M3 code = sign bit (bit 3) | nearest integer 0..7 to |x| (ties to
+ *     the even integer), x = clamp(w / (S*s2), -7, 7);
+ *   - w' = BF16((c*S)*s2) with c the signed integer level;
+ *   - the map is row-major [rows/tile_rows, cols/tile_cols], one byte per
+ *     tile (nonzero = E0M3). */
+
+unsigned oracle_e0m3_round(float x)
+{
+    unsigned sign = (bits_from_f32(x) >> 31) & 1u;
+    double a = fabs((double)x);
+    unsigned best = 0;
+    double best_d = INFINITY;
+    for (unsigned k = 0; k < 8; ++k) {
+        double d = fabs(a - (double)k);
+        if (d < best_d || (d == best_d && (k & 1u) == 0u)) {
+            best_d = d;
+            best = k;
+        }
+    }
+    return (sign << 3) | best;
+}
+
+float oracle_e0m3_value(unsigned code)
+{
+    float v = (float)(code & 7u);
+    return (code & 8u) ? -v : v;
+}
+
+/* One E0M3 block: scale byte, 16 codes. */
+unsigned oracle_e0m3_block(const uint16_t* wb, float s2, uint8_t* codes16)
+{
+    if (s2 == 0.0f) {
+        for (int i = 0; i < 16; ++i) codes16[i] = (uint8_t)(((uint32_t)wb[i] >> 15) << 3);
+        return 0x38;
+    }
+    float a = 0.0f;
+    for (int i = 0; i < 16; ++i) {
+        float v = fabsf(oracle_bf16_value(wb[i]));
+        if (v > a) a = v;
+    }
+    float t = a / (7.0f * s2);
+    if (t == 0.0f) t = 1.0f;
+    t = fminf(fmaxf(t, 0x1p-6f), 448.0f);
+    unsigned sb = oracle_e4m3_round(t);
+    float S = oracle_e4m3_value(sb);
+    float d = S * s2;
+    for (int i = 0; i < 16; ++i) {
+        float x = oracle_bf16_value(wb[i]) / d;
+        x = fminf(fmaxf(x, -7.0f), 7.0f);
+        codes16[i] = (uint8_t)oracle_e0m3_round(x);
+    }
+    return sb;
+}
+
+void oracle_mixfp4_quantize(const uint16_t* w, int64_t rows, int64_t cols, float s2,
+                            const uint8_t* map, int64_t tile_rows, int64_t tile_cols,
+                            uint8_t* codes, uint8_t* scales, uint16_t* wdeq)
+{
+    int64_t nb = cols / 16, tiles_per_row = cols / tile_cols;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint16_t* wb = w + r * cols + b * 16;
+            int e0m3 = map[(r / tile_rows) * tiles_per_row + (b * 16) / tile_cols] != 0;
+            uint8_t c[16];
+            unsigned sb = e0m3 ? oracle_e0m3_block(wb, s2, c) : oracle_fo6_block(wb, s2, c);
+            float S = oracle_e4m3_value(sb);
+            scales[r * nb + b] = (uint8_t)sb;
+            for (int j = 0; j < 8; ++j)
+                codes[r * (cols / 2) + b * 8 + j] = (uint8_t)(c[2 * j] | (c[2 * j + 1] << 4));
+            if (wdeq)
+                for (int i = 0; i < 16; ++i) {
+                    float cv = e0m3 ? oracle_e0m3_value(c[i]) : oracle_e2m1_value(c[i]);
+                    wdeq[r * cols + b * 16 + i] = oracle_bf16_round((cv * S) * s2);
+                }
+        }
+    }
+}

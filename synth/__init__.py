@@ -119,6 +119,20 @@ def activations(shape: Tuple[int, int], *, seed: int, tensor_id: int = 0,
     return x.to(torch.bfloat16)
 
 
+def tile_map(rows: int, cols: int, tile: Tuple[int, int], *, frac: float, seed: int,
+             tensor_id: int, device="cpu") -> torch.Tensor:
+    """uint8 format map [rows/th, cols/tw], row-major: each tile is 1 (E0M3)
+    independently with probability frac, else 0 (E2M1)."""
+    th, tw = tile
+    g = generator(seed, tensor_id, device)
+    u = torch.rand((rows // th, cols // tw), generator=g, device=device)
+    return (u < frac).to(torch.uint8)
+
+
+# E0M3 fraction of each published map: E0M3 tiles / all tiles.
+MIXFP4_FRAC = {(8, 64): 83_771 / 13_631_488, (16, 64): 52_719 / 6_815_744, (256, 64): 9_447 / 425_984}
+
+
 # ---------------------------------------------------------------------------
 # weight sets
 # ---------------------------------------------------------------------------

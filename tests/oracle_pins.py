@@ -730,6 +730,64 @@ def check_mx_plain_reduction(o):
     assert np.all(sc[3, 1] == 127) and np.all(unpack_codes(pc)[3, 32:64] == 0)
 
 
+# ---------------------------------------------------------------------------
+# FlipQuant MixFP4
+# ---------------------------------------------------------------------------
+
+def check_e0m3_levels(o):
+    """E0M3 = uniform levels 0..7 (FlipQuant page, "What this is"): nearest
+    integer, ties to the even one, sign kept, after the clamp to [-7, 7]."""
+    table = [(0.0, 0), (0.5, 0), (np.nextafter(np.float32(0.5), 1), 1), (1.5, 2), (2.5, 2),
+             (3.5, 4), (4.5, 4), (5.5, 6), (6.5, 6), (np.nextafter(np.float32(6.5), 7), 7), (7.0, 7),
+             (-0.0, 8), (-0.3, 8), (-7.0, 15), (-2.5, 10), (3.49, 3)]
+    for x, code in table:
+        assert o.e0m3_round(float(np.float32(x))) == code, (x, code)
+    assert [o.e0m3_value(c) for c in (0, 7, 8, 13)] == [0.0, 7.0, -0.0, -5.0]
+
+
+def _e0m3_fixed_case(rng, rows=24, nb=8):
+    """Blocks c * S * s2 with integer levels c (|c| <= 7, one |c| = 7) and every
+    normal E4M3 scale: t = 7*S*s2 / (7*s2) = S exactly."""
+    sb = rng.integers(0x08, 0x7F, (rows, nb)).astype(np.uint8)
+    S = torch_e4m3_value(sb).astype(np.float64)
+    codes = rng.integers(0, 16, (rows, nb * 16)).astype(np.uint8)
+    pos = rng.integers(0, 16, (rows, nb))
+    for r in range(rows):
+        for b in range(nb):
+            codes[r, 16 * b + pos[r, b]] |= 7
+    lv = (codes & 7).astype(np.float64) * np.where(codes & 8, -1.0, 1.0)
+    w = lv * np.repeat(S, 16, axis=1) * float(S2_POW2)
+    wb = torch_bf16_bits(w.astype(np.float32))
+    assert np.array_equal(bf16_float(wb).astype(np.float64), w)
+    wb = np.where(codes == 8, np.uint16(0x8000), wb).astype(np.uint16)
+    return sb, codes, wb
+
+
+def check_mixfp4_maps(o):
+    """All-clear map = FourOverSix everywhere; all-set map = E0M3 everywhere,
+    whose fixed points return (S, levels) and w' = w; a random 8x64 map on a
+    16 x 256 tensor selects per tile exactly (a transposed or shifted tile
+    index fails)."""
+    rng = np.random.default_rng(95)
+    sb, codes, wb = _e0m3_fixed_case(rng, rows=16, nb=16)
+    ones = np.ones((2, 4), np.uint8)
+    pc, sc, wd = o.mixfp4_quantize(wb, S2_POW2, ones, 8, 64)
+    assert np.array_equal(sc, sb) and np.array_equal(unpack_codes(pc), codes) and np.array_equal(wd, wb)
+    wr, _, _ = _random_case(96, rows=16, cols=256)
+    s2, _ = o.tensor_scale(wr)
+    z = o.mixfp4_quantize(wr, s2, np.zeros((2, 4), np.uint8), 8, 64)
+    f = o.fo6_quantize(wr, s2)
+    assert all(np.array_equal(a, b) for a, b in zip(z, f))
+    e = o.mixfp4_quantize(wr, s2, ones, 8, 64)
+    tmap = np.array([[1, 1, 0, 0], [0, 0, 1, 0]], np.uint8)
+    mx = o.mixfp4_quantize(wr, s2, tmap, 8, 64)
+    sel_blocks = np.repeat(np.repeat(tmap, 8, axis=0), 4, axis=1).astype(bool)   # [16, 16] blocks
+    assert np.array_equal(mx[1], np.where(sel_blocks, e[1], f[1]))
+    sel_el = np.repeat(sel_blocks, 16, axis=1)
+    assert np.array_equal(unpack_codes(mx[0]), np.where(sel_el, unpack_codes(e[0]), unpack_codes(f[0])))
+    assert np.array_equal(mx[2], np.where(sel_el, e[2], f[2]))
+
+
 ALL_CHECKS = [
     check_e2m1_table, check_e2m1_nearest_dense, check_e4m3_vs_torch, check_e4m3_decode_vs_torch,
     check_bf16_vs_torch, check_sigmoid, check_expf_correctly_rounded, check_tensor_scale,
@@ -738,6 +796,6 @@ ALL_CHECKS = [
     check_plain_rtn_reduction, check_dequantize_roundtrip, check_act_per_token,
     check_fo6_four_fixed_points, check_fo6_six_fixed_points, check_fo6_ties_keep_six,
     check_fo6_never_worse_than_rtn, check_mx_scale_closed_forms, check_mx_fixed_points,
-    check_mx_factor_and_subblocks, check_mx_plain_reduction,
+    check_mx_factor_and_subblocks, check_mx_plain_reduction, check_e0m3_levels, check_mixfp4_maps,
     check_fo6_zero_and_act,
 ]

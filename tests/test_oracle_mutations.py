@@ -59,6 +59,14 @@ MUTATIONS = [
     ("MXFP4 q indexed as NVFP4", "q[r * (4 * nb) + 4 * b + k]", "q[r * (4 * nb) + 2 * b + k]"),
     ("MXFP4 32-block max over 16", "for (int i = 0; i < 32; ++i) {\n                float v = fabsf",
      "for (int i = 0; i < 16; ++i) {\n                float v = fabsf"),
+    ("E0M3 ties to odd", "if (d < best_d || (d == best_d && (k & 1u) == 0u)) {\n            best_d = d;\n            best = k;\n        }\n    }\n    return (sign << 3) | best;\n}\n\nfloat oracle_e0m3_value",
+     "if (d < best_d || (d == best_d && (k & 1u) == 1u)) {\n            best_d = d;\n            best = k;\n        }\n    }\n    return (sign << 3) | best;\n}\n\nfloat oracle_e0m3_value"),
+    ("E0M3 maps the block max to 6", "float t = a / (7.0f * s2);", "float t = a / (6.0f * s2);"),
+    ("E0M3 clamps at 6", "x = fminf(fmaxf(x, -7.0f), 7.0f);", "x = fminf(fmaxf(x, -6.0f), 6.0f);"),
+    ("MixFP4 tile index transposed", "map[(r / tile_rows) * tiles_per_row + (b * 16) / tile_cols]",
+     "map[((b * 16) / tile_cols) * (rows / tile_rows) + r / tile_rows]"),
+    ("MixFP4 map ignored", "int e0m3 = map[(r / tile_rows) * tiles_per_row + (b * 16) / tile_cols] != 0;",
+     "int e0m3 = 0;"),
     ("block max over the first sub-block only", "for (int i = 0; i < 16; ++i) {\n                float v = fabsf",
      "for (int i = 0; i < 8; ++i) {\n                float v = fabsf"),
 ]

@@ -54,6 +54,17 @@ def test_llama_8b_tiles_match_page():
     assert synth.LLAMA_8B.numel == 6_979_321_856
 
 
+def test_mixfp4_fractions_match_page():
+    c = page_counts()
+    for (th, tw), f in synth.MIXFP4_FRAC.items():
+        key = f"{th}x{tw}_llama_3_1_8b"
+        assert f == c["e0m3_tiles_" + key] / c["tiles_" + key]
+    m = synth.tile_map(4096, 14336, (8, 64), frac=0.25, seed=1, tensor_id=3)
+    assert m.shape == (512, 224) and m.dtype == torch.uint8
+    assert abs(m.float().mean().item() - 0.25) < 0.01
+    assert torch.equal(m, synth.tile_map(4096, 14336, (8, 64), frac=0.25, seed=1, tensor_id=3))
+
+
 def test_llama_70b_count():
     assert len(synth.LLAMA_70B.linears()) == 560
     assert synth.LLAMA_70B.numel == 68_451_041_280
