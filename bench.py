@@ -186,6 +186,14 @@ def main():
                                                              OUT[i].scales.view(-1)[:lins[i].numel // 32]
                                                              .view(lins[i].rows, lins[i].cols // 32), None, None)
                                              for i in c], dequant=False, run=False) for c in chunks]
+    MIX_TILES = [(8, 64), (16, 64), (256, 64)]
+    MAPS = {} if not extra_rows else {
+        t: [synth.tile_map(l.rows, l.cols, t, frac=synth.MIXFP4_FRAC[t], seed=42, tensor_id=l.tid(3), device=dev)
+            for l in lins] for t in MIX_TILES}
+    MIXB = {} if not extra_rows else {
+        t: [focus.quantize_mixfp4_many([W[i] for i in c], [MAPS[t][i] for i in c], [t] * len(c),
+                                       [S2[i] for i in c], outs=[OUT[i] for i in c], dequant=True, run=False)
+            for c in chunks] for t in MIX_TILES}
     DB = [focus.dequantize_many([OUT[i].codes for i in c], [OUT[i].scales for i in c], [S2[i] for i in c],
                                 outs=[DEQ[i] for i in c], run=False) for c in chunks]
     nq = len(QB)
@@ -261,6 +269,7 @@ def main():
         t_mxn = time_calls(lambda: [b.run() for b in MXB_nodq])
         ACT6 = focus.quantize_act_per_token_fo6(X)
         t_a6 = time_calls(lambda: focus.quantize_act_per_token_fo6(X, out=ACT6), reps=20)
+        t_mix = {t: time_calls(lambda t=t: [b.run() for b in MIXB[t]]) for t in MIX_TILES}
     torch.cuda.synchronize()
 
     def row(ms, nbytes, units):
@@ -284,6 +293,10 @@ def main():
             "FourOverSix act per token [8192,4096] (after the steps, cache-resident)":
                 row(t_a6, B_ACT * X.numel() + 4 * X.shape[0], X.numel()),
         })
+        for (th, tw) in MIX_TILES:
+            share = synth.MIXFP4_FRAC[(th, tw)]
+            rows[f"FlipQuant MixFP4 {th}x{tw} map ({100 * share:.2f}% E0M3 tiles) + w' (after the steps)"] = \
+                row(t_mix[(th, tw)], (B_ACT + 2.0 + 1.0 / (th * tw)) * n_weights, n_weights)
 
     # ---- CPU baseline: the oracle on a bounded sample ----------------------
     cpu = None

@@ -35,6 +35,7 @@ from ._lib import FocusError, FocusLibraryMissing, library_path  # noqa: F401
 
 __all__ = ["tensor_scale", "quantize", "dequantize", "quantize_act_per_token", "Quantized",
            "quantize_fo6", "quantize_act_per_token_fo6", "quantize_fo6_many",
+           "quantize_mixfp4", "quantize_mixfp4_many",
            "quantize_mx", "quantize_mx_many", "dequantize_mx",
            "tensor_scale_many", "quantize_many", "dequantize_many", "Batch",
            "FocusError", "FocusLibraryMissing", "abi_version", "library_path"]
@@ -303,6 +304,68 @@ def quantize_mx_many(ws, ms, qs, outs=None, dequant: bool = True, run: bool = Tr
         res.append(Quantized(o.codes, o.scales, deq, None))
         arr[i] = _lib.QuantDesc(_p(w), rows, cols, _p(m), _p(q), 0, _p(o.codes), _p(o.scales), _p(deq))
     b = Batch("focus_quantize_mx_many", arr, (list(ws), list(ms), list(qs), res), dev)
+    b.outs = res
+    return b.run() if run else b
+
+
+# ---------------------------------------------------------------------------
+# FlipQuant MixFP4
+# ---------------------------------------------------------------------------
+
+def _mix_desc(i, w, tile_map, tile_rows, tile_cols, s2, dev, dequant, out):
+    _check_dev(f"ws[{i}]", w, torch.bfloat16, dev)
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [rows, cols]")
+    rows, cols = w.shape
+    if tile_rows < 1 or tile_cols < 16 or tile_cols % 16 or rows % tile_rows or cols % tile_cols:
+        raise ValueError("tiles must divide the tensor and tile_cols must be a multiple of 16")
+    _check_dev(f"maps[{i}]", tile_map, torch.uint8, dev)
+    if tuple(tile_map.shape) != (rows // tile_rows, cols // tile_cols) or not tile_map.is_contiguous():
+        raise ValueError(f"map must be a contiguous [{rows // tile_rows}, {cols // tile_cols}] uint8 tensor")
+    _check_dev(f"s2s[{i}]", s2, torch.float32, dev)
+    if out is None:
+        out = Quantized(torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+                        torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
+                        torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) if dequant else None,
+                        s2)
+    elif out.codes.numel() != rows * cols // 2 or out.scales.numel() != rows * cols // 16:
+        raise ValueError(f"outs[{i}] has the wrong size")
+    deq = out.deq if dequant else None
+    res = Quantized(out.codes, out.scales, deq, s2)
+    return res, _lib.MixDesc(_p(w), rows, cols, _p(s2), _p(tile_map), tile_rows, tile_cols, _p(out.codes),
+                             _p(out.scales), _p(deq))
+
+
+def quantize_mixfp4(w: torch.Tensor, tile_map: torch.Tensor, tile_rows: int, tile_cols: int = 64,
+                    s2: Optional[torch.Tensor] = None, dequant: bool = True,
+                    out: Optional[Quantized] = None) -> Quantized:
+    """FlipQuant MixFP4 of W [rows, cols]: tile_map [rows/tile_rows,
+    cols/tile_cols] uint8 (nonzero = E0M3 levels 0..7, zero = E2M1 with
+    FourOverSix); per-tensor s2 computed with ``tensor_scale`` when None."""
+    _check_dev("w", w, torch.bfloat16)
+    if s2 is None:
+        s2, _ = tensor_scale(w)
+    res, d = _mix_desc(0, w, tile_map, tile_rows, tile_cols, s2, w.device, dequant, out)
+    _lib.check(_lib.lib().focus_quantize_mixfp4(d.w_bf16, d.rows, d.cols, d.s2, d.map, d.tile_rows,
+                                                d.tile_cols, d.codes, d.scales, d.w_deq, _stream(w)))
+    return res
+
+
+def quantize_mixfp4_many(ws, maps, tiles, s2s, outs=None, dequant: bool = True, run: bool = True) -> "Batch":
+    """Batched MixFP4: maps[i] and tiles[i] = (tile_rows, tile_cols) per
+    tensor; s2s one-element FP32 tensors; the result's ``outs`` holds the
+    outputs."""
+    n = len(ws)
+    if not (len(maps) == len(tiles) == len(s2s) == n):
+        raise ValueError("ws, maps, tiles, s2s must have the same length")
+    dev = ws[0].device
+    arr = (_lib.MixDesc * n)()
+    res = []
+    for i in range(n):
+        r, arr[i] = _mix_desc(i, ws[i], maps[i], tiles[i][0], tiles[i][1], s2s[i], dev, dequant,
+                              None if outs is None else outs[i])
+        res.append(r)
+    b = Batch("focus_quantize_mixfp4_many", arr, (list(ws), list(maps), list(s2s), res), dev)
     b.outs = res
     return b.run() if run else b
 

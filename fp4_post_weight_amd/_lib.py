@@ -30,6 +30,12 @@ class DequantDesc(ct.Structure):
                 ("rows", _I64), ("cols", _I64), ("out", _VP)]
 
 
+class MixDesc(ct.Structure):
+    _fields_ = [("w_bf16", _VP), ("rows", _I64), ("cols", _I64), ("s2", _VP), ("map", _VP),
+                ("tile_rows", _I64), ("tile_cols", _I64), ("codes", _VP), ("scales", _VP),
+                ("w_deq", _VP)]
+
+
 _SIGNATURES = {
     "focus_abi_version": (_INT, []),
     "focus_status_string": (ct.c_char_p, [_INT]),
@@ -46,6 +52,8 @@ _SIGNATURES = {
     "focus_quantize_mx": (_INT, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP]),
     "focus_quantize_mx_many": (_INT, [ct.POINTER(QuantDesc), _INT, _VP]),
     "focus_dequantize_mx": (_INT, [_VP, _VP, _I64, _I64, _VP, _VP]),
+    "focus_quantize_mixfp4": (_INT, [_VP, _I64, _I64, _VP, _VP, _I64, _I64, _VP, _VP, _VP, _VP]),
+    "focus_quantize_mixfp4_many": (_INT, [ct.POINTER(MixDesc), _INT, _VP]),
 }
 
 EXPORTED = tuple(_SIGNATURES)

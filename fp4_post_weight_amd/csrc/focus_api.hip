@@ -72,6 +72,70 @@ int check_quant_mx(const focus_quant_desc& d) {
     return FOCUS_OK;
 }
 
+// MixFP4: tiles of tile_rows x tile_cols (tile_cols a multiple of 16, both
+// dividing the shape); the kernel indexes blocks in 32 bits.
+constexpr int64_t kMaxMixBlocks = (int64_t)1 << 31;
+
+int check_quant_mix(const focus_mixfp4_desc& d) {
+    int st = shape_2d(d.rows, d.cols);
+    if (st != FOCUS_OK) return st;
+    if (d.tile_rows < 1 || d.tile_cols < 16 || d.tile_cols % 16 != 0) return FOCUS_ERR_SHAPE;
+    if (d.rows % d.tile_rows != 0 || d.cols % d.tile_cols != 0) return FOCUS_ERR_SHAPE;
+    if (d.rows == 0 || d.cols == 0) return FOCUS_OK;
+    if (d.rows * (d.cols / 16) >= kMaxMixBlocks) return FOCUS_ERR_RANGE;
+    if (!d.w_bf16 || !d.s2 || !d.map || !d.codes || !d.scales) return FOCUS_ERR_NULL;
+    if (!aligned(d.w_bf16, 16) || !aligned(d.s2, 4) || !aligned(d.codes, 8) || !aligned(d.w_deq, 16))
+        return FOCUS_ERR_ALIGN;
+    return FOCUS_OK;
+}
+
+// Multiplier and shift of focus::div_magic for a divisor 1 <= d < 2^31:
+// l = ceil(log2 d), shift = 31 + l, M = ceil(2^shift / d).
+void div_magic_host(uint32_t d, uint32_t& M, uint32_t& shift) {
+    uint32_t l = 0;
+    while (((uint64_t)1 << l) < d) ++l;
+    shift = 31 + l;
+    M = (uint32_t)((((uint64_t)1 << shift) + d - 1) / d);
+}
+
+int run_quantize_mix(const focus_mixfp4_desc* descs, int n, hipStream_t stream) {
+    focus::MixBatch bt;
+    bool deq = false;
+    bt.n = 0;
+    for (int i = 0; i <= n; ++i) {
+        const bool end = (i == n);
+        if (!end && (descs[i].rows == 0 || descs[i].cols == 0)) continue;
+        const bool k = !end && descs[i].w_deq != nullptr;
+        if (bt.n > 0 && (end || k != deq || bt.n == focus::kBatch)) {
+            int st = hip_status(focus::launch_quantize_mix(bt, deq, stream));
+            if (st != FOCUS_OK) return st;
+            bt.n = 0;
+        }
+        if (end) break;
+        const focus_mixfp4_desc& d = descs[i];
+        deq = k;
+        const int j = bt.n++;
+        bt.w[j] = reinterpret_cast<const uint4*>(d.w_bf16);
+        bt.m[j] = nullptr;
+        bt.q[j] = nullptr;
+        bt.s2[j] = d.s2;
+        bt.codes[j] = reinterpret_cast<uint2*>(d.codes);
+        bt.scales[j] = d.scales;
+        bt.wdeq[j] = reinterpret_cast<uint4*>(d.w_deq);
+        bt.nblk[j] = d.rows * (d.cols / 16);
+        bt.map[j] = d.map;
+        const uint32_t nb = (uint32_t)(d.cols / 16), tcb = (uint32_t)(d.tile_cols / 16);
+        bt.nb_row[j] = nb;
+        bt.tiles_per_row[j] = (uint32_t)(d.cols / d.tile_cols);
+        uint32_t s0, s1, s2;
+        div_magic_host(nb, bt.mul[j][0], s0);
+        div_magic_host((uint32_t)d.tile_rows, bt.mul[j][1], s1);
+        div_magic_host(tcb, bt.mul[j][2], s2);
+        bt.sh[j] = s0 | (s1 << 8) | (s2 << 16);
+    }
+    return FOCUS_OK;
+}
+
 int quant_key(const focus_quant_desc& d) {
     return (d.m ? 4 : 0) | (d.q ? 2 : 0) | (d.w_deq ? 1 : 0);
 }
@@ -304,6 +368,25 @@ int focus_quantize_act_per_token_fo6(const uint16_t* x_bf16, int64_t tokens, int
         return FOCUS_ERR_ALIGN;
     return hip_status(focus::launch_act_per_token(x_bf16, tokens, hidden, codes, scales, s2_out,
                                                   x_deq, true, (hipStream_t)stream));
+}
+
+int focus_quantize_mixfp4(const uint16_t* w_bf16, int64_t rows, int64_t cols, const float* s2,
+                          const uint8_t* map, int64_t tile_rows, int64_t tile_cols, uint8_t* codes,
+                          uint8_t* scales, uint16_t* w_deq, void* stream) {
+    const focus_mixfp4_desc d = {w_bf16, rows, cols, s2, map, tile_rows, tile_cols, codes, scales, w_deq};
+    int st = check_quant_mix(d);
+    if (st != FOCUS_OK) return st;
+    return run_quantize_mix(&d, 1, (hipStream_t)stream);
+}
+
+int focus_quantize_mixfp4_many(const focus_mixfp4_desc* descs, int n, void* stream) {
+    if (n < 0) return FOCUS_ERR_RANGE;
+    if (n > 0 && !descs) return FOCUS_ERR_NULL;
+    for (int i = 0; i < n; ++i) {
+        int st = check_quant_mix(descs[i]);
+        if (st != FOCUS_OK) return st;
+    }
+    return run_quantize_mix(descs, n, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -24,6 +24,18 @@ struct QuantBatch {
     int n;
 };
 
+// FlipQuant MixFP4: a QuantBatch plus, per tensor, the tile map and the three
+// divisors that turn a block index into its tile (blocks per row, tile rows,
+// tile columns in blocks) as div_magic multipliers; shift k of tensor j is
+// byte k of sh[j].  About 3.3 KB in all.
+struct MixBatch : QuantBatch {
+    const uint8_t* map[kBatch];
+    uint32_t nb_row[kBatch];
+    uint32_t tiles_per_row[kBatch];
+    uint32_t mul[kBatch][3];
+    uint32_t sh[kBatch];
+};
+
 struct DequantBatch {
     const uint2* codes[kBatch];
     const uint8_t* scales[kBatch];
@@ -49,6 +61,7 @@ struct ScaleBatch {
 // FourOverSix without / with w' (m and q absent); 16 + (m, q, w' bits) =
 // FOCUS on MXFP4; every tensor of one batch shares the key.
 hipError_t launch_quantize(QuantBatch& bt, int key, hipStream_t stream);
+hipError_t launch_quantize_mix(MixBatch& bt, bool deq, hipStream_t stream);
 hipError_t launch_dequantize(DequantBatch& bt, bool mx, hipStream_t stream);
 hipError_t launch_tensor_scale(ScaleBatch& bt, hipStream_t stream);
 hipError_t launch_act_per_token(const uint16_t* x, int64_t tokens, int64_t hidden, uint8_t* codes,

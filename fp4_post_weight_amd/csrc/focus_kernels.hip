@@ -231,6 +231,43 @@ __device__ __forceinline__ void fo6_block(uint4 a, uint4 b, float s2, double rde
     }
 }
 
+// FlipQuant MixFP4 E0M3 block: the scale maps the block maximum to 7
+// (rden7 = RN64(1/RN32(7*s2))), codes are the signed levels 0..7; same
+// interface as fo6_block.
+template <bool DEQ>
+__device__ __forceinline__ void e0m3_block(uint4 a, uint4 b, float s2, double rden7,
+                                           uint2* codes_out, uint8_t* scale_out, uint4& deq0,
+                                           uint4& deq1) {
+    const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float f[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        f[2 * i] = bf16_lo(v[i]);
+        f[2 * i + 1] = bf16_hi(v[i]);
+    }
+    if (s2 == 0.0f) {
+        *scale_out = 0x38;
+        st8(codes_out, 0, make_uint2(sign_codes8(a), sign_codes8(b)));
+        if (DEQ) {
+            const uint32_t z = 0x80008000u;
+            deq0 = make_uint4(a.x & z, a.y & z, a.z & z, a.w & z);
+            deq1 = make_uint4(b.x & z, b.y & z, b.z & z, b.w & z);
+        }
+        return;
+    }
+    const uint32_t sb = e4m3_byte_normal(block_t(block_amax_bits(a, b), 1.0f, rden7));
+    const float S = e4m3_normal_value(sb);
+    const float d = S * s2;
+    const uint32_t c0 = encode8_e0m3(f, d);
+    const uint32_t c1 = encode8_e0m3(f + 8, d);
+    st8(codes_out, 0, make_uint2(c0, c1));
+    *scale_out = (uint8_t)sb;
+    if (DEQ) {
+        deq0 = dequant8_e0m3(c0, S, s2);
+        deq1 = dequant8_e0m3(c1, S, s2);
+    }
+}
+
 // One 16-element half of an MXFP4 32-block whose scale S (a power of two) is
 // already known: the codes of its two relaxed 8-element sub-blocks (q0, q1),
 // w' = BF16(c*S).  Same interface as quantize_block otherwise.
@@ -293,10 +330,11 @@ constexpr int64_t kQuantTile = (int64_t)kThreads * kQuantU;
 
 // MODE 0: FOCUS NVFP4; 1: FourOverSix (m, q absent); 2: FOCUS on MXFP4 (lanes
 // 2j and 2j+1 share one 32-block: m[blk/2], scale byte stored by the even
-// lane, no tensor scale).
-template <bool HAS_M, bool HAS_Q, bool DEQ, int MODE = 0>
-__global__ __launch_bounds__(kThreads) void k_quantize(QuantBatch bt, int64_t ntiles) {
-    constexpr bool FO6 = MODE == 1, MX = MODE == 2;
+// lane, no tensor scale); 3: FlipQuant MixFP4 (Batch = MixBatch; each block
+// looks up its tile's map byte: E0M3 if set, FourOverSix otherwise).
+template <bool HAS_M, bool HAS_Q, bool DEQ, int MODE = 0, typename Batch = QuantBatch>
+__global__ __launch_bounds__(kThreads) void k_quantize(Batch bt, int64_t ntiles) {
+    constexpr bool FO6 = MODE == 1 || MODE == 3, MX = MODE == 2, MIX = MODE == 3;
     __shared__ uint4 xch[DEQ ? kThreads / 64 : 1][128];
     constexpr bool kLdsLoadW = LdsLoadW<DEQ>::value;
     __shared__ uint4 xchw[kLdsLoadW ? kThreads / 64 : 1][128];
@@ -312,11 +350,13 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QuantBatch bt, int64_t nt
         const float s2 = MX ? 1.0f : ld_uniform(bt.s2[j]);
         const double rden = MX ? 0.0 : 1.0 / (double)(6.0f * s2);
         const double rden4 = FO6 ? 1.0 / (double)(4.0f * s2) : 0.0;
+        const double rden7 = MIX ? 1.0 / (double)(7.0f * s2) : 0.0;
         const int64_t nblk = bt.nblk[j];
         const int64_t tile0 = (tile - bt.tile_start[j]) * kQuantTile;
         uint4 va[kQuantU] = {}, vb[kQuantU] = {};
         float mb[kQuantU];
         float2 qq[kQuantU];
+        bool e0[kQuantU] = {};
 #pragma unroll
         for (int k = 0; k < kQuantU; ++k) {
             const int64_t first = tile0 + (int64_t)k * kThreads + wave * 64;  // block of lane 0
@@ -333,6 +373,16 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QuantBatch bt, int64_t nt
             if (blk < nblk) {
                 mb[k] = HAS_M ? ld4f(m, MX ? blk >> 1 : blk) : 1.0f;
                 qq[k] = HAS_Q ? ld8f(q, blk) : make_float2(0.0f, 0.0f);
+                if constexpr (MIX) {
+                    // block -> (row, block in row) -> (tile row, tile column);
+                    // every index is below 2^31 (checked on the host)
+                    const uint32_t ub = (uint32_t)blk, sh = bt.sh[j];
+                    const uint32_t r = div_magic(ub, bt.mul[j][0], sh & 255u);
+                    const uint32_t b = ub - r * bt.nb_row[j];
+                    const uint32_t tr = div_magic(r, bt.mul[j][1], (sh >> 8) & 255u);
+                    const uint32_t tc = div_magic(b, bt.mul[j][2], sh >> 16);
+                    e0[k] = bt.map[j][tr * bt.tiles_per_row[j] + tc] != 0;
+                }
             }
         }
 #pragma unroll
@@ -351,7 +401,10 @@ __global__ __launch_bounds__(kThreads) void k_quantize(QuantBatch bt, int64_t nt
                     mx_half_block<HAS_Q, DEQ>(va[k], vb[k], e8m0_value(mx_sb), qq[k].x, qq[k].y, tab,
                                               bt.codes[j] + blk, d0, d1);
                     if ((lane & 1) == 0) bt.scales[j][blk >> 1] = (uint8_t)mx_sb;
-                } else if (FO6)
+                } else if (MIX && e0[k])
+                    e0m3_block<DEQ>(va[k], vb[k], s2, rden7, bt.codes[j] + blk, bt.scales[j] + blk,
+                                    d0, d1);
+                else if (FO6)
                     fo6_block<DEQ>(va[k], vb[k], s2, rden, rden4, bt.codes[j] + blk,
                                    bt.scales[j] + blk, d0, d1);
                 else
@@ -666,6 +719,21 @@ hipError_t launch_quantize(QuantBatch& bt, int key, hipStream_t stream) {
         FOCUS_MX_CASE(7, true, true, true)
 #undef FOCUS_MX_CASE
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_mix(MixBatch& bt, bool deq, hipStream_t stream) {
+    int64_t t = 0;
+    for (int j = 0; j < bt.n; ++j) {
+        bt.tile_start[j] = t;
+        t += (bt.nblk[j] + kQuantTile - 1) / kQuantTile;
+    }
+    bt.tile_start[bt.n] = t;
+    const dim3 grid(grid_for_tiles(t)), block(kThreads);
+    if (deq)
+        hipLaunchKernelGGL((k_quantize<false, false, true, 3, MixBatch>), grid, block, 0, stream, bt, t);
+    else
+        hipLaunchKernelGGL((k_quantize<false, false, false, 3, MixBatch>), grid, block, 0, stream, bt, t);
     return hipGetLastError();
 }
 

@@ -287,4 +287,62 @@ __device__ __forceinline__ void fo6_candidate(const float* f, float amax, double
     err = e;
 }
 
+// ---------------------------------------------------------------------------
+// FlipQuant MixFP4 E0M3 elements: uniform levels 0..7 with a sign bit (bit
+// 3); the block scale maps the block maximum to 7.
+// ---------------------------------------------------------------------------
+
+// Code of a binary32 x in [-7, 7]: |x| + 2^23 is rounded to an integer by
+// the binary32 addition (the spacing of binary32 in [2^23, 2^24) is 1), to
+// nearest with ties to the even integer, and that integer is the low three
+// bits.  The sign bit of x (also of -0) becomes bit 3.
+__device__ __forceinline__ uint32_t e0m3_code(float x) {
+    const uint32_t mag = __float_as_uint(__builtin_fabsf(x) + 0x1p23f) & 7u;
+    return ((__float_as_uint(x) >> 28) & 8u) | mag;
+}
+
+// E0M3 codes of f[0..7] for the denominator d = S*s2, element 2j in the low
+// nibble of byte j; the quotient is formed exactly as in encode8.
+__device__ __forceinline__ uint32_t encode8_e0m3(const float* f, float d) {
+    uint32_t v = 0;
+    if (d != 0.0f) {
+        const double r = recip_f64((double)d);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float x = fminf(fmaxf((float)((double)f[i] * r), -7.0f), 7.0f);
+            v |= e0m3_code(x) << (4 * i);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v |= e0m3_code(fminf(fmaxf(f[i] / d, -7.0f), 7.0f)) << (4 * i);
+    }
+    return v;
+}
+
+// Signed level of an E0M3 code (-0 for code 8).
+__device__ __forceinline__ float e0m3_level(uint32_t c) {
+    return __uint_as_float(__float_as_uint((float)(c & 7u)) | ((c & 8u) << 28));
+}
+
+// w' of eight E0M3 codes: BF16((c*S)*s2).
+__device__ __forceinline__ uint4 dequant8_e0m3(uint32_t codes, float S, float s2) {
+    uint32_t o[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float v0 = (e0m3_level(codes >> (8 * p)) * S) * s2;
+        const float v1 = (e0m3_level(codes >> (8 * p + 4)) * S) * s2;
+        o[p] = bf16_pair(v0, v1);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// n / d for n < 2^31 and 1 <= d < 2^31 with a precomputed multiplier:
+// M = ceil(2^(31+l) / d), l = ceil(log2 d), so M in [2^31, 2^32) and
+// M*d - 2^(31+l) < d; then floor(n*M / 2^(31+l)) = floor(n/d), because the
+// excess n*(M*d - 2^(31+l)) / (d*2^(31+l)) is below 2^-l <= 1/d and the
+// fractional part of n/d is at most (d-1)/d.
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t M, uint32_t sh) {
+    return (uint32_t)(((uint64_t)n * M) >> sh);
+}
+
 }  // namespace focus

@@ -223,6 +223,49 @@ int focus_quantize_fo6_many(const focus_quant_desc* descs, int n, void* stream);
 /* Batched FOCUS on MXFP4 (cols % 32 == 0; s2 ignored). */
 int focus_quantize_mx_many(const focus_quant_desc* descs, int n, void* stream);
 
+/*
+ * FlipQuant MixFP4 ("Llama-3.1-8B-Instruct FlipQuant MixFP4 maps", section
+ * "What this is", first paragraph and the tile table): NVFP4 (16-element
+ * blocks, E4M3 block scale, FP32 tensor scale s2) in which a map with one
+ * entry per weight tile of tile_rows x tile_cols (output rows x input
+ * columns; the page's maps use 8x64, 16x64 and 256x64) chooses the element
+ * format of every block in the tile: a set entry stores E0M3 (uniform levels
+ * 0..7), a clear one E2M1 with the FourOverSix scale rule (as
+ * focus_quantize_fo6).  Readings where the page is silent: an E0M3 block's
+ * scale maps the block maximum to 7, S = e4m3(clamp(max|w_b| / (7*s2),
+ * 2^-6, 448)) with a zero maximum giving 1; its code is the sign (bit 3)
+ * and the nearest integer 0..7 (ties to even) to |clamp(w / (S*s2), -7, 7)|;
+ * w' = BF16((c*S)*s2) with c the signed level (E2M1 value or E0M3 level);
+ * binary32 arithmetic throughout; s2 = amax / (6*448) as for NVFP4.
+ *   w_bf16   [rows, cols] BF16, 16-byte aligned.
+ *   s2       one float (from focus_tensor_scale).
+ *   map      [rows/tile_rows, cols/tile_cols] bytes, row-major, nonzero = E0M3
+ *            (device memory, like every data pointer).
+ *   tile_rows >= 1, tile_cols a positive multiple of 16, dividing rows and
+ *            cols (FOCUS_ERR_SHAPE otherwise); rows * cols / 16 < 2^31
+ *            (FOCUS_ERR_RANGE otherwise).
+ *   codes    [rows, cols/2], E2M1 or E0M3 nibbles as the tile's entry says
+ *            (element 2j in the low nibble);  scales [rows, cols/16] E4M3;
+ *   w_deq    [rows, cols] BF16 or NULL.
+ */
+int focus_quantize_mixfp4(const uint16_t* w_bf16, int64_t rows, int64_t cols, const float* s2,
+                          const uint8_t* map, int64_t tile_rows, int64_t tile_cols, uint8_t* codes,
+                          uint8_t* scales, uint16_t* w_deq, void* stream);
+
+typedef struct focus_mixfp4_desc {
+    const uint16_t* w_bf16;  /* [rows, cols] BF16 */
+    int64_t rows, cols;
+    const float* s2;         /* one float */
+    const uint8_t* map;      /* [rows/tile_rows, cols/tile_cols] */
+    int64_t tile_rows, tile_cols;
+    uint8_t* codes;          /* [rows, cols/2] */
+    uint8_t* scales;         /* [rows, cols/16] */
+    uint16_t* w_deq;         /* [rows, cols] or NULL */
+} focus_mixfp4_desc;
+
+/* Batched MixFP4, with the rules of the batched calls above. */
+int focus_quantize_mixfp4_many(const focus_mixfp4_desc* descs, int n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

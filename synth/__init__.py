@@ -153,7 +153,7 @@ class Linear:
         return self.rows * self.cols
 
     def tid(self, field: int) -> int:
-        """Tensor id of field 0 (W), 1 (m), 2 (q) of this linear."""
+        """Tensor id of field 0 (W), 1 (m), 2 (q), 3 (tile map) of this linear."""
         return (self.layer * 16 + self.proj) * 4 + field
 
 

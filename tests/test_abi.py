@@ -183,3 +183,28 @@ def test_mx_validation(lib):
                                       None) == ERR_SHAPE
     assert lib.focus_dequantize_mx(FAKE, FAKE, 2, 48, FAKE, None) == ERR_SHAPE
     assert lib.focus_dequantize_mx(FAKE, None, 2, 64, FAKE, None) == ERR_NULL
+
+
+def test_mixfp4_validation(lib):
+    MD = _lib.MixDesc
+    q = lib.focus_quantize_mixfp4
+    #        w     rows cols s2    map   th  tw  codes scales deq
+    assert q(FAKE, 16, 128, FAKE, FAKE, 0, 64, FAKE, FAKE, None, None) == ERR_SHAPE   # tile_rows < 1
+    assert q(FAKE, 16, 128, FAKE, FAKE, 8, 8, FAKE, FAKE, None, None) == ERR_SHAPE    # tile_cols < 16
+    assert q(FAKE, 16, 128, FAKE, FAKE, 8, 40, FAKE, FAKE, None, None) == ERR_SHAPE   # not a multiple of 16
+    assert q(FAKE, 12, 128, FAKE, FAKE, 8, 64, FAKE, FAKE, None, None) == ERR_SHAPE   # rows % tile_rows
+    assert q(FAKE, 16, 160, FAKE, FAKE, 8, 64, FAKE, FAKE, None, None) == ERR_SHAPE   # cols % tile_cols
+    assert q(FAKE, 1 << 24, 2048, FAKE, FAKE, 8, 64, FAKE, FAKE, None, None) == ERR_RANGE  # 2^31 blocks
+    assert q(FAKE, 16, 128, FAKE, None, 8, 64, FAKE, FAKE, None, None) == ERR_NULL
+    assert q(FAKE, 16, 128, None, FAKE, 8, 64, FAKE, FAKE, None, None) == ERR_NULL
+    assert q(FAKE + 2, 16, 128, FAKE, FAKE, 8, 64, FAKE, FAKE, None, None) == ERR_ALIGN
+    assert q(FAKE, 16, 128, FAKE, FAKE, 8, 64, FAKE + 4, FAKE, None, None) == ERR_ALIGN
+    assert q(FAKE, 16, 128, FAKE, FAKE, 8, 64, FAKE, FAKE, FAKE + 8, None) == ERR_ALIGN
+    assert q(None, 0, 128, None, None, 8, 64, None, None, None, None) == OK
+    many = lib.focus_quantize_mixfp4_many
+    good = MD(FAKE, 16, 128, FAKE, FAKE, 8, 64, FAKE, FAKE, None)
+    bad = MD(FAKE, 16, 128, FAKE, FAKE, 16, 48, FAKE, FAKE, None)
+    assert many((MD * 2)(good, bad), 2, None) == ERR_SHAPE
+    assert many(None, 0, None) == OK
+    assert many(None, 1, None) == ERR_NULL
+    assert ct.sizeof(MD) == 10 * 8

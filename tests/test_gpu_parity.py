@@ -604,3 +604,139 @@ def test_mx_many_matches_single(focus, orc):
         torch.cuda.synchronize()
         assert torch.equal(b.outs[i].codes, single.codes) and torch.equal(b.outs[i].scales, single.scales)
         assert torch.equal(b.outs[i].deq.view(torch.int16), single.deq.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# FlipQuant MixFP4 (per-tile E0M3 / E2M1-FourOverSix)
+# ---------------------------------------------------------------------------
+
+def run_mix(focus, wb, tmap, th, tw, s2=None, dequant=True):
+    w = torch.from_numpy(np.ascontiguousarray(wb).view(np.int16).copy()).view(torch.bfloat16).to(DEV)
+    md = torch.from_numpy(np.ascontiguousarray(tmap, dtype=np.uint8)).to(DEV)
+    s2d = None if s2 is None else torch.tensor([s2], dtype=torch.float32, device=DEV)
+    res = focus.quantize_mixfp4(w, md, th, tw, s2d, dequant=dequant)
+    torch.cuda.synchronize()
+    return (res.codes.cpu().numpy(), res.scales.cpu().numpy(),
+            None if res.deq is None else np_bits(res.deq), np.float32(res.s2.item()))
+
+
+def check_mix(focus, orc, wb, tmap, th, tw, dequant=True, s2=None, label=""):
+    codes, scales, deq, s2g = run_mix(focus, wb, tmap, th, tw, s2, dequant)
+    if s2 is None:
+        s2_o, _ = orc.tensor_scale(wb)
+        assert s2g == s2_o, label
+    else:
+        s2_o = np.float32(s2)
+    c, sc, d = orc.mixfp4_quantize(wb, s2_o, tmap, th, tw, dequant=dequant)
+    assert np.array_equal(scales, sc), f"{label}: {np.count_nonzero(scales != sc)} scale bytes differ"
+    assert np.array_equal(codes, c), f"{label}: {np.count_nonzero(codes != c)} code bytes differ"
+    if dequant:
+        assert np.array_equal(deq, d), f"{label}: {np.count_nonzero(deq != d)} w' values differ"
+
+
+MIX_CASES = [((256, 1024), (8, 64)), ((256, 1024), (16, 64)), ((512, 1024), (256, 64)),
+             ((24, 1088), (8, 64)), ((3, 48), (3, 48)), ((7, 112), (1, 16)), ((33, 4112), (11, 16)),
+             ((129, 1040), (43, 208)), ((1, 65536 + 64), (1, 64))]
+
+
+@pytest.mark.parametrize("shape,tile", MIX_CASES, ids=lambda v: f"{v[0]}x{v[1]}")
+def test_mixfp4_maps(focus, orc, shape, tile):
+    """Random maps at a high E0M3 share and at the page's share; full and
+    odd tilings (the division by blocks per row, tile rows and tile columns
+    in blocks at several divisors), partial last launch tiles."""
+    rows, cols = shape
+    w = synth.weights(shape, seed=rows + 3 * cols, tensor_id=21, zero_block_p=0.02)
+    wb = np_bits(w)
+    for i, frac in enumerate((0.4, synth.MIXFP4_FRAC.get(tile, 0.02))):
+        tmap = synth.tile_map(rows, cols, tile, frac=frac, seed=rows + i, tensor_id=22).numpy()
+        check_mix(focus, orc, wb, tmap, tile[0], tile[1], dequant=(i == 0) or rows % 2 == 1,
+                  label=f"mix {shape} tile {tile} frac {frac:.4f}")
+
+
+def test_mixfp4_constructed_cases(focus, orc):
+    rng = np.random.default_rng(97)
+    sb, codes, wb = pins._e0m3_fixed_case(rng, rows=24, nb=8)
+    check_mix(focus, orc, wb, np.ones((3, 2), np.uint8), 8, 64, s2=float(pins.S2_POW2), label="e0m3 fixed points")
+    # the GPU reproduces the fixed points themselves
+    c, s, d, _ = run_mix(focus, wb, np.ones((3, 2), np.uint8), 8, 64, s2=float(pins.S2_POW2))
+    assert np.array_equal(s, sb) and np.array_equal(parity.unpack(c), codes) and np.array_equal(d, wb)
+    # all-clear map: FourOverSix bit for bit
+    w, _, _ = synth.make_single()
+    wb1 = np_bits(w)
+    c0, s0, d0, _ = run_mix(focus, wb1, np.zeros((32, 16), np.uint8), 8, 64)
+    f = focus.quantize_fo6(w.to(DEV), dequant=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(c0, f.codes.cpu().numpy()) and np.array_equal(s0, f.scales.cpu().numpy())
+    assert np.array_equal(d0, np_bits(f.deq))
+    # all-zero tensor and signed zeros
+    wz = np.zeros((16, 128), np.uint16)
+    wz[1, 3] = 0x8000
+    check_mix(focus, orc, wz, np.array([[1, 0], [0, 1]], np.uint8), 8, 64, label="mix all zero")
+
+
+def test_mixfp4_extreme_magnitudes(focus, orc):
+    rng = np.random.default_rng(98)
+    e = rng.integers(-140, 127, (64, 256)).astype(np.float64)
+    x = (rng.standard_normal((64, 256)) * np.exp2(e)).astype(np.float32)
+    x[0, 0] = 3.3e38
+    tmap = (rng.random((8, 4)) < 0.5).astype(np.uint8)
+    check_mix(focus, orc, pins.torch_bf16_bits(x), tmap, 8, 64, label="mix extreme")
+    for amax_exp in (-133, -120):
+        y = (rng.uniform(-1, 1, (16, 128)) * 2.0 ** amax_exp).astype(np.float32)
+        check_mix(focus, orc, pins.torch_bf16_bits(y), np.array([[1, 0], [0, 1]], np.uint8), 8, 64,
+                  label=f"mix tiny 2^{amax_exp}")
+
+
+@pytest.mark.parametrize("tile", [(8, 64), (16, 64), (256, 64)], ids=lambda t: f"{t[0]}x{t[1]}")
+def test_mixfp4_full_size_sampled(focus, orc, tile):
+    """Every 8B linear shape at full size with a map at the page's E0M3 share,
+    launched batched as the benchmark launches them; sampled rows checked
+    (row i against its map row, i.e. the oracle with one-row tiles)."""
+    shapes = sorted(set(synth.LLAMA_8B.layer_shapes()))
+    ws, maps = [], []
+    for k, (rows, cols) in enumerate(shapes):
+        lin = next(l for l in synth.LLAMA_8B.linears() if (l.rows, l.cols) == (rows, cols))
+        w, _, _ = synth.make_linear(synth.LLAMA_8B, lin, device=DEV, with_m=False, with_q=False)
+        ws.append(w)
+        maps.append(synth.tile_map(rows, cols, tile, frac=synth.MIXFP4_FRAC[tile], seed=k, tensor_id=23,
+                                   device=DEV))
+    ts = focus.tensor_scale_many(ws)
+    b = focus.quantize_mixfp4_many(ws, maps, [tile] * len(ws), [ts.s2[i] for i in range(len(ws))], dequant=True)
+    torch.cuda.synchronize()
+    for k, w in enumerate(ws):
+        rows = w.shape[0]
+        wb = np_bits(w)
+        s2_o, _ = orc.tensor_scale(wb)
+        assert ts.s2[k].item() == float(s2_o)
+        idx = np.unique(np.concatenate([[0, rows - 1], np.random.default_rng(rows + k).integers(0, rows, 12)]))
+        it = torch.from_numpy(idx).to(DEV)
+        mrows = maps[k].cpu().numpy()[idx // tile[0]]
+        c, sc, d = orc.mixfp4_quantize(wb[idx], s2_o, mrows, 1, tile[1])
+        o = b.outs[k]
+        assert np.array_equal(o.scales[it].cpu().numpy(), sc)
+        assert np.array_equal(o.codes[it].cpu().numpy(), c)
+        assert np.array_equal(np_bits(o.deq[it]), d)
+
+
+def test_mixfp4_many_matches_single(focus, orc):
+    rng = np.random.default_rng(99)
+    ws, maps, tiles = [], [], []
+    for i in range(37):
+        th, tw = int(rng.integers(1, 9)), 16 * int(rng.integers(1, 5))
+        r, c = th * int(rng.integers(1, 8)), tw * int(rng.integers(1, 20))
+        ws.append(synth.weights((r, c), seed=i, tensor_id=24).to(DEV))
+        maps.append(synth.tile_map(r, c, (th, tw), frac=0.3, seed=i, tensor_id=25, device=DEV))
+        tiles.append((th, tw))
+    ts = focus.tensor_scale_many(ws)
+    s2s = [ts.s2[i] for i in range(37)]
+    b = focus.quantize_mixfp4_many(ws, maps, tiles, s2s, dequant=True)
+    torch.cuda.synchronize()
+    for i in range(37):
+        single = focus.quantize_mixfp4(ws[i], maps[i], tiles[i][0], tiles[i][1], s2s[i], dequant=True)
+        torch.cuda.synchronize()
+        assert torch.equal(b.outs[i].codes, single.codes) and torch.equal(b.outs[i].scales, single.scales)
+        assert torch.equal(b.outs[i].deq.view(torch.int16), single.deq.view(torch.int16))
+        c, sc, d = orc.mixfp4_quantize(np_bits(ws[i]), np.float32(s2s[i].item()), maps[i].cpu().numpy(),
+                                       tiles[i][0], tiles[i][1])
+        assert np.array_equal(single.codes.cpu().numpy(), c) and np.array_equal(single.scales.cpu().numpy(), sc)
+        assert np.array_equal(np_bits(single.deq), d)
