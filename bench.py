@@ -68,10 +68,14 @@ def parse():
     return ap.parse_args()
 
 
+# The sources the quantize kernel is compiled from.
+QUANT_KERNEL_SOURCES = ("focus_internal.h", "focus_kernels.hip", "focus_numerics.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp4_post_weight_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in QUANT_KERNEL_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]

@@ -22,6 +22,7 @@ LIB_PATH = _os.path.join(_HERE, "liboracle.so")
 _u16p = _ct.POINTER(_ct.c_uint16)
 _u8p = _ct.POINTER(_ct.c_uint8)
 _f32p = _ct.POINTER(_ct.c_float)
+_f64p = _ct.POINTER(_ct.c_double)
 _i64 = _ct.c_int64
 _f = _ct.c_float
 
@@ -58,6 +59,8 @@ _SIGNATURES = {
     "oracle_mx_dequantize": (None, [_u8p, _u8p, _i64, _i64, _u16p]),
     "oracle_fo6_quantize": (None, [_u16p, _i64, _i64, _f32p, _ct.c_int, _u8p, _u8p, _u16p]),
     "oracle_fo6_quantize_act_per_token": (None, [_u16p, _i64, _i64, _u8p, _u8p, _f32p, _u16p]),
+    "oracle_nvfp4_linear": (None, [_u8p, _u8p, _f32p, _ct.c_int, _i64, _u8p, _u8p, _f32p, _i64, _i64,
+                                   _f64p, _f64p]),
 }
 
 
@@ -303,6 +306,27 @@ class Oracle:
                                         tile_rows, tile_cols, _ptr(codes, _u8p), _ptr(scales, _u8p),
                                         _ptr(wdeq, _u16p))
         return codes, scales, wdeq
+
+    def nvfp4_linear(self, x_codes, x_scales, x_s2, w_codes, w_scales, w_s2):
+        """Y = X' W'^T of NVFP4 activations X [M, K] (s2 per token, or one
+        value) and NVFP4 weights W [N, K] (one s2): returns (Y, Yabs) in
+        float64, Yabs the matching sum of |products| (error-bound scale)."""
+        x_codes, x_scales = _as(x_codes, _np.uint8), _as(x_scales, _np.uint8)
+        w_codes, w_scales = _as(w_codes, _np.uint8), _as(w_scales, _np.uint8)
+        M, K = x_codes.shape[0], 2 * x_codes.shape[1]
+        N = w_codes.shape[0]
+        assert K % 16 == 0 and w_codes.shape[1] * 2 == K
+        assert x_scales.shape == (M, K // 16) and w_scales.shape == (N, K // 16)
+        xs2 = _np.ascontiguousarray(_np.atleast_1d(_np.asarray(x_s2, _np.float32)))
+        ws2 = _np.ascontiguousarray(_np.atleast_1d(_np.asarray(w_s2, _np.float32)))
+        assert xs2.size in (1, M) and ws2.size == 1
+        y = _np.empty((M, N), _np.float64)
+        yabs = _np.empty((M, N), _np.float64)
+        self.lib.oracle_nvfp4_linear(_ptr(x_codes, _u8p), _ptr(x_scales, _u8p), _ptr(xs2, _f32p),
+                                     1 if xs2.size == M else 0, M, _ptr(w_codes, _u8p),
+                                     _ptr(w_scales, _u8p), _ptr(ws2, _f32p), N, K, _ptr(y, _f64p),
+                                     _ptr(yabs, _f64p))
+        return y, yabs
 
 
 _default = None

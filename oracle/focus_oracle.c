@@ -44,6 +44,11 @@
  * nearest representable value, ties to the code whose last mantissa bit is
  * 0.  This is slow and meant to be obviously right, not fast.
  *
+ * Later sections, each citing its own source: FourOverSix (block scale for
+ * maximum 6 or 4), FOCUS on MXFP4 (32-blocks, E8M0 scale), FlipQuant MixFP4
+ * (per-tile E0M3 / E2M1), and the NVFP4 linear layer that consumes the
+ * stored format (Y = X' W'^T in binary64).
+ *
  * Readings where the pages are silent (each one is tested):
  *   - the sign of a zero code follows the sign of the quotient, so a
  *     negative element that rounds to zero is stored as code 0x8;
@@ -586,6 +591,49 @@ void oracle_mixfp4_quantize(const uint16_t* w, int64_t rows, int64_t cols, float
                     float cv = e0m3 ? oracle_e0m3_value(c[i]) : oracle_e2m1_value(c[i]);
                     wdeq[r * cols + b * 16 + i] = oracle_bf16_round((cv * S) * s2);
                 }
+        }
+    }
+}
+
+/* ---------- the NVFP4 linear layer (consumer of the stored format) ------ */
+
+/* "FOCUS NVFP4 scales for Llama-3.2-1B-Instruct (our reproduction)": section
+ * "What this is" (the deployed model is plain NVFP4 and runs on standard
+ * NVFP4 kernels) and section "Perplexity" (weights in NVFP4 with one FP32
+ * scale per tensor, activations in NVFP4 with one scale per token).  The
+ * layer computes Y = X' W'^T with the dequantized operands taken as real
+ * numbers: X'[t,k] = c*S*s2x[t], W'[o,k] = c*S*s2w (no BF16 rounding of the
+ * operands).  Written out: for every (t, o) the sum over k, in k order, of
+ * the products (c_x*S_x)*(c_w*S_w) -- each exact in binary64 (at most
+ * 10 significant bits) -- accumulated in binary64, then multiplied by
+ * s2x[t] and s2w.  yabs receives the same sum of |products| times
+ * |s2x[t]*s2w|, the scale of any rounding error in another summation order.
+ * Layouts: codes [rows, K/2] (element 2j in the low nibble), scale bytes
+ * [rows, K/16], Y [M, N] row-major; xs2 has M entries when xs2_per_row, else 1. */
+static double nvfp4_element(const uint8_t* codes, const uint8_t* scales, int64_t row, int64_t K,
+                            int64_t k)
+{
+    uint8_t byte = codes[row * (K / 2) + k / 2];
+    unsigned c = (k & 1) ? (byte >> 4) : (byte & 15u);
+    return (double)oracle_e2m1_value(c) * (double)oracle_e4m3_value(scales[row * (K / 16) + k / 16]);
+}
+
+void oracle_nvfp4_linear(const uint8_t* xc, const uint8_t* xs, const float* xs2, int xs2_per_row,
+                         int64_t M, const uint8_t* wc, const uint8_t* ws, const float* ws2,
+                         int64_t N, int64_t K, double* y, double* yabs)
+{
+    for (int64_t t = 0; t < M; ++t) {
+        double sx = (double)xs2[xs2_per_row ? t : 0];
+        for (int64_t o = 0; o < N; ++o) {
+            double acc = 0.0, aabs = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = nvfp4_element(xc, xs, t, K, k) * nvfp4_element(wc, ws, o, K, k);
+                acc += p;
+                aabs += fabs(p);
+            }
+            double s = sx * (double)ws2[0];
+            y[t * N + o] = acc * s;
+            if (yabs) yabs[t * N + o] = aabs * fabs(s);
         }
     }
 }

@@ -788,6 +788,62 @@ def check_mixfp4_maps(o):
     assert np.array_equal(mx[2], np.where(sel_el, e[2], f[2]))
 
 
+# ---------------------------------------------------------------------------
+# the NVFP4 linear layer Y = X' W'^T
+# ---------------------------------------------------------------------------
+
+def check_linear_closed_forms(o):
+    """Codes 1.0 (0x2) and -1.0 (0xA) with scale 1 (0x38): every output is
+    +-K * s2x[t] * s2w; Yabs = K * s2x[t] * s2w."""
+    K = 48
+    xc = np.full((3, K // 2), 0x22, np.uint8)
+    xs = np.full((3, K // 16), 0x38, np.uint8)
+    wc = np.full((2, K // 2), 0x22, np.uint8)
+    wc[1] = 0xAA
+    ws = np.full((2, K // 16), 0x38, np.uint8)
+    s2x = np.float32([1.0, 0.25, 3.0])
+    y, ya = o.nvfp4_linear(xc, xs, s2x, wc, ws, np.float32(0.5))
+    want = K * s2x.astype(np.float64)[:, None] * 0.5 * np.array([1.0, -1.0])
+    assert np.array_equal(y, want) and np.array_equal(ya, np.abs(want))
+    # one s2 for all rows
+    y1, _ = o.nvfp4_linear(xc, xs, np.float32(2.0), wc, ws, np.float32(0.5))
+    assert np.array_equal(y1, K * 2.0 * 0.5 * np.array([[1.0, -1.0]] * 3))
+
+
+def check_linear_fixed_points(o):
+    """Weights and activations built as NVFP4 fixed points (w = c*S*s2, every
+    E4M3 scale): the pinned quantizer returns their codes and scales, and the
+    layer on those equals numpy's float64 product X @ W.T of the original
+    values exactly (K = 64 keeps every partial sum exact in binary64).  A
+    transposed operand, a wrong scale or nibble index, or a dropped or
+    misplaced s2 all change it."""
+    rng = np.random.default_rng(120)
+    _, _, _, wb = _fixed_point_case(rng, n_rows=119, nb=4)
+    wc, wsc, _ = o.quantize(wb, None, None, S2_POW2, dequant=False)
+    # activations: per-token s2 = 2^-10 * 2^(t mod 5), a random scale per
+    # block, and one |c| = 6 per block so each block is a fixed point
+    _, _, codes_x, _ = _fixed_point_case(rng, n_rows=119, nb=4)
+    sb = rng.integers(0x08, 0x7F, (119, 4)).astype(np.uint8)
+    S = np.repeat(torch_e4m3_value(sb).astype(np.float64), 16, axis=1)
+    s2x = (float(S2_POW2) * np.exp2(np.arange(119) % 5)).astype(np.float32)
+    x = code_value(codes_x) * S * s2x[:, None].astype(np.float64)
+    xb = torch_bf16_bits(x.astype(np.float32))
+    assert np.array_equal(bf16_float(xb).astype(np.float64), x)
+    xc = np.empty((119, 32), np.uint8)
+    xsc = np.empty((119, 4), np.uint8)
+    for t in range(119):
+        c, sc_, _ = o.quantize(xb[t:t + 1], None, None, s2x[t], dequant=False)
+        xc[t], xsc[t] = c[0], sc_[0]
+    assert np.array_equal(xsc, sb)
+    y, ya = o.nvfp4_linear(xc, xsc, s2x, wc, wsc, S2_POW2)
+    xf, wf = bf16_float(xb).astype(np.float64), bf16_float(wb).astype(np.float64)
+    assert np.array_equal(y, xf @ wf.T)
+    assert np.array_equal(ya, np.abs(xf) @ np.abs(wf).T)
+    # rows and columns are independent: a slice gives the same entries
+    y2, _ = o.nvfp4_linear(xc[5:9], xsc[5:9], s2x[5:9], wc[17:30], wsc[17:30], S2_POW2)
+    assert np.array_equal(y2, y[5:9, 17:30])
+
+
 ALL_CHECKS = [
     check_e2m1_table, check_e2m1_nearest_dense, check_e4m3_vs_torch, check_e4m3_decode_vs_torch,
     check_bf16_vs_torch, check_sigmoid, check_expf_correctly_rounded, check_tensor_scale,
@@ -797,5 +853,6 @@ ALL_CHECKS = [
     check_fo6_four_fixed_points, check_fo6_six_fixed_points, check_fo6_ties_keep_six,
     check_fo6_never_worse_than_rtn, check_mx_scale_closed_forms, check_mx_fixed_points,
     check_mx_factor_and_subblocks, check_mx_plain_reduction, check_e0m3_levels, check_mixfp4_maps,
+    check_linear_closed_forms, check_linear_fixed_points,
     check_fo6_zero_and_act,
 ]

@@ -67,6 +67,15 @@ MUTATIONS = [
      "map[((b * 16) / tile_cols) * (rows / tile_rows) + r / tile_rows]"),
     ("MixFP4 map ignored", "int e0m3 = map[(r / tile_rows) * tiles_per_row + (b * 16) / tile_cols] != 0;",
      "int e0m3 = 0;"),
+    ("linear drops the block scale",
+     "return (double)oracle_e2m1_value(c) * (double)oracle_e4m3_value(scales[row * (K / 16) + k / 16]);",
+     "return (double)oracle_e2m1_value(c);"),
+    ("linear ignores the per-token s2", "double sx = (double)xs2[xs2_per_row ? t : 0];",
+     "double sx = (double)xs2[0];"),
+    ("linear drops the weight s2", "double s = sx * (double)ws2[0];", "double s = sx;"),
+    ("linear scale of the first row only", "scales[row * (K / 16) + k / 16]", "scales[k / 16]"),
+    ("linear output transposed", "y[t * N + o] = acc * s;", "y[o * M + t] = acc * s;"),
+    ("linear scale per 8 elements", "scales[row * (K / 16) + k / 16]", "scales[row * (K / 16) + (k / 8) % (K / 16)]"),
     ("block max over the first sub-block only", "for (int i = 0; i < 16; ++i) {\n                float v = fabsf",
      "for (int i = 0; i < 8; ++i) {\n                float v = fabsf"),
 ]
