@@ -35,7 +35,7 @@ from ._lib import FocusError, FocusLibraryMissing, library_path  # noqa: F401
 
 __all__ = ["tensor_scale", "quantize", "dequantize", "quantize_act_per_token", "Quantized",
            "quantize_fo6", "quantize_act_per_token_fo6", "quantize_fo6_many",
-           "quantize_mixfp4", "quantize_mixfp4_many",
+           "quantize_mixfp4", "quantize_mixfp4_many", "nvfp4_linear",
            "quantize_mx", "quantize_mx_many", "dequantize_mx",
            "tensor_scale_many", "quantize_many", "dequantize_many", "Batch",
            "FocusError", "FocusLibraryMissing", "abi_version", "library_path"]
@@ -368,6 +368,44 @@ def quantize_mixfp4_many(ws, maps, tiles, s2s, outs=None, dequant: bool = True, 
     b = Batch("focus_quantize_mixfp4_many", arr, (list(ws), list(maps), list(s2s), res), dev)
     b.outs = res
     return b.run() if run else b
+
+
+# ---------------------------------------------------------------------------
+# the NVFP4 linear layer
+# ---------------------------------------------------------------------------
+
+def nvfp4_linear(x: Quantized, w: Quantized, out_dtype: torch.dtype = torch.bfloat16,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X' W'^T for NVFP4 activations ``x`` (codes [M, K/2], scales
+    [M, K/16], s2 [M] per token or one value) and NVFP4 weights ``w`` (codes
+    [N, K/2], scales [N, K/16], one s2), on the matrix cores; Y [M, N] in
+    ``out_dtype`` (bfloat16 or float32)."""
+    dev = x.codes.device
+    for name, t in (("x.codes", x.codes), ("x.scales", x.scales), ("w.codes", w.codes), ("w.scales", w.scales)):
+        _check_dev(name, t, torch.uint8, dev)
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _check_dev("x.s2", x.s2, torch.float32, dev)
+    _check_dev("w.s2", w.s2, torch.float32, dev)
+    M, K = x.codes.shape[0], 2 * x.codes.shape[1]
+    N = w.codes.shape[0]
+    if w.codes.shape[1] * 2 != K or tuple(x.scales.shape) != (M, K // 16) or tuple(w.scales.shape) != (N, K // 16):
+        raise ValueError("operand shapes do not match: x [M, K], w [N, K] with K % 16 == 0")
+    if x.s2.numel() not in (1, M) or w.s2.numel() != 1:
+        raise ValueError("x.s2 needs 1 or M values, w.s2 one")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    else:
+        _check_dev("out", out, out_dtype, dev)
+        if tuple(out.shape) != (M, N) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [M, N] tensor")
+    per_row = 1 if (x.s2.numel() == M and M > 1) else 0
+    _lib.check(_lib.lib().focus_nvfp4_linear(_p(x.codes), _p(x.scales), _p(x.s2), per_row, M, _p(w.codes),
+                                             _p(w.scales), _p(w.s2), N, K, _p(out),
+                                             0 if out_dtype == torch.float32 else 1, _stream(x.codes)))
+    return out
 
 
 # ---------------------------------------------------------------------------

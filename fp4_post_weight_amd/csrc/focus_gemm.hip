@@ -1,0 +1,316 @@
+// focus_gemm.hip -- the NVFP4 linear layer on gfx950 matrix cores.
+//
+// What it computes ("FOCUS NVFP4 scales for Llama-3.2-1B-Instruct (our
+// reproduction)": section "What this is" -- the deployed model is plain
+// NVFP4 and runs on standard NVFP4 kernels -- and section "Perplexity" --
+// NVFP4 weights with one FP32 scale per tensor, NVFP4 activations with one
+// scale per token):
+//     Y[t, o] = s2x[t] * s2w * sum_k (cx[t,k] * Sx[t, k/16]) * (cw[o,k] * Sw[o, k/16])
+// with c an E2M1 value and S an E4M3 block scale.
+//
+// How it maps onto CDNA4:
+//  * Each operand element c*S has at most 5 significant bits (E2M1 has 2,
+//    E4M3 4) and lies in [2^-10, 2688] for normal scales, so it is exact in
+//    FP16, and the product of two such values is exact in FP32.  The
+//    contraction therefore runs on the FP16 matrix cores
+//    (v_mfma_f32_32x32x16_f16) with FP32 accumulation, and s2x*s2w is applied
+//    once per output.  (gfx950's FP4 matrix instructions take one E8M0
+//    scale per 32 elements; NVFP4's E4M3 scale per 16 elements is not
+//    expressible there.)
+//  * Dequantization costs about one vector operation per element and is
+//    done once per workgroup, before LDS: the scale byte is split into
+//    S = 2^E * mu (mu in [1, 2)); v_cvt_scalef32_pk_f16_fp4 with scale 2^E
+//    gives c * 2^E for two codes, and one packed FP16 multiply by mu gives
+//    c * S, both exact.
+//  * Workgroup tile 256 x 256 x 64 (4 wavefronts, each 128 x 128 = 4 x 4
+//    MFMA tiles of 32 x 32, 256 FP32 accumulators per lane).  Both operand
+//    tiles are FP16 in LDS (rows padded to 144 bytes) in two stages: while
+//    the matrix cores consume one k-step, the codes of the next step
+//    (loaded into registers one step earlier) are dequantized into the other
+//    stage, and the step after that is being loaded.  Fragments are read two
+//    k16 slices ahead, the dequantization runs in slices 0-1 interleaved with
+//    the matrix instructions, and the one barrier per step sits after slice
+//    1, so slices 2-3 cover the reads of the next step's first fragments.
+//    LDS traffic (about 192 KB per step per CU against an LDS that delivers
+//    about 128 B per clock) is what bounds this kernel below the matrix-core
+//    peak.
+//  * Loads are straight-line in the common case (K % 64 == 0, aligned): a
+//    row past the end of X or W reads the last row instead; it only feeds
+//    outputs that are never stored.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "focus_gemm.h"
+#include "focus_numerics.h"
+
+namespace focus {
+
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kGemmThreads = 256;
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kWaveM = 128, kWaveN = 128;
+constexpr int kTilesM = kWaveM / 32, kTilesN = kWaveN / 32;
+constexpr int kLdsStride = kBK + 8;  // halves per LDS row: 144 bytes
+
+// Codes (8 bytes per 16-element block) and scale bytes of one row's k-step:
+// four blocks.  Rows beyond `nrows` and blocks beyond K read as zero.
+struct RowChunk {
+    uint2 c[4];
+    uint32_t s;
+};
+
+// FAST: K % 64 == 0, codes 16-byte and scales 4-byte aligned (two 16-byte
+// loads and one 4-byte load per row); otherwise one 8-byte load and one byte
+// per block.
+template <bool FAST>
+__device__ __forceinline__ RowChunk load_chunk(const uint8_t* __restrict__ codes,
+                                               const uint8_t* __restrict__ scales, int64_t row,
+                                               int64_t nrows, int64_t K, int64_t k0) {
+    RowChunk r;
+    if (FAST) {
+        // Unconditional loads: a row beyond the tensor reads the last row
+        // (always in bounds; nrows >= 1 here).  Such a row of X only feeds
+        // output rows >= M and such a row of W only output columns >= N,
+        // which are never stored, so no masking is needed -- and straight-
+        // line loads let the wait counters track them exactly.
+        const int64_t rr = row < nrows ? row : nrows - 1;
+        const uint8_t* cp = codes + rr * (K / 2) + k0 / 2;
+        const uint4 v0 = *reinterpret_cast<const uint4*>(cp);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(cp + 16);
+        r.s = *reinterpret_cast<const uint32_t*>(scales + rr * (K / 16) + k0 / 16);
+        r.c[0] = make_uint2(v0.x, v0.y);
+        r.c[1] = make_uint2(v0.z, v0.w);
+        r.c[2] = make_uint2(v1.x, v1.y);
+        r.c[3] = make_uint2(v1.z, v1.w);
+        return r;
+    }
+    r.s = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) r.c[b] = make_uint2(0, 0);
+    if (row >= nrows) return r;
+    const uint8_t* cp = codes + row * (K / 2) + k0 / 2;
+    const uint8_t* sp = scales + row * (K / 16) + k0 / 16;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        if (k0 + 16 * b < K) {
+            r.c[b] = *reinterpret_cast<const uint2*>(cp + 8 * b);
+            r.s |= (uint32_t)sp[b] << (8 * b);
+        }
+    }
+    return r;
+}
+
+// c * S for the 16 elements of one block, as FP16, elements 0-7 in lo and
+// 8-15 in hi, branch-free for every scale byte.  With exponent field e and
+// mantissa field m, S = 2^(max(e,1) - 10) * mu, mu = 8 + m (normal, e >= 1)
+// or m (zero and subnormal, e == 0), an integer in [0, 15]; 0x7F / 0xFF are
+// NaN.  v_cvt_scalef32_pk_f16_fp4 with the power of two gives
+// c * 2^(max(e,1) - 10) in [2^-10, 192] and one packed FP16 multiply by mu
+// gives c * S (at most 6 significant bits, at most 2880): both exact.
+__device__ __forceinline__ void dequant_block_f16(uint2 c, uint32_t sbyte, f16x8& lo, f16x8& hi) {
+    const uint32_t ef = (sbyte >> 3) & 15u, mb = sbyte & 7u;
+    const float p2 = __uint_as_float((max(ef, 1u) + 117u) << 23);
+    const _Float16 mag = (_Float16)(uint16_t)(mb | (ef != 0u ? 8u : 0u));
+    uint16_t mu_bits = __builtin_bit_cast(uint16_t, mag) | (uint16_t)((sbyte & 0x80u) << 8);
+    mu_bits = (sbyte & 0x7Fu) == 0x7Fu ? (uint16_t)0x7E00u : mu_bits;
+    const _Float16 mu = __builtin_bit_cast(_Float16, mu_bits);
+    const f16x2 m2 = {mu, mu};
+    const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c.x, p2, 0) * m2;
+    const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c.x, p2, 1) * m2;
+    const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c.x, p2, 2) * m2;
+    const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c.x, p2, 3) * m2;
+    const f16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c.y, p2, 0) * m2;
+    const f16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c.y, p2, 1) * m2;
+    const f16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c.y, p2, 2) * m2;
+    const f16x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c.y, p2, 3) * m2;
+    lo = (f16x8){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+    hi = (f16x8){b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+}
+
+__device__ __forceinline__ void store_chunk(_Float16* lds_row, const RowChunk& r) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        f16x8 lo, hi;
+        dequant_block_f16(r.c[b], (r.s >> (8 * b)) & 0xFFu, lo, hi);
+        *reinterpret_cast<f16x8*>(lds_row + 16 * b) = lo;
+        *reinterpret_cast<f16x8*>(lds_row + 16 * b + 8) = hi;
+    }
+}
+
+// Fragments of k16-slice kk of the wavefront's 128 rows of one operand tile.
+__device__ __forceinline__ void load_frags(f16x8 (&f)[4], const _Float16* tile, int row0, int kk,
+                                           int frag_row, int frag_k) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        f[i] = *reinterpret_cast<const f16x8*>(tile + (row0 + i * 32 + frag_row) * kLdsStride + kk * 16 +
+                                               frag_k);
+}
+
+template <bool FAST, bool BF16_OUT>
+__global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64_t tiles_n) {
+    // two stages of both operand tiles: the matrix cores read one while the
+    // next k-step is dequantized into the other
+    __shared__ _Float16 lds[2][(kBM + kBN) * kLdsStride];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t tile = blockIdx.x;
+    const int64_t m0 = (tile / tiles_n) * kBM;
+    const int64_t n0 = (tile % tiles_n) * kBN;
+    const int frag_row = lane & 31;
+    const int frag_k = (lane >> 5) * 8;
+
+    f32x16 acc[kTilesM][kTilesN];
+#pragma unroll
+    for (int i = 0; i < kTilesM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTilesN; ++j) acc[i][j] = (f32x16){};
+
+    // thread tid stages row tid of both operand tiles (K == 0: nothing to read)
+    const int64_t nsteps = (a.K + kBK - 1) / kBK;
+    const int64_t mrows = nsteps > 0 ? a.M : 0, nrows = nsteps > 0 ? a.N : 0;
+    RowChunk ra = load_chunk<FAST>(a.xc, a.xs, m0 + tid, mrows, a.K, 0);
+    RowChunk rb = load_chunk<FAST>(a.wc, a.ws, n0 + tid, nrows, a.K, 0);
+    store_chunk(lds[0] + tid * kLdsStride, ra);
+    store_chunk(lds[0] + (kBM + tid) * kLdsStride, rb);
+    if (nsteps > 1) {
+        ra = load_chunk<FAST>(a.xc, a.xs, m0 + tid, a.M, a.K, kBK);
+        rb = load_chunk<FAST>(a.wc, a.ws, n0 + tid, a.N, a.K, kBK);
+    }
+    __syncthreads();
+    const int arow = wm * kWaveM, brow = kBM + wn * kWaveN;
+    // fragments of the four k16 slices of a step, read two slices ahead
+    f16x8 fa0[4], fb0[4], fa1[4], fb1[4], fa2[4], fb2[4], fa3[4], fb3[4];
+    load_frags(fa0, lds[0], arow, 0, frag_row, frag_k);
+    load_frags(fb0, lds[0], brow, 0, frag_row, frag_k);
+    load_frags(fa1, lds[0], arow, 1, frag_row, frag_k);
+    load_frags(fb1, lds[0], brow, 1, frag_row, frag_k);
+
+    auto mfma16 = [&](const f16x8 (&fa)[4], const f16x8 (&fb)[4]) {
+#pragma unroll
+        for (int i = 0; i < kTilesM; ++i)
+#pragma unroll
+            for (int j = 0; j < kTilesN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    };
+    // One k-step s: slices 0 and 1 read the fragments of slices 2 and 3 and
+    // dequantize chunk s + 1 (blocks 0-1, then 2-3, both operands) into the
+    // other stage; after the barrier, slices 2 and 3 read the next step's
+    // slices 0 and 1 from it.  Chunk s + 2 is loaded at the start of the
+    // step (clamped to the last chunk so the code stays straight-line).
+    for (int64_t s = 0; s < nsteps; ++s) {
+        const _Float16* cur = lds[s & 1];
+        _Float16* nxt = lds[(s + 1) & 1];
+        const int64_t kn = (s + 2 < nsteps ? s + 2 : nsteps - 1) * kBK;
+        const RowChunk na = load_chunk<FAST>(a.xc, a.xs, m0 + tid, a.M, a.K, kn);
+        const RowChunk nb = load_chunk<FAST>(a.wc, a.ws, n0 + tid, a.N, a.K, kn);
+        auto dequant = [&](int b) {
+            f16x8 lo, hi;
+            dequant_block_f16(ra.c[b], (ra.s >> (8 * b)) & 0xFFu, lo, hi);
+            *reinterpret_cast<f16x8*>(nxt + tid * kLdsStride + 16 * b) = lo;
+            *reinterpret_cast<f16x8*>(nxt + tid * kLdsStride + 16 * b + 8) = hi;
+            dequant_block_f16(rb.c[b], (rb.s >> (8 * b)) & 0xFFu, lo, hi);
+            *reinterpret_cast<f16x8*>(nxt + (kBM + tid) * kLdsStride + 16 * b) = lo;
+            *reinterpret_cast<f16x8*>(nxt + (kBM + tid) * kLdsStride + 16 * b + 8) = hi;
+        };
+        // slice 0
+        load_frags(fa2, cur, arow, 2, frag_row, frag_k);
+        load_frags(fb2, cur, brow, 2, frag_row, frag_k);
+        mfma16(fa0, fb0);
+        dequant(0);
+        dequant(1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            if (g >= 12) __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // slice 1
+        load_frags(fa3, cur, arow, 3, frag_row, frag_k);
+        load_frags(fb3, cur, brow, 3, frag_row, frag_k);
+        mfma16(fa1, fb1);
+        dequant(2);
+        dequant(3);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            if (g >= 12) __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // the other stage is complete and this stage's reads are done
+        __syncthreads();
+        // slice 2
+        load_frags(fa0, nxt, arow, 0, frag_row, frag_k);
+        load_frags(fb0, nxt, brow, 0, frag_row, frag_k);
+        mfma16(fa2, fb2);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // slice 3
+        load_frags(fa1, nxt, arow, 1, frag_row, frag_k);
+        load_frags(fb1, nxt, brow, 1, frag_row, frag_k);
+        mfma16(fa3, fb3);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        ra = na;
+        rb = nb;
+    }
+
+    // epilogue: register r of lane l in a 32 x 32 tile holds row
+    // 8*(r/4) + 4*(l/32) + r%4 and column l%32; Y = acc * (s2x[row] * s2w)
+    const float s2w = a.ws2[0];
+#pragma unroll
+    for (int i = 0; i < kTilesM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t row = m0 + wm * kWaveM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (row >= a.M) continue;
+            const float sc = a.xs2[a.xs2_per_row ? row : 0] * s2w;
+#pragma unroll
+            for (int j = 0; j < kTilesN; ++j) {
+                const int64_t col = n0 + wn * kWaveN + j * 32 + (lane & 31);
+                if (col >= a.N) continue;
+                const float v = acc[i][j][r] * sc;
+                if (BF16_OUT) {
+                    const uint32_t p = bf16_pair(v, 0.0f);
+                    reinterpret_cast<uint16_t*>(a.y)[row * a.N + col] = (uint16_t)(p & 0xFFFFu);
+                } else {
+                    reinterpret_cast<float*>(a.y)[row * a.N + col] = v;
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_nvfp4_linear(const GemmArgs& a, bool fast, bool bf16_out, hipStream_t stream) {
+    const int64_t tiles_m = (a.M + kBM - 1) / kBM, tiles_n = (a.N + kBN - 1) / kBN;
+    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kGemmThreads);
+    if (fast) {
+        if (bf16_out) hipLaunchKernelGGL((k_nvfp4_linear<true, true>), grid, block, 0, stream, a, tiles_n);
+        else hipLaunchKernelGGL((k_nvfp4_linear<true, false>), grid, block, 0, stream, a, tiles_n);
+    } else {
+        if (bf16_out) hipLaunchKernelGGL((k_nvfp4_linear<false, true>), grid, block, 0, stream, a, tiles_n);
+        else hipLaunchKernelGGL((k_nvfp4_linear<false, false>), grid, block, 0, stream, a, tiles_n);
+    }
+    return hipGetLastError();
+}
+
+int64_t nvfp4_linear_workgroups(int64_t M, int64_t N) {
+    return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+}
+
+}  // namespace focus

@@ -266,6 +266,31 @@ typedef struct focus_mixfp4_desc {
 /* Batched MixFP4, with the rules of the batched calls above. */
 int focus_quantize_mixfp4_many(const focus_mixfp4_desc* descs, int n, void* stream);
 
+/*
+ * The NVFP4 linear layer, the consumer of the stored format ("FOCUS NVFP4
+ * scales for Llama-3.2-1B-Instruct (our reproduction)": section "What this
+ * is" -- the deployed model is plain NVFP4 on standard NVFP4 kernels -- and
+ * section "Perplexity" -- NVFP4 weights with one FP32 scale per tensor and
+ * NVFP4 activations with one scale per token):
+ *     Y[t, o] = s2x[t] * s2w * sum_k (cx[t,k] * Sx[t,k/16]) * (cw[o,k] * Sw[o,k/16])
+ * c the E2M1 value of a code, S the E4M3 value of a block's scale byte.
+ *   x_codes  [M, K/2], x_scales [M, K/16]   activations, e.g. from
+ *            focus_quantize_act_per_token(_fo6) (element 2j in the low nibble)
+ *   x_s2     [M] when x_s2_per_row == 1, else one float
+ *   w_codes  [N, K/2], w_scales [N, K/16], w_s2 one float: a quantized weight
+ *            [out_features = N, in_features = K]
+ *   y        [M, N] row-major, FP32 (y_dtype 0) or BF16 (y_dtype 1)
+ *   K % 16 == 0; M, N <= 2^31; codes 8-byte aligned, y aligned to its type.
+ * Arithmetic: each c*S is exact in FP16 and each product exact in FP32; the
+ * sum over k is accumulated in FP32 by the matrix cores (order unspecified),
+ * then multiplied by RN32(s2x[t] * s2w) and, for BF16 output, rounded once
+ * to nearest even.  |Y - exact| <= (about K * 2^-24) * sum_k |products| *
+ * s2x * s2w (+ half a BF16 ulp of Y).  K == 0 writes zeros.
+ */
+int focus_nvfp4_linear(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_s2,
+                       int x_s2_per_row, int64_t M, const uint8_t* w_codes, const uint8_t* w_scales,
+                       const float* w_s2, int64_t N, int64_t K, void* y, int y_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -129,6 +129,17 @@ def tile_map(rows: int, cols: int, tile: Tuple[int, int], *, frac: float, seed: 
     return (u < frac).to(torch.uint8)
 
 
+def nvfp4_operand(rows: int, K: int, *, seed: int, tensor_id: int, scale_lo: int = 0x28,
+                  scale_hi: int = 0x50, device="cpu"):
+    """A stored NVFP4 tensor [rows, K] as random bytes: codes uniform over all
+    256 byte values (two E2M1 codes each), scale bytes uniform over the
+    normal E4M3 range [scale_lo, scale_hi)."""
+    g = generator(seed, tensor_id, device)
+    codes = torch.randint(0, 256, (rows, K // 2), generator=g, dtype=torch.uint8, device=device)
+    scales = torch.randint(scale_lo, scale_hi, (rows, K // 16), generator=g, dtype=torch.uint8, device=device)
+    return codes, scales
+
+
 # E0M3 fraction of each published map: E0M3 tiles / all tiles.
 MIXFP4_FRAC = {(8, 64): 83_771 / 13_631_488, (16, 64): 52_719 / 6_815_744, (256, 64): 9_447 / 425_984}
 

@@ -208,3 +208,23 @@ def test_mixfp4_validation(lib):
     assert many(None, 0, None) == OK
     assert many(None, 1, None) == ERR_NULL
     assert ct.sizeof(MD) == 10 * 8
+
+
+def test_linear_validation(lib):
+    f = lib.focus_nvfp4_linear
+    #        xc    xs    xs2 per  M   wc    ws    ws2   N   K   y    dt  stream
+    assert f(FAKE, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, 40, FAKE, 0, None) == ERR_SHAPE   # K % 16
+    assert f(FAKE, FAKE, FAKE, 1, -1, FAKE, FAKE, FAKE, 8, 64, FAKE, 0, None) == ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, (1 << 31) + 1, 64, FAKE, 0, None) == ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 2, 4, FAKE, FAKE, FAKE, 8, 64, FAKE, 0, None) == ERR_RANGE
+    assert f(FAKE, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, 64, FAKE, 2, None) == ERR_RANGE
+    assert f(FAKE, FAKE, FAKE, 1, 1 << 21, FAKE, FAKE, FAKE, 1 << 21, 16, FAKE, 0, None) == ERR_RANGE  # grid
+    assert f(None, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, 64, FAKE, 0, None) == ERR_NULL
+    assert f(FAKE, FAKE, FAKE, 1, 4, FAKE, None, FAKE, 8, 64, FAKE, 0, None) == ERR_NULL
+    assert f(FAKE, FAKE, None, 1, 4, FAKE, FAKE, FAKE, 8, 64, FAKE, 0, None) == ERR_NULL
+    assert f(FAKE, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, 64, None, 0, None) == ERR_NULL
+    assert f(FAKE + 4, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, 64, FAKE, 0, None) == ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, 64, FAKE + 2, 0, None) == ERR_ALIGN
+    assert f(FAKE, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE + 1, 8, 64, FAKE, 0, None) == ERR_ALIGN
+    assert f(None, None, None, 1, 0, None, None, None, 8, 64, None, 0, None) == OK    # empty
+    assert f(None, None, None, 1, 4, None, None, None, 0, 64, None, 1, None) == OK

@@ -1,0 +1,149 @@
+"""The NVFP4 linear layer Y = X' W'^T on the matrix cores (through the C
+ABI) against the oracle's binary64 definition.  MI355X only (marker gpu).
+
+Bound (derived from the arithmetic): every c*S is exact in FP16 and every
+product exact in FP32; the FP32 accumulation of K products in any order errs
+by at most (K - 1) roundings of at most 2^-23 relative each (round-to-nearest
+gives 2^-24; 2^-23 also covers truncation), and two more roundings come from
+s2x*s2w and the final product, so
+    |Y - exact| <= (2K + 4) * 2^-24 * sum_k |products| * s2x * s2w,
+plus half a BF16 spacing (2^-9 |Y|, 2^-8 taken) for BF16 output.  When all
+scales are 1 and the s2 are powers of two every partial sum is exact in FP32
+and Y must equal the oracle bit for bit; that case pins the operand and
+output layouts exactly.  Inputs are random NVFP4 bytes (synth.nvfp4_operand),
+never outputs of the HIP path.
+"""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import parity
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def focus():
+    import fp4_post_weight_amd as f
+    f._lib.lib()
+    assert torch.cuda.is_available()
+    return f
+
+
+def operands(M, N, K, seed, **kw):
+    xc, xs = synth.nvfp4_operand(M, K, seed=seed, tensor_id=40, **kw)
+    wc, ws = synth.nvfp4_operand(N, K, seed=seed, tensor_id=41, **kw)
+    return xc, xs, wc, ws
+
+
+def oracle_linear(orc, xc, xs, s2x, wc, ws, s2w):
+    """The oracle over row chunks of X on all host threads."""
+    M = xc.shape[0]
+    n = max(1, min(parity.threads(), M))
+    bounds = np.linspace(0, M, n + 1).astype(int)
+    s2x = np.atleast_1d(s2x)
+
+    def run(i):
+        a, b = bounds[i], bounds[i + 1]
+        return orc.nvfp4_linear(xc[a:b], xs[a:b], s2x[a:b] if s2x.size == M else s2x, wc, ws, s2w)
+
+    with ThreadPoolExecutor(n) as ex:
+        parts = list(ex.map(run, range(n)))
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+
+
+def gpu_linear(focus, xc, xs, s2x, wc, ws, s2w, out_dtype):
+    x = focus.Quantized(xc.to(DEV), xs.to(DEV), None, torch.as_tensor(s2x, dtype=torch.float32).reshape(-1).to(DEV))
+    w = focus.Quantized(wc.to(DEV), ws.to(DEV), None, torch.tensor([s2w], dtype=torch.float32, device=DEV))
+    y = focus.nvfp4_linear(x, w, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+def check_bound(y, ref, refabs, K, bf16, label):
+    bound = (2 * K + 4) * 2.0 ** -24 * refabs
+    if bf16:
+        bound = bound + 2.0 ** -8 * np.abs(ref)
+    err = np.abs(y - ref)
+    bad = err > bound
+    assert not bad.any(), (f"{label}: {bad.sum()} outputs outside the bound; worst at "
+                           f"{np.unravel_index(np.argmax(err - bound), err.shape)}")
+    return float(np.max(err / np.maximum(refabs, 1e-300)))
+
+
+def test_exact_when_partial_sums_are_exact(focus, orc):
+    M, N, K = 300, 520, 1024
+    xc, _, wc, _ = operands(M, N, K, 1)
+    xs = torch.full((M, K // 16), 0x38, dtype=torch.uint8)
+    ws = torch.full((N, K // 16), 0x38, dtype=torch.uint8)
+    s2x = np.exp2(-(np.arange(M) % 7)).astype(np.float32)
+    s2w = np.float32(0.125)
+    ref, _ = oracle_linear(orc, xc.numpy(), xs.numpy(), s2x, wc.numpy(), ws.numpy(), s2w)
+    y32 = gpu_linear(focus, xc, xs, s2x, wc, ws, s2w, torch.float32)
+    assert np.array_equal(y32, ref), f"{np.count_nonzero(y32 != ref)} FP32 outputs differ"
+    y16 = gpu_linear(focus, xc, xs, s2x, wc, ws, s2w, torch.bfloat16)
+    want = torch.from_numpy(ref).float().to(torch.bfloat16).float().numpy().astype(np.float64)
+    assert np.array_equal(y16, want)
+
+
+SHAPES = [(1, 1, 16), (7, 33, 48), (255, 257, 64), (257, 255, 1040), (300, 520, 4096), (64, 512, 8192),
+          (513, 96, 80)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES, ids=lambda v: str(v))
+def test_linear_within_bound(focus, orc, M, N, K):
+    xc, xs, wc, ws = operands(M, N, K, M + N + K)
+    rng = np.random.default_rng(K)
+    s2x = (rng.uniform(0.5, 2.0, M) * 2.0 ** -9).astype(np.float32)
+    s2w = np.float32(3.0e-4)
+    ref, refabs = oracle_linear(orc, xc.numpy(), xs.numpy(), s2x, wc.numpy(), ws.numpy(), s2w)
+    for dt in (torch.float32, torch.bfloat16):
+        y = gpu_linear(focus, xc, xs, s2x, wc, ws, s2w, dt)
+        check_bound(y, ref, refabs, K, dt == torch.bfloat16, f"{(M, N, K)} {dt}")
+
+
+def test_linear_single_activation_scale_and_wide_scales(focus, orc):
+    M, N, K = 130, 200, 512
+    xc, xs, wc, ws = operands(M, N, K, 5, scale_lo=0x01, scale_hi=0x7F)  # subnormal to 448
+    ref, refabs = oracle_linear(orc, xc.numpy(), xs.numpy(), np.float32(0.02), wc.numpy(), ws.numpy(),
+                                np.float32(0.001))
+    y = gpu_linear(focus, xc, xs, np.float32(0.02), wc, ws, np.float32(0.001), torch.float32)
+    check_bound(y, ref, refabs, K, False, "one s2x, scale bytes 0x01..0x7E")
+
+
+def test_linear_degenerate(focus):
+    x = focus.Quantized(torch.zeros((5, 0), dtype=torch.uint8, device=DEV),
+                        torch.zeros((5, 0), dtype=torch.uint8, device=DEV), None,
+                        torch.ones(5, dtype=torch.float32, device=DEV))
+    w = focus.Quantized(torch.zeros((3, 0), dtype=torch.uint8, device=DEV),
+                        torch.zeros((3, 0), dtype=torch.uint8, device=DEV), None,
+                        torch.ones(1, dtype=torch.float32, device=DEV))
+    y = focus.nvfp4_linear(x, w, out_dtype=torch.float32, out=torch.full((5, 3), 7.0, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(y, torch.zeros((5, 3), device=DEV))  # K = 0: the empty sum
+
+
+@pytest.mark.parametrize("N,K", sorted(set(synth.LLAMA_8B.layer_shapes())), ids=lambda v: str(v))
+def test_linear_full_size_sampled(focus, orc, N, K):
+    """8192 tokens through every 8B linear shape at full size (the launch the
+    benchmark times); sampled rows and columns against the oracle."""
+    M = 8192
+    xc, xs = synth.nvfp4_operand(M, K, seed=7, tensor_id=42, device=DEV)
+    wc, ws = synth.nvfp4_operand(N, K, seed=7, tensor_id=43, device=DEV)
+    s2x = torch.rand(M, generator=synth.generator(7, 44, DEV), device=DEV) * 1e-3 + 1e-4
+    s2w = torch.tensor([2.0e-4], device=DEV)
+    y = focus.nvfp4_linear(focus.Quantized(xc, xs, None, s2x), focus.Quantized(wc, ws, None, s2w),
+                           out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(N + K)
+    ri = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 6)]))
+    ci = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 62)]))
+    ref, refabs = oracle_linear(orc, xc[ri].cpu().numpy(), xs[ri].cpu().numpy(), s2x[ri].cpu().numpy(),
+                                wc[ci].cpu().numpy(), ws[ci].cpu().numpy(), np.float32(2.0e-4))
+    got = y[torch.from_numpy(ri).to(DEV)][:, torch.from_numpy(ci).to(DEV)].float().cpu().numpy().astype(np.float64)
+    check_bound(got, ref, refabs, K, True, f"8192 x {N} x {K}")
