@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Gweights/s + achieved HBM GB/s (% of peak), FOCUS NVFP4 quantize+pack, 8B set"
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0   # dense FP16 matrix-core peak (the linear layer's contraction type)
 
 # algorithmic bytes per weight (per element for activations)
 B_TENSOR_SCALE = 2.0
@@ -302,6 +303,9 @@ def main():
             rows[f"FlipQuant MixFP4 {th}x{tw} map ({100 * share:.2f}% E0M3 tiles) + w' (after the steps)"] = \
                 row(t_mix[(th, tw)], (B_ACT + 2.0 + 1.0 / (th * tw)) * n_weights, n_weights)
 
+    if extra_rows:
+        rows.update(linear_rows(focus, synth, ws, dev, stream))
+
     # ---- CPU baseline: the oracle on a bounded sample ----------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -348,6 +352,49 @@ def main():
         "gpu_ms_timed": round(gpu_ms, 3),
     }
     print(json.dumps(line), flush=True)
+
+
+def linear_rows(focus, synth, ws, dev, stream):
+    """The NVFP4 linear layer Y = X' W'^T on each distinct layer shape of the
+    set: 8192 tokens (matrix-core bound; FLOP/s against the FP16 peak) and 16
+    tokens (bound by streaming W; operand bytes against the HBM peak).  Each
+    shape is timed over repeated calls of the C ABI with prepared arguments,
+    the operands random NVFP4 bytes."""
+    import torch
+    lib = focus._lib.lib()
+    out = {}
+    shapes = sorted(set(ws.layer_shapes()))
+    for m_tok, reps in ((8192, 10), (16, 50)):
+        tot_ms, tot_flop, tot_bytes = 0.0, 0.0, 0.0
+        for n, k in shapes:
+            xc, xs = synth.nvfp4_operand(m_tok, k, seed=3, tensor_id=60, device=dev)
+            wc, wsc = synth.nvfp4_operand(n, k, seed=3, tensor_id=61, device=dev)
+            s2x = torch.full((m_tok,), 1e-3, dtype=torch.float32, device=dev)
+            s2w = torch.full((1,), 1e-3, dtype=torch.float32, device=dev)
+            y = torch.empty((m_tok, n), dtype=torch.bfloat16, device=dev)
+            args = (xc.data_ptr(), xs.data_ptr(), s2x.data_ptr(), 1, m_tok, wc.data_ptr(), wsc.data_ptr(),
+                    s2w.data_ptr(), n, k, y.data_ptr(), 1, stream.cuda_stream)
+            for _ in range(3):
+                focus._lib.check(lib.focus_nvfp4_linear(*args))
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                lib.focus_nvfp4_linear(*args)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / reps
+            tot_ms += ms
+            tot_flop += 2.0 * m_tok * n * k
+            tot_bytes += (m_tok + n) * k * 0.5625 + 2.0 * m_tok * n
+            del xc, xs, wc, wsc, y
+        tflops = tot_flop / (tot_ms * 1e-3) / 1e12
+        gbs = tot_bytes / (tot_ms * 1e-3) / 1e9
+        key = f"NVFP4 linear Y = X' W'^T, {m_tok} tokens through the {len(shapes)} layer shapes (after the steps)"
+        out[key] = {"ms": round(tot_ms, 4), "TFLOP_s": round(tflops, 1),
+                    "frac_mfma_f16_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                    "GB_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
 
 
 def cpu_baseline(lins, W, M, Q, X, frac):

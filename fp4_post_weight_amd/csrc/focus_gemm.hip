@@ -294,9 +294,208 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
     }
 }
 
+// ---------------------------------------------------------------------------
+// Few tokens (M <= 64): every weight element is used by at most 64 outputs,
+// so the layer is bound by streaming W, and no operand needs sharing through
+// LDS.  A workgroup of 16 wavefronts owns 32 output columns (32 rows of W)
+// and all M <= 32 * MT rows of X; the 64-wide k-steps are dealt round-robin
+// to its wavefronts (neighbouring wavefronts read neighbouring bytes of each
+// row), each accumulates a partial 32 x 32 tile per M-tile, and one LDS
+// reduction sums the 16 partial tiles (deterministic, no workspace).
+//
+// Within a k-step the sum is order-free, so lane group h = lane / 32 takes
+// k in [32h, 32h + 32): one 16-byte load per row and step, and slice kk (one
+// MFMA k-depth of 16) is dword kk of it in both operands.
+// ---------------------------------------------------------------------------
+
+constexpr int kSkinnyWaves = 16;
+
+// A lane's share of one row and k-step: 16 bytes of codes (32 elements,
+// blocks 2h and 2h+1 of the step) and their two scale bytes (bits 0-7 and
+// 8-15).  Rows past `nrows` read the last row (FAST) or zeros; k past K reads
+// zeros.
+struct LaneChunk {
+    uint4 c;
+    uint32_t s;
+};
+
+template <bool FAST>
+__device__ __forceinline__ LaneChunk load_lane(const uint8_t* __restrict__ codes,
+                                               const uint8_t* __restrict__ scales, int64_t row,
+                                               int64_t nrows, int64_t K, int64_t k0, int h) {
+    LaneChunk r;
+    if (FAST) {
+        const int64_t rr = row < nrows ? row : nrows - 1;
+        r.c = *reinterpret_cast<const uint4*>(codes + rr * (K / 2) + k0 / 2 + 16 * h);
+        r.s = *reinterpret_cast<const uint16_t*>(scales + rr * (K / 16) + k0 / 16 + 2 * h);
+        return r;
+    }
+    r.c = make_uint4(0, 0, 0, 0);
+    r.s = 0;
+    if (row >= nrows || k0 < 0) return r;
+    const uint8_t* cp = codes + row * (K / 2) + k0 / 2 + 16 * h;
+    const uint8_t* sp = scales + row * (K / 16) + k0 / 16 + 2 * h;
+    const int64_t kb = k0 + 32 * h;
+    if (kb < K) {
+        const uint2 v = *reinterpret_cast<const uint2*>(cp);
+        r.c.x = v.x;
+        r.c.y = v.y;
+        r.s = sp[0];
+    }
+    if (kb + 16 < K) {
+        const uint2 v = *reinterpret_cast<const uint2*>(cp + 8);
+        r.c.z = v.x;
+        r.c.w = v.y;
+        r.s |= (uint32_t)sp[1] << 8;
+    }
+    return r;
+}
+
+// 2^E and mu of a scale byte (the decomposition of dequant_block_f16), mu as
+// an FP16 pair.
+struct ScaleParts {
+    float p2;
+    f16x2 mu;
+};
+
+__device__ __forceinline__ ScaleParts split_scale(uint32_t sbyte) {
+    const uint32_t ef = (sbyte >> 3) & 15u, mb = sbyte & 7u;
+    ScaleParts r;
+    r.p2 = __uint_as_float((max(ef, 1u) + 117u) << 23);
+    const _Float16 mag = (_Float16)(uint16_t)(mb | (ef != 0u ? 8u : 0u));
+    uint16_t mu_bits = __builtin_bit_cast(uint16_t, mag) | (uint16_t)((sbyte & 0x80u) << 8);
+    mu_bits = (sbyte & 0x7Fu) == 0x7Fu ? (uint16_t)0x7E00u : mu_bits;
+    const _Float16 mu = __builtin_bit_cast(_Float16, mu_bits);
+    r.mu = (f16x2){mu, mu};
+    return r;
+}
+
+// Eight codes (one dword) -> fragment of c * S.
+__device__ __forceinline__ f16x8 frag_from_codes(uint32_t w, const ScaleParts& sp) {
+    const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sp.p2, 0) * sp.mu;
+    const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sp.p2, 1) * sp.mu;
+    const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sp.p2, 2) * sp.mu;
+    const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sp.p2, 3) * sp.mu;
+    return (f16x8){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int kk) {
+    return kk == 0 ? v.x : kk == 1 ? v.y : kk == 2 ? v.z : v.w;
+}
+
+template <bool FAST, bool BF16_OUT, int MT>
+__global__ __launch_bounds__(64 * kSkinnyWaves) void k_nvfp4_linear_skinny(GemmArgs a) {
+    __shared__ float red[kSkinnyWaves][MT * 32 * 32];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int r32 = lane & 31, h = lane >> 5;
+    const int64_t n0 = (int64_t)blockIdx.x * 32;
+    const int64_t nsteps = (a.K + kBK - 1) / kBK;
+
+    f32x16 acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = (f32x16){};
+
+    auto load = [&](int64_t s, LaneChunk& w, LaneChunk (&x)[MT]) {
+        const int64_t k0 = (s < nsteps ? s : nsteps - 1) * kBK;
+        w = load_lane<FAST>(a.wc, a.ws, n0 + r32, a.N, a.K, k0, h);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) x[t] = load_lane<FAST>(a.xc, a.xs, 32 * t + r32, a.M, a.K, k0, h);
+    };
+    auto compute = [&](const LaneChunk& w, const LaneChunk (&x)[MT]) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const ScaleParts sw = split_scale((w.s >> (8 * half)) & 0xFFu);
+            ScaleParts sx[MT];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) sx[t] = split_scale((x[t].s >> (8 * half)) & 0xFFu);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int kk = 2 * half + q;
+                const f16x8 fb = frag_from_codes(dword_of(w.c, kk), sw);
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    const f16x8 fa = frag_from_codes(dword_of(x[t].c, kk), sx[t]);
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, fb, acc[t], 0, 0, 0);
+                }
+            }
+        }
+    };
+    // this wavefront's steps: wave + 16 i for i < my; four in flight in
+    // static slots, refilled four steps ahead in full rounds (straight-line,
+    // so the load counters are exact); the last 0-3 steps need no refill
+    if (nsteps > 0) {  // K == 0: nothing to load (and no step to clamp to)
+        const int64_t my = wave < nsteps ? (nsteps - wave + kSkinnyWaves - 1) / kSkinnyWaves : 0;
+        LaneChunk w[4], x[4][MT];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) load(wave + (int64_t)kSkinnyWaves * d, w[d], x[d]);
+        int64_t i = 0;
+        for (; i + 4 <= my; i += 4) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                compute(w[d], x[d]);
+                load(wave + (int64_t)kSkinnyWaves * (i + 4 + d), w[d], x[d]);
+            }
+        }
+        const int64_t rest = my - i;
+        if (rest > 0) compute(w[0], x[0]);
+        if (rest > 1) compute(w[1], x[1]);
+        if (rest > 2) compute(w[2], x[2]);
+    }
+
+    // partial tiles to LDS (register r of lane l: row 8*(r/4) + 4*(l/32) +
+    // r%4, column l%32), then one thread per output sums the 16 wavefronts
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+            red[wave][row * 32 + r32] = acc[t][r];
+        }
+    __syncthreads();
+    const float s2w = a.ws2[0];
+#pragma unroll
+    for (int e = tid; e < MT * 32 * 32; e += 64 * kSkinnyWaves) {
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kSkinnyWaves; ++w) v += red[w][e];
+        const int64_t row = e >> 5, col = n0 + (e & 31);
+        if (row < a.M && col < a.N) {
+            const float y = v * (a.xs2[a.xs2_per_row ? row : 0] * s2w);
+            if (BF16_OUT) {
+                const uint32_t p = bf16_pair(y, 0.0f);
+                reinterpret_cast<uint16_t*>(a.y)[row * a.N + col] = (uint16_t)(p & 0xFFFFu);
+            } else {
+                reinterpret_cast<float*>(a.y)[row * a.N + col] = y;
+            }
+        }
+    }
+}
+
 }  // namespace
 
+// Up to this many rows of X the few-token kernel is used.
+constexpr int64_t kSkinnyMaxM = 64;
+
 hipError_t launch_nvfp4_linear(const GemmArgs& a, bool fast, bool bf16_out, hipStream_t stream) {
+    if (a.M <= kSkinnyMaxM) {
+        const dim3 grid((unsigned)((a.N + 31) / 32)), block(64 * kSkinnyWaves);
+#define FOCUS_SK(F, B)                                                                                 \
+    do {                                                                                               \
+        if (a.M <= 32) hipLaunchKernelGGL((k_nvfp4_linear_skinny<F, B, 1>), grid, block, 0, stream, a); \
+        else hipLaunchKernelGGL((k_nvfp4_linear_skinny<F, B, 2>), grid, block, 0, stream, a);          \
+    } while (0)
+        if (fast) {
+            if (bf16_out) FOCUS_SK(true, true);
+            else FOCUS_SK(true, false);
+        } else {
+            if (bf16_out) FOCUS_SK(false, true);
+            else FOCUS_SK(false, false);
+        }
+#undef FOCUS_SK
+        return hipGetLastError();
+    }
     const int64_t tiles_m = (a.M + kBM - 1) / kBM, tiles_n = (a.N + kBN - 1) / kBN;
     const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kGemmThreads);
     if (fast) {

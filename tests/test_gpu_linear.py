@@ -91,8 +91,10 @@ def test_exact_when_partial_sums_are_exact(focus, orc):
     assert np.array_equal(y16, want)
 
 
-SHAPES = [(1, 1, 16), (7, 33, 48), (255, 257, 64), (257, 255, 1040), (300, 520, 4096), (64, 512, 8192),
-          (513, 96, 80)]
+# M <= 64 takes the few-token kernel (one or two 32-row tiles of X), larger M
+# the tiled kernel; K % 64 != 0 takes the masked loads.
+SHAPES = [(1, 1, 16), (7, 33, 48), (16, 200, 1040), (16, 4096, 4096), (17, 64, 64), (32, 4096, 4096), (33, 1000, 1040), (64, 512, 8192), (64, 300, 14336),
+          (65, 130, 192), (255, 257, 64), (257, 255, 1040), (300, 520, 4096), (513, 96, 80)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES, ids=lambda v: str(v))
@@ -147,3 +149,22 @@ def test_linear_full_size_sampled(focus, orc, N, K):
                                 wc[ci].cpu().numpy(), ws[ci].cpu().numpy(), np.float32(2.0e-4))
     got = y[torch.from_numpy(ri).to(DEV)][:, torch.from_numpy(ci).to(DEV)].float().cpu().numpy().astype(np.float64)
     check_bound(got, ref, refabs, K, True, f"8192 x {N} x {K}")
+
+
+@pytest.mark.parametrize("M", [1, 16, 64])
+@pytest.mark.parametrize("N,K", sorted(set(synth.LLAMA_8B.layer_shapes())), ids=lambda v: str(v))
+def test_linear_few_tokens_full_size(focus, orc, M, N, K):
+    """Decode-sized activations through every 8B linear shape at full size;
+    all rows, sampled columns against the oracle."""
+    xc, xs = synth.nvfp4_operand(M, K, seed=9, tensor_id=45, device=DEV)
+    wc, ws = synth.nvfp4_operand(N, K, seed=9, tensor_id=46, device=DEV)
+    s2x = torch.rand(M, generator=synth.generator(9, 47, DEV), device=DEV) * 1e-3 + 1e-4
+    s2w = torch.tensor([3.0e-4], device=DEV)
+    y = focus.nvfp4_linear(focus.Quantized(xc, xs, None, s2x), focus.Quantized(wc, ws, None, s2w),
+                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ci = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(N + K + M).integers(0, N, 94)]))
+    ref, refabs = oracle_linear(orc, xc.cpu().numpy(), xs.cpu().numpy(), s2x.cpu().numpy(), wc[ci].cpu().numpy(),
+                                ws[ci].cpu().numpy(), np.float32(3.0e-4))
+    got = y[:, torch.from_numpy(ci).to(DEV)].cpu().numpy().astype(np.float64)
+    check_bound(got, ref, refabs, K, False, f"{M} x {N} x {K}")
