@@ -59,6 +59,7 @@ _SIGNATURES = {
     "oracle_mx_dequantize": (None, [_u8p, _u8p, _i64, _i64, _u16p]),
     "oracle_fo6_quantize": (None, [_u16p, _i64, _i64, _f32p, _ct.c_int, _u8p, _u8p, _u16p]),
     "oracle_fo6_quantize_act_per_token": (None, [_u16p, _i64, _i64, _u8p, _u8p, _f32p, _u16p]),
+    "oracle_mixfp4_dequantize": (None, [_u8p, _u8p, _f, _u8p, _i64, _i64, _i64, _i64, _u16p]),
     "oracle_nvfp4_linear": (None, [_u8p, _u8p, _f32p, _ct.c_int, _i64, _u8p, _u8p, _f32p, _i64, _i64,
                                    _f64p, _f64p]),
 }
@@ -306,6 +307,18 @@ class Oracle:
                                         tile_rows, tile_cols, _ptr(codes, _u8p), _ptr(scales, _u8p),
                                         _ptr(wdeq, _u16p))
         return codes, scales, wdeq
+
+    def mixfp4_dequantize(self, codes, scales, s2, tile_map, tile_rows, tile_cols=64):
+        """Stored MixFP4 [rows, cols] -> BF16 bits (E0M3 or E2M1 per tile)."""
+        codes, scales = _as(codes, _np.uint8), _as(scales, _np.uint8)
+        rows, cols = codes.shape[0], 2 * codes.shape[1]
+        assert scales.shape == (rows, cols // 16) and rows % tile_rows == 0 and cols % tile_cols == 0
+        tile_map = _as(_np.asarray(tile_map).astype(_np.uint8), _np.uint8)
+        assert tile_map.shape == (rows // tile_rows, cols // tile_cols)
+        out = _np.empty((rows, cols), _np.uint16)
+        self.lib.oracle_mixfp4_dequantize(_ptr(codes, _u8p), _ptr(scales, _u8p), float(s2), _ptr(tile_map, _u8p),
+                                          rows, cols, tile_rows, tile_cols, _ptr(out, _u16p))
+        return out
 
     def nvfp4_linear(self, x_codes, x_scales, x_s2, w_codes, w_scales, w_s2):
         """Y = X' W'^T of NVFP4 activations X [M, K] (s2 per token, or one

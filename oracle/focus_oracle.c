@@ -637,3 +637,25 @@ void oracle_nvfp4_linear(const uint8_t* xc, const uint8_t* xs, const float* xs2,
         }
     }
 }
+
+/* Dequantize stored MixFP4 ("Llama-3.1-8B-Instruct FlipQuant MixFP4 maps",
+ * section "What this is"): the tile's map entry says how the block's codes
+ * read (E0M3 level or E2M1 value); w' = BF16((c*S)*s2) as in the quantizer. */
+void oracle_mixfp4_dequantize(const uint8_t* codes, const uint8_t* scales, float s2, const uint8_t* map,
+                              int64_t rows, int64_t cols, int64_t tile_rows, int64_t tile_cols,
+                              uint16_t* out)
+{
+    int64_t nb = cols / 16, tiles_per_row = cols / tile_cols;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < nb; ++b) {
+            int e0m3 = map[(r / tile_rows) * tiles_per_row + (b * 16) / tile_cols] != 0;
+            float S = oracle_e4m3_value(scales[r * nb + b]);
+            for (int i = 0; i < 16; ++i) {
+                uint8_t byte = codes[r * (cols / 2) + b * 8 + i / 2];
+                unsigned c = (i & 1) ? (byte >> 4) : (byte & 15u);
+                float cv = e0m3 ? oracle_e0m3_value(c) : oracle_e2m1_value(c);
+                out[r * cols + b * 16 + i] = oracle_bf16_round((cv * S) * s2);
+            }
+        }
+    }
+}

@@ -788,6 +788,26 @@ def check_mixfp4_maps(o):
     assert np.array_equal(mx[2], np.where(sel_el, e[2], f[2]))
 
 
+def check_mixfp4_dequantize(o):
+    """Dequantizing stored MixFP4 gives the quantizer's fused w' bit for bit
+    (random data, a mixed map), and hand-written E0M3 codes read as levels:
+    codes 0x7 / 0xF / 0x8 with scale 1 and s2 = 2^-10 are +7, -7, -0 times
+    2^-10, the same bytes in an E2M1 tile +6, -6, -0."""
+    w, _, _ = _random_case(97, rows=32, cols=384)
+    s2, _ = o.tensor_scale(w)
+    tmap = np.array([[1, 0, 1, 0, 0, 1], [0, 1, 1, 0, 1, 0], [1, 1, 0, 0, 0, 1], [0, 0, 0, 1, 1, 1]], np.uint8)
+    c, sc, wd = o.mixfp4_quantize(w, s2, tmap, 8, 64)
+    assert np.array_equal(o.mixfp4_dequantize(c, sc, s2, tmap, 8, 64), wd)
+    codes = np.zeros((1, 8), np.uint8)
+    codes[0, 0] = 0xF7          # elements 0, 1: codes 0x7, 0xF
+    codes[0, 1] = 0x08          # element 2: code 0x8
+    scales = np.full((1, 1), 0x38, np.uint8)
+    for e0, big in ((1, 7.0), (0, 6.0)):
+        d = bf16_float(o.mixfp4_dequantize(codes, scales, S2_POW2, np.array([[e0]], np.uint8), 1, 16))
+        assert d[0, 0] == big * 2.0 ** -10 and d[0, 1] == -big * 2.0 ** -10
+        assert d[0, 2] == 0.0 and np.signbit(d[0, 2]) and not np.signbit(d[0, 3])
+
+
 # ---------------------------------------------------------------------------
 # the NVFP4 linear layer Y = X' W'^T
 # ---------------------------------------------------------------------------
@@ -853,6 +873,6 @@ ALL_CHECKS = [
     check_fo6_four_fixed_points, check_fo6_six_fixed_points, check_fo6_ties_keep_six,
     check_fo6_never_worse_than_rtn, check_mx_scale_closed_forms, check_mx_fixed_points,
     check_mx_factor_and_subblocks, check_mx_plain_reduction, check_e0m3_levels, check_mixfp4_maps,
-    check_linear_closed_forms, check_linear_fixed_points,
+    check_linear_closed_forms, check_linear_fixed_points, check_mixfp4_dequantize,
     check_fo6_zero_and_act,
 ]

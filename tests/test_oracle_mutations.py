@@ -67,6 +67,11 @@ MUTATIONS = [
      "map[((b * 16) / tile_cols) * (rows / tile_rows) + r / tile_rows]"),
     ("MixFP4 map ignored", "int e0m3 = map[(r / tile_rows) * tiles_per_row + (b * 16) / tile_cols] != 0;",
      "int e0m3 = 0;"),
+    ("MixFP4 dequantize reads every tile as E2M1",
+     "float cv = e0m3 ? oracle_e0m3_value(c) : oracle_e2m1_value(c);\n                out[r * cols + b * 16 + i]",
+     "float cv = oracle_e2m1_value(c);\n                out[r * cols + b * 16 + i]"),
+    ("MixFP4 dequantize nibbles swapped", "unsigned c = (i & 1) ? (byte >> 4) : (byte & 15u);\n                float cv = e0m3",
+     "unsigned c = (i & 1) ? (byte & 15u) : (byte >> 4);\n                float cv = e0m3"),
     ("linear drops the block scale",
      "return (double)oracle_e2m1_value(c) * (double)oracle_e4m3_value(scales[row * (K / 16) + k / 16]);",
      "return (double)oracle_e2m1_value(c);"),
