@@ -275,6 +275,11 @@ def main():
         ACT6 = focus.quantize_act_per_token_fo6(X)
         t_a6 = time_calls(lambda: focus.quantize_act_per_token_fo6(X, out=ACT6), reps=20)
         t_mix = {t: time_calls(lambda t=t: [b.run() for b in MIXB[t]]) for t in MIX_TILES}
+        # per-token activations on a tensor too large for any cache (1 GiB)
+        XL = synth.make_activations((131072, 4096), device=dev)
+        ACTL = focus.quantize_act_per_token(XL)
+        t_al = time_calls(lambda: focus.quantize_act_per_token(XL, out=ACTL), reps=10)
+        del XL, ACTL
     torch.cuda.synchronize()
 
     def row(ms, nbytes, units):
@@ -298,6 +303,8 @@ def main():
             "FourOverSix act per token [8192,4096] (after the steps, cache-resident)":
                 row(t_a6, B_ACT * X.numel() + 4 * X.shape[0], X.numel()),
         })
+        rows["act per token [131072,4096] (after the steps)"] = row(t_al, B_ACT * 131072 * 4096 + 4 * 131072,
+                                                                     131072 * 4096)
         for (th, tw) in MIX_TILES:
             share = synth.MIXFP4_FRAC[(th, tw)]
             rows[f"FlipQuant MixFP4 {th}x{tw} map ({100 * share:.2f}% E0M3 tiles) + w' (after the steps)"] = \

@@ -35,7 +35,7 @@ from ._lib import FocusError, FocusLibraryMissing, library_path  # noqa: F401
 
 __all__ = ["tensor_scale", "quantize", "dequantize", "quantize_act_per_token", "Quantized",
            "quantize_fo6", "quantize_act_per_token_fo6", "quantize_fo6_many",
-           "quantize_mixfp4", "quantize_mixfp4_many", "nvfp4_linear",
+           "quantize_mixfp4", "quantize_mixfp4_many", "dequantize_mixfp4", "nvfp4_linear",
            "quantize_mx", "quantize_mx_many", "dequantize_mx",
            "tensor_scale_many", "quantize_many", "dequantize_many", "Batch",
            "FocusError", "FocusLibraryMissing", "abi_version", "library_path"]
@@ -368,6 +368,27 @@ def quantize_mixfp4_many(ws, maps, tiles, s2s, outs=None, dequant: bool = True, 
     b = Batch("focus_quantize_mixfp4_many", arr, (list(ws), list(maps), list(s2s), res), dev)
     b.outs = res
     return b.run() if run else b
+
+
+def dequantize_mixfp4(codes: torch.Tensor, scales: torch.Tensor, s2: torch.Tensor, tile_map: torch.Tensor,
+                      tile_rows: int, tile_cols: int = 64, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Stored MixFP4 codes [rows, cols/2] and scales [rows, cols/16] -> BF16
+    [rows, cols]; tile_map as for ``quantize_mixfp4``."""
+    dev = codes.device
+    _check_dev("codes", codes, torch.uint8, dev)
+    _check_dev("scales", scales, torch.uint8, dev)
+    _check_dev("s2", s2, torch.float32, dev)
+    _check_dev("tile_map", tile_map, torch.uint8, dev)
+    rows, cols = codes.shape[0], 2 * codes.shape[1]
+    if tuple(scales.shape) != (rows, cols // 16) or not (codes.is_contiguous() and scales.is_contiguous()):
+        raise ValueError("codes [rows, cols/2] and scales [rows, cols/16] must be contiguous")
+    if tuple(tile_map.shape) != (rows // max(tile_rows, 1), cols // max(tile_cols, 1)) or not tile_map.is_contiguous():
+        raise ValueError("tile_map must be a contiguous [rows/tile_rows, cols/tile_cols] uint8 tensor")
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    _lib.check(_lib.lib().focus_dequantize_mixfp4(_p(codes), _p(scales), _p(s2), _p(tile_map), rows, cols, tile_rows,
+                                                  tile_cols, _p(out), _stream(codes)))
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -390,6 +390,36 @@ int focus_quantize_mixfp4_many(const focus_mixfp4_desc* descs, int n, void* stre
     return run_quantize_mix(descs, n, (hipStream_t)stream);
 }
 
+int focus_dequantize_mixfp4(const uint8_t* codes, const uint8_t* scales, const float* s2,
+                            const uint8_t* map, int64_t rows, int64_t cols, int64_t tile_rows,
+                            int64_t tile_cols, uint16_t* out, void* stream) {
+    int st = shape_2d(rows, cols);
+    if (st != FOCUS_OK) return st;
+    if (tile_rows < 1 || tile_cols < 16 || tile_cols % 16 != 0) return FOCUS_ERR_SHAPE;
+    if (rows % tile_rows != 0 || cols % tile_cols != 0) return FOCUS_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return FOCUS_OK;
+    if (rows * (cols / 16) >= kMaxMixBlocks) return FOCUS_ERR_RANGE;
+    if (!codes || !scales || !s2 || !map || !out) return FOCUS_ERR_NULL;
+    if (!aligned(codes, 8) || !aligned(s2, 4) || !aligned(out, 16)) return FOCUS_ERR_ALIGN;
+    focus::MixDequantBatch bt;
+    bt.n = 1;
+    bt.codes[0] = reinterpret_cast<const uint2*>(codes);
+    bt.scales[0] = scales;
+    bt.s2[0] = s2;
+    bt.out[0] = reinterpret_cast<uint4*>(out);
+    bt.nb_row[0] = cols / 16;
+    bt.nblk[0] = rows * (cols / 16);
+    bt.per_row[0] = 0;
+    bt.map[0] = map;
+    bt.tiles_per_row[0] = (uint32_t)(cols / tile_cols);
+    uint32_t s0, s1, sh2;
+    div_magic_host((uint32_t)(cols / 16), bt.mul[0][0], s0);
+    div_magic_host((uint32_t)tile_rows, bt.mul[0][1], s1);
+    div_magic_host((uint32_t)(tile_cols / 16), bt.mul[0][2], sh2);
+    bt.sh[0] = s0 | (s1 << 8) | (sh2 << 16);
+    return hip_status(focus::launch_dequantize_mix(bt, (hipStream_t)stream));
+}
+
 int focus_nvfp4_linear(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_s2,
                        int x_s2_per_row, int64_t M, const uint8_t* w_codes, const uint8_t* w_scales,
                        const float* w_s2, int64_t N, int64_t K, void* y, int y_dtype, void* stream) {

@@ -57,12 +57,22 @@ struct ScaleBatch {
     int n;
 };
 
+// MixFP4 dequantize: a DequantBatch plus the tile map and its divisors, as in
+// MixBatch (nb_row of the base batch is the first divisor).
+struct MixDequantBatch : DequantBatch {
+    const uint8_t* map[kBatch];
+    uint32_t tiles_per_row[kBatch];
+    uint32_t mul[kBatch][3];
+    uint32_t sh[kBatch];
+};
+
 // key: bit 2 = m present, bit 1 = q present, bit 0 = w' written; 8 / 9 =
 // FourOverSix without / with w' (m and q absent); 16 + (m, q, w' bits) =
 // FOCUS on MXFP4; every tensor of one batch shares the key.
 hipError_t launch_quantize(QuantBatch& bt, int key, hipStream_t stream);
 hipError_t launch_quantize_mix(MixBatch& bt, bool deq, hipStream_t stream);
 hipError_t launch_dequantize(DequantBatch& bt, bool mx, hipStream_t stream);
+hipError_t launch_dequantize_mix(MixDequantBatch& bt, hipStream_t stream);
 hipError_t launch_tensor_scale(ScaleBatch& bt, hipStream_t stream);
 hipError_t launch_act_per_token(const uint16_t* x, int64_t tokens, int64_t hidden, uint8_t* codes,
                                 uint8_t* scales, float* s2_out, uint16_t* xdeq, bool fo6,

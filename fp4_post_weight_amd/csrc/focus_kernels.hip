@@ -328,6 +328,19 @@ __device__ __forceinline__ int find_tensor(const int64_t* tile_start, int n, int
 constexpr int kQuantU = 2;
 constexpr int64_t kQuantTile = (int64_t)kThreads * kQuantU;
 
+// FlipQuant MixFP4: is block `blk` of tensor j in an E0M3 tile?  block ->
+// (row, block in row) -> (tile row, tile column) with the batch's div_magic
+// multipliers; every index is below 2^31 (checked on the host).
+template <typename Batch>
+__device__ __forceinline__ bool mix_block_is_e0m3(const Batch& bt, int j, int64_t blk, uint32_t nb_row) {
+    const uint32_t ub = (uint32_t)blk, sh = bt.sh[j];
+    const uint32_t r = div_magic(ub, bt.mul[j][0], sh & 255u);
+    const uint32_t b = ub - r * nb_row;
+    const uint32_t tr = div_magic(r, bt.mul[j][1], (sh >> 8) & 255u);
+    const uint32_t tc = div_magic(b, bt.mul[j][2], sh >> 16);
+    return bt.map[j][tr * bt.tiles_per_row[j] + tc] != 0;
+}
+
 // MODE 0: FOCUS NVFP4; 1: FourOverSix (m, q absent); 2: FOCUS on MXFP4 (lanes
 // 2j and 2j+1 share one 32-block: m[blk/2], scale byte stored by the even
 // lane, no tensor scale); 3: FlipQuant MixFP4 (Batch = MixBatch; each block
@@ -373,16 +386,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize(Batch bt, int64_t ntiles)
             if (blk < nblk) {
                 mb[k] = HAS_M ? ld4f(m, MX ? blk >> 1 : blk) : 1.0f;
                 qq[k] = HAS_Q ? ld8f(q, blk) : make_float2(0.0f, 0.0f);
-                if constexpr (MIX) {
-                    // block -> (row, block in row) -> (tile row, tile column);
-                    // every index is below 2^31 (checked on the host)
-                    const uint32_t ub = (uint32_t)blk, sh = bt.sh[j];
-                    const uint32_t r = div_magic(ub, bt.mul[j][0], sh & 255u);
-                    const uint32_t b = ub - r * bt.nb_row[j];
-                    const uint32_t tr = div_magic(r, bt.mul[j][1], (sh >> 8) & 255u);
-                    const uint32_t tc = div_magic(b, bt.mul[j][2], sh >> 16);
-                    e0[k] = bt.map[j][tr * bt.tiles_per_row[j] + tc] != 0;
-                }
+                if constexpr (MIX) e0[k] = mix_block_is_e0m3(bt, j, blk, bt.nb_row[j]);
             }
         }
 #pragma unroll
@@ -424,9 +428,12 @@ __global__ __launch_bounds__(kThreads) void k_quantize(Batch bt, int64_t ntiles)
 
 constexpr int64_t kDeqTile = (int64_t)kThreads * 2;
 
-// MX: E8M0 scale byte per 32 elements (per pair of 16-element blocks), no s2.
-template <bool MX>
-__global__ __launch_bounds__(kThreads) void k_dequantize(DequantBatch bt, int64_t ntiles) {
+// MODE 0: NVFP4; 1: MXFP4 (E8M0 scale byte per 32 elements, i.e. per pair of
+// 16-element blocks, no s2); 2: FlipQuant MixFP4 (Batch = MixDequantBatch;
+// blocks of E0M3 tiles decode their codes as levels 0..7).
+template <int MODE, typename Batch = DequantBatch>
+__global__ __launch_bounds__(kThreads) void k_dequantize(Batch bt, int64_t ntiles) {
+    constexpr bool MX = MODE == 1, MIX = MODE == 2;
     __shared__ uint4 xch[kThreads / 64][128];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -468,8 +475,15 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(DequantBatch bt, int64_
             uint4 d0 = make_uint4(0, 0, 0, 0), d1 = d0;
             if (blk < nblk) {
                 const float S = MX ? e8m0_value(sb[k]) : e4m3_any_value(sb[k]);
-                d0 = dequant8(c[k].x, S, s2v[k]);
-                d1 = dequant8(c[k].y, S, s2v[k]);
+                bool e0 = false;
+                if constexpr (MIX) e0 = mix_block_is_e0m3(bt, j, blk, (uint32_t)nb_row);
+                if (e0) {
+                    d0 = dequant8_e0m3(c[k].x, S, s2v[k]);
+                    d1 = dequant8_e0m3(c[k].y, S, s2v[k]);
+                } else {
+                    d0 = dequant8(c[k].x, S, s2v[k]);
+                    d1 = dequant8(c[k].y, S, s2v[k]);
+                }
             }
             if (first < nblk) wave_store_blocks(bt.out[j] + 2 * first, d0, d1, xch[wave], lane, nblk - first);
         }
@@ -745,9 +759,21 @@ hipError_t launch_dequantize(DequantBatch& bt, bool mx, hipStream_t stream) {
     }
     bt.tile_start[bt.n] = t;
     if (mx)
-        hipLaunchKernelGGL(k_dequantize<true>, dim3(grid_for_tiles(t)), dim3(kThreads), 0, stream, bt, t);
+        hipLaunchKernelGGL(k_dequantize<1>, dim3(grid_for_tiles(t)), dim3(kThreads), 0, stream, bt, t);
     else
-        hipLaunchKernelGGL(k_dequantize<false>, dim3(grid_for_tiles(t)), dim3(kThreads), 0, stream, bt, t);
+        hipLaunchKernelGGL(k_dequantize<0>, dim3(grid_for_tiles(t)), dim3(kThreads), 0, stream, bt, t);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize_mix(MixDequantBatch& bt, hipStream_t stream) {
+    int64_t t = 0;
+    for (int j = 0; j < bt.n; ++j) {
+        bt.tile_start[j] = t;
+        t += (bt.nblk[j] + kDeqTile - 1) / kDeqTile;
+    }
+    bt.tile_start[bt.n] = t;
+    hipLaunchKernelGGL((k_dequantize<2, MixDequantBatch>), dim3(grid_for_tiles(t)), dim3(kThreads), 0, stream,
+                       bt, t);
     return hipGetLastError();
 }
 

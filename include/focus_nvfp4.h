@@ -266,6 +266,16 @@ typedef struct focus_mixfp4_desc {
 /* Batched MixFP4, with the rules of the batched calls above. */
 int focus_quantize_mixfp4_many(const focus_mixfp4_desc* descs, int n, void* stream);
 
+/* Dequantize stored MixFP4 (same page and readings): out = BF16((c*S)*s2)
+ * with c the E0M3 level of a code in a tile whose map entry is nonzero and
+ * its E2M1 value otherwise.  codes [rows, cols/2] (8-byte aligned), scales
+ * [rows, cols/16], s2 one float, map and tiles as focus_quantize_mixfp4,
+ * out [rows, cols] BF16 (16-byte aligned); the shape and range rules of
+ * focus_quantize_mixfp4. */
+int focus_dequantize_mixfp4(const uint8_t* codes, const uint8_t* scales, const float* s2,
+                            const uint8_t* map, int64_t rows, int64_t cols, int64_t tile_rows,
+                            int64_t tile_cols, uint16_t* out, void* stream);
+
 /*
  * The NVFP4 linear layer, the consumer of the stored format ("FOCUS NVFP4
  * scales for Llama-3.2-1B-Instruct (our reproduction)": section "What this

@@ -228,3 +228,14 @@ def test_linear_validation(lib):
     assert f(FAKE, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE + 1, 8, 64, FAKE, 0, None) == ERR_ALIGN
     assert f(None, None, None, 1, 0, None, None, None, 8, 64, None, 0, None) == OK    # empty
     assert f(None, None, None, 1, 4, None, None, None, 0, 64, None, 1, None) == OK
+
+
+def test_mixfp4_dequantize_validation(lib):
+    d = lib.focus_dequantize_mixfp4
+    #        codes scales s2  map   rows cols th  tw  out   stream
+    assert d(FAKE, FAKE, FAKE, FAKE, 16, 128, 8, 48, FAKE, None) == ERR_SHAPE
+    assert d(FAKE, FAKE, FAKE, FAKE, 12, 128, 8, 64, FAKE, None) == ERR_SHAPE
+    assert d(FAKE, FAKE, FAKE, None, 16, 128, 8, 64, FAKE, None) == ERR_NULL
+    assert d(FAKE, FAKE, FAKE, FAKE, 16, 128, 8, 64, FAKE + 8, None) == ERR_ALIGN
+    assert d(FAKE, FAKE, FAKE, FAKE, 1 << 24, 2048, 8, 64, FAKE, None) == ERR_RANGE
+    assert d(None, None, None, None, 0, 128, 8, 64, None, None) == OK

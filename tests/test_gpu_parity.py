@@ -740,3 +740,28 @@ def test_mixfp4_many_matches_single(focus, orc):
                                        tiles[i][0], tiles[i][1])
         assert np.array_equal(single.codes.cpu().numpy(), c) and np.array_equal(single.scales.cpu().numpy(), sc)
         assert np.array_equal(np_bits(single.deq), d)
+
+
+@pytest.mark.parametrize("shape,tile", MIX_CASES[:6], ids=lambda v: f"{v[0]}x{v[1]}")
+def test_mixfp4_dequantize(focus, orc, shape, tile):
+    """Stored MixFP4 back to BF16 against the oracle, and equal to the fused
+    w' of the quantizer (the same map)."""
+    rows, cols = shape
+    w = synth.weights(shape, seed=rows + 5 * cols, tensor_id=26, zero_block_p=0.02)
+    wb = np_bits(w)
+    tmap = synth.tile_map(rows, cols, tile, frac=0.4, seed=rows, tensor_id=27).numpy()
+    md = torch.from_numpy(tmap).to(DEV)
+    res = focus.quantize_mixfp4(w.to(DEV), md, tile[0], tile[1], dequant=True)
+    deq = focus.dequantize_mixfp4(res.codes, res.scales, res.s2, md, tile[0], tile[1])
+    torch.cuda.synchronize()
+    assert torch.equal(deq.view(torch.int16), res.deq.view(torch.int16))
+    # the oracle on random stored bytes (every code and scale byte, both formats)
+    rng = np.random.default_rng(rows)
+    codes = rng.integers(0, 256, (rows, cols // 2)).astype(np.uint8)
+    scales = rng.integers(0, 256, (rows, cols // 16)).astype(np.uint8)
+    scales[(scales & 0x7F) == 0x7F] = 0x38  # no NaN scale bytes (NaN payloads are not compared)
+    s2 = np.float32(3.0e-3)
+    got = focus.dequantize_mixfp4(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                                  torch.tensor([s2], device=DEV), md, tile[0], tile[1])
+    torch.cuda.synchronize()
+    assert np.array_equal(np_bits(got), orc.mixfp4_dequantize(codes, scales, s2, tmap, tile[0], tile[1]))
