@@ -61,8 +61,8 @@ def parse():
                          "70b: Llama-3.1-70B-shaped, processed layer by layer with w' and the "
                          "dequantized copy written to one reused per-layer buffer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows-fraction", type=float, default=None,
-                    help="fraction of the rows of layer 0 the CPU oracle quantizes")
+    ap.add_argument("--cpu-weights", type=float, default=1.6e9,
+                    help="weights of the set (in linear order) the CPU oracle quantizes")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="before the steps, copy a buffer of BYTES bytes three times (a plain copy "
                          "kernel of known traffic, to scale hardware byte counters)")
@@ -114,8 +114,6 @@ def main():
     torch.cuda.set_device(dev)
     ws = {"8b": synth.LLAMA_8B, "1b": synth.LLAMA_1B, "70b": synth.LLAMA_70B}[args.workload]
     layered = args.workload == "70b"
-    if args.cpu_rows_fraction is None:
-        args.cpu_rows_fraction = 0.05 if layered else 0.5
     lins = ws.linears()
     n_weights = sum(l.numel for l in lins)
 
@@ -316,7 +314,7 @@ def main():
     # ---- CPU baseline: the oracle on a bounded sample ----------------------
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(lins, W, M, Q, X, args.cpu_rows_fraction)
+        cpu = cpu_baseline(lins, W, M, Q, X, args.cpu_weights)
 
     line = {
         "metric": METRIC if args.workload == "8b" else METRIC.replace("8B set", f"{args.workload.upper()} set"),
@@ -404,11 +402,12 @@ def linear_rows(focus, synth, ws, dev, stream):
     return out
 
 
-def cpu_baseline(lins, W, M, Q, X, frac):
-    """The oracle, unchanged, on layer 0 of the set: s2 of each full tensor,
-    then quantize (+ w') and dequantize of the first `frac` of its rows, and
-    per-token activations of the first 512 tokens; row chunks run on the
-    host's cores through ctypes (which releases the GIL)."""
+def cpu_baseline(lins, W, M, Q, X, budget):
+    """The oracle, unchanged, on the first `budget` weights of the set in
+    linear order (whole tensors, the last one cut by rows): s2 of each full
+    tensor, then quantize (+ w') and dequantize, and per-token activations of
+    the first 512 tokens; row chunks run on the host's cores through ctypes
+    (which releases the GIL)."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
@@ -422,12 +421,14 @@ def cpu_baseline(lins, W, M, Q, X, frac):
     except AttributeError:
         n_thr = os.cpu_count() or 1
     n_thr = max(1, min(n_thr, 64))
-    layer0 = [i for i, l in enumerate(lins) if l.layer == 0]
-    host = []
-    for i in layer0:
+    host, left = [], int(budget)
+    for i, lin in enumerate(lins):
+        if left <= 0:
+            break
         wb = synth.bits(W[i])
-        r = max(1, int(lins[i].rows * frac))
+        r = max(1, min(lin.rows, left // lin.cols))
         host.append((wb, M[i][:r].cpu().numpy(), Q[i][:r].cpu().numpy(), r))
+        left -= r * lin.cols
     xb = synth.bits(X[:512])
     weights = 0
     t0 = time.perf_counter()
@@ -450,9 +451,9 @@ def cpu_baseline(lins, W, M, Q, X, frac):
     dt = time.perf_counter() - t0
     return {"value": round(weights / dt / 1e9, 5), "unit": "Gweights/s", "cores": n_thr,
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"layer 0 of the set: full-tensor s2, then quantize (+w') and dequantize of the "
-                      f"first {frac:g} of the rows of its 7 linears ({weights} weights), and per-token "
-                      f"activations of 512 x 4096"}
+            "sample": f"the first {weights} weights of the set in linear order ({len(host)} linears, the "
+                      f"last cut by rows): full-tensor s2, then quantize (+w') and dequantize, and "
+                      f"per-token activations of 512 x 4096"}
 
 
 if __name__ == "__main__":
