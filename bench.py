@@ -308,6 +308,13 @@ def main():
             rows[f"FlipQuant MixFP4 {th}x{tw} map ({100 * share:.2f}% E0M3 tiles) + w' (after the steps)"] = \
                 row(t_mix[(th, tw)], (B_ACT + 2.0 + 1.0 / (th * tw)) * n_weights, n_weights)
 
+    # streaming ceiling on this GPU: a plain device copy of 2 GiB (read + write)
+    csrc = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    t_cp = time_calls(lambda: cdst.copy_(csrc), reps=5)
+    del csrc, cdst
+    copy_gbs = 2.0 * (1 << 31) / (t_cp * 1e-3) / 1e9
+    rows["device copy 2 GiB (streaming ceiling, after the steps)"] = row(t_cp, 2.0 * (1 << 31), 1 << 31)
     if extra_rows:
         rows.update(linear_rows(focus, synth, ws, dev, stream))
 
@@ -350,6 +357,8 @@ def main():
             "mean_launch_ms": round(mean_launch_ms, 5),
             "launches": len(q_launch_ms),
             "launches_per_step": nq,
+            "copy_ceiling_GB_s": round(copy_gbs, 1),
+            "frac_of_copy_ceiling": round(achieved / copy_gbs, 4),
         },
         "cpu_baseline": cpu,
         "rows": rows,
@@ -449,7 +458,22 @@ def cpu_baseline(lins, W, M, Q, X, budget):
         tb = np.linspace(0, xb.shape[0], n_thr + 1).astype(int)
         list(ex.map(lambda k: o.quantize_act_per_token(xb[tb[k]:tb[k + 1]]), range(n_thr)))
     dt = time.perf_counter() - t0
+    # one core: the first 32 M weights of the same sample on one thread
+    wb, m, q, r = host[0]
+    r1 = max(1, min(r, (1 << 25) // wb.shape[1]))
+    s2, _ = o.tensor_scale(wb)
+    t1 = time.perf_counter()
+    codes, scales, _ = o.quantize(wb[:r1], m[:r1], q[:r1], s2, True)
+    o.dequantize(codes, scales, s2)
+    per_core = r1 * wb.shape[1] / (time.perf_counter() - t1) / 1e9
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+    except OSError:
+        pass
     return {"value": round(weights / dt / 1e9, 5), "unit": "Gweights/s", "cores": n_thr,
+            "per_core_value": round(per_core, 5), "cpu_model": model,
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"the first {weights} weights of the set in linear order ({len(host)} linears, the "
                       f"last cut by rows): full-tensor s2, then quantize (+w') and dequantize, and "
