@@ -19,6 +19,11 @@ Calls (same names as the C ABI, without the ``focus_`` prefix):
   calls (one launch per run of up to 32 tensors).  Each returns a ``Batch``
   whose descriptor array is built once; calling it again re-launches the same
   work on the current stream without rebuilding anything.
+* FourOverSix: ``quantize_fo6``, ``quantize_fo6_many``,
+  ``quantize_act_per_token_fo6``; FOCUS on MXFP4: ``quantize_mx``,
+  ``quantize_mx_many``, ``dequantize_mx``; FlipQuant MixFP4:
+  ``quantize_mixfp4``, ``quantize_mixfp4_many``, ``dequantize_mixfp4``; the
+  NVFP4 linear layer: ``nvfp4_linear``; ``abi_version``, ``status_string``.
 
 BF16 inputs are ``torch.bfloat16`` tensors; codes and scales are ``uint8``
 ([rows, cols/2] with element 2j in the low nibble, and [rows, cols/16] E4M3
@@ -38,7 +43,7 @@ __all__ = ["tensor_scale", "quantize", "dequantize", "quantize_act_per_token", "
            "quantize_mixfp4", "quantize_mixfp4_many", "dequantize_mixfp4", "nvfp4_linear",
            "quantize_mx", "quantize_mx_many", "dequantize_mx",
            "tensor_scale_many", "quantize_many", "dequantize_many", "Batch",
-           "FocusError", "FocusLibraryMissing", "abi_version", "library_path"]
+           "FocusError", "FocusLibraryMissing", "abi_version", "status_string", "library_path"]
 
 
 class Quantized(NamedTuple):
@@ -46,6 +51,11 @@ class Quantized(NamedTuple):
     scales: torch.Tensor
     deq: Optional[torch.Tensor]
     s2: torch.Tensor
+
+
+def status_string(status: int) -> str:
+    """The library's description of a status code."""
+    return _lib.lib().focus_status_string(int(status)).decode()
 
 
 def abi_version() -> int:

@@ -239,3 +239,12 @@ def test_mixfp4_dequantize_validation(lib):
     assert d(FAKE, FAKE, FAKE, FAKE, 16, 128, 8, 64, FAKE + 8, None) == ERR_ALIGN
     assert d(FAKE, FAKE, FAKE, FAKE, 1 << 24, 2048, 8, 64, FAKE, None) == ERR_RANGE
     assert d(None, None, None, None, 0, 128, 8, 64, None, None) == OK
+
+
+def test_binding_has_every_call():
+    """The Python binding exposes every C call under the same name without
+    the focus_ prefix."""
+    import fp4_post_weight_amd as focus
+    for name in _lib.EXPORTED:
+        assert hasattr(focus, name[len("focus_"):]), name
+    assert focus.status_string(0) == "ok"
