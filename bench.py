@@ -74,11 +74,19 @@ QUANT_KERNEL_SOURCES = ("focus_internal.h", "focus_kernels.hip", "focus_numerics
 
 
 def kernel_source_hash() -> str:
+    """Hash of the quantize kernel's code: its sources with comments and
+    whitespace removed, so only a change to the code itself invalidates a
+    stored measurement."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp4_post_weight_amd", "csrc")
     for name in QUANT_KERNEL_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            code = f.read()
+        code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        code = "".join(code.split())
+        h.update(name.encode() + b"\0" + code.encode())
     return h.hexdigest()[:16]
 
 

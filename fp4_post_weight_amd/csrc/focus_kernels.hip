@@ -46,6 +46,15 @@
 //  * E4M3 rounding of t in [2^-6, 448] is integer RNE on the binary32 bits
 //    (normal range only, so no subnormal or overflow case exists).
 
+//
+// The same streaming kernels also carry the adjacent formats, selected at
+// compile time: FourOverSix (each 16-block's scale maps its maximum to 6 or 4,
+// whichever gives the lower binary32 squared error; "FOCUS NVFP4 scales ...",
+// sections "Calibration" and "Perplexity"), FOCUS on MXFP4 (32-blocks with an
+// E8M0 scale; the technical summary's section "Methodologie"), and FlipQuant
+// MixFP4 (a per-tile map choosing E0M3 levels 0..7 or FourOverSix E2M1;
+// "Llama-3.1-8B-Instruct FlipQuant MixFP4 maps", section "What this is").
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
