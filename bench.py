@@ -378,15 +378,16 @@ def main():
 
 def linear_rows(focus, synth, ws, dev, stream):
     """The NVFP4 linear layer Y = X' W'^T on each distinct layer shape of the
-    set: 8192 tokens (matrix-core bound; FLOP/s against the FP16 peak) and 16
-    tokens (bound by streaming W; operand bytes against the HBM peak).  Each
-    shape is timed over repeated calls of the C ABI with prepared arguments,
-    the operands random NVFP4 bytes."""
+    set: 8192 tokens and 2048 tokens (one evaluation window; matrix-core
+    bound, FLOP/s against the FP16 peak) and 16 tokens (bound by streaming W;
+    operand bytes against the HBM peak).  Each shape is timed over repeated
+    calls of the C ABI with prepared arguments and the split-k workspace the
+    library asks for; the operands are random NVFP4 bytes."""
     import torch
     lib = focus._lib.lib()
     out = {}
     shapes = sorted(set(ws.layer_shapes()))
-    for m_tok, reps in ((8192, 10), (16, 50)):
+    for m_tok, reps in ((8192, 10), (2048, 20), (16, 50)):
         tot_ms, tot_flop, tot_bytes = 0.0, 0.0, 0.0
         for n, k in shapes:
             xc, xs = synth.nvfp4_operand(m_tok, k, seed=3, tensor_id=60, device=dev)
@@ -394,8 +395,10 @@ def linear_rows(focus, synth, ws, dev, stream):
             s2x = torch.full((m_tok,), 1e-3, dtype=torch.float32, device=dev)
             s2w = torch.full((1,), 1e-3, dtype=torch.float32, device=dev)
             y = torch.empty((m_tok, n), dtype=torch.bfloat16, device=dev)
+            nws = int(lib.focus_nvfp4_linear_workspace_bytes(m_tok, n, k))
+            wsp = torch.empty(max(nws // 4, 1), dtype=torch.float32, device=dev)
             args = (xc.data_ptr(), xs.data_ptr(), s2x.data_ptr(), 1, m_tok, wc.data_ptr(), wsc.data_ptr(),
-                    s2w.data_ptr(), n, k, y.data_ptr(), 1, stream.cuda_stream)
+                    s2w.data_ptr(), n, k, y.data_ptr(), 1, wsp.data_ptr(), nws, stream.cuda_stream)
             for _ in range(3):
                 focus._lib.check(lib.focus_nvfp4_linear(*args))
             torch.cuda.synchronize()
@@ -409,7 +412,7 @@ def linear_rows(focus, synth, ws, dev, stream):
             tot_ms += ms
             tot_flop += 2.0 * m_tok * n * k
             tot_bytes += (m_tok + n) * k * 0.5625 + 2.0 * m_tok * n
-            del xc, xs, wc, wsc, y
+            del xc, xs, wc, wsc, y, wsp
         tflops = tot_flop / (tot_ms * 1e-3) / 1e12
         gbs = tot_bytes / (tot_ms * 1e-3) / 1e9
         key = f"NVFP4 linear Y = X' W'^T, {m_tok} tokens through the {len(shapes)} layer shapes (after the steps)"

@@ -41,6 +41,7 @@ from ._lib import FocusError, FocusLibraryMissing, library_path  # noqa: F401
 __all__ = ["tensor_scale", "quantize", "dequantize", "quantize_act_per_token", "Quantized",
            "quantize_fo6", "quantize_act_per_token_fo6", "quantize_fo6_many",
            "quantize_mixfp4", "quantize_mixfp4_many", "dequantize_mixfp4", "nvfp4_linear",
+           "nvfp4_linear_workspace_bytes",
            "quantize_mx", "quantize_mx_many", "dequantize_mx",
            "tensor_scale_many", "quantize_many", "dequantize_many", "Batch",
            "FocusError", "FocusLibraryMissing", "abi_version", "status_string", "library_path"]
@@ -405,12 +406,19 @@ def dequantize_mixfp4(codes: torch.Tensor, scales: torch.Tensor, s2: torch.Tenso
 # the NVFP4 linear layer
 # ---------------------------------------------------------------------------
 
+def nvfp4_linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace bytes for ``nvfp4_linear`` to split the sum over k (0: none)."""
+    return int(_lib.lib().focus_nvfp4_linear_workspace_bytes(M, N, K))
+
+
 def nvfp4_linear(x: Quantized, w: Quantized, out_dtype: torch.dtype = torch.bfloat16,
-                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                 out: Optional[torch.Tensor] = None, workspace="auto") -> torch.Tensor:
     """Y = X' W'^T for NVFP4 activations ``x`` (codes [M, K/2], scales
     [M, K/16], s2 [M] per token or one value) and NVFP4 weights ``w`` (codes
     [N, K/2], scales [N, K/16], one s2), on the matrix cores; Y [M, N] in
-    ``out_dtype`` (bfloat16 or float32)."""
+    ``out_dtype`` (bfloat16 or float32).  ``workspace``: "auto" allocates the
+    split-k workspace the library asks for, None uses none, or a float32
+    device tensor."""
     dev = x.codes.device
     for name, t in (("x.codes", x.codes), ("x.scales", x.scales), ("w.codes", w.codes), ("w.scales", w.scales)):
         _check_dev(name, t, torch.uint8, dev)
@@ -432,10 +440,19 @@ def nvfp4_linear(x: Quantized, w: Quantized, out_dtype: torch.dtype = torch.bflo
         _check_dev("out", out, out_dtype, dev)
         if tuple(out.shape) != (M, N) or not out.is_contiguous():
             raise ValueError("out must be a contiguous [M, N] tensor")
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a float32 tensor")
+        nbytes = nvfp4_linear_workspace_bytes(M, N, K) if M and N else 0
+        workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=dev) if nbytes else None
+    if workspace is not None:
+        _check_dev("workspace", workspace, torch.float32, dev)
     per_row = 1 if (x.s2.numel() == M and M > 1) else 0
     _lib.check(_lib.lib().focus_nvfp4_linear(_p(x.codes), _p(x.scales), _p(x.s2), per_row, M, _p(w.codes),
                                              _p(w.scales), _p(w.s2), N, K, _p(out),
-                                             0 if out_dtype == torch.float32 else 1, _stream(x.codes)))
+                                             0 if out_dtype == torch.float32 else 1, _p(workspace),
+                                             0 if workspace is None else workspace.numel() * 4,
+                                             _stream(x.codes)))
     return out
 
 

@@ -55,7 +55,9 @@ _SIGNATURES = {
     "focus_quantize_mixfp4": (_INT, [_VP, _I64, _I64, _VP, _VP, _I64, _I64, _VP, _VP, _VP, _VP]),
     "focus_quantize_mixfp4_many": (_INT, [ct.POINTER(MixDesc), _INT, _VP]),
     "focus_dequantize_mixfp4": (_INT, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _VP, _VP]),
-    "focus_nvfp4_linear": (_INT, [_VP, _VP, _VP, _INT, _I64, _VP, _VP, _VP, _I64, _I64, _VP, _INT, _VP]),
+    "focus_nvfp4_linear": (_INT, [_VP, _VP, _VP, _INT, _I64, _VP, _VP, _VP, _I64, _I64, _VP, _INT, _VP, _I64,
+                                  _VP]),
+    "focus_nvfp4_linear_workspace_bytes": (_I64, [_I64, _I64, _I64]),
 }
 
 EXPORTED = tuple(_SIGNATURES)

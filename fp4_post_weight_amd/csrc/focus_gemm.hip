@@ -166,6 +166,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
     const int64_t n0 = (tile % tiles_n) * kBN;
     const int frag_row = lane & 31;
     const int frag_k = (lane >> 5) * 8;
+    // this workgroup's range of 64-wide k-steps [sb, se)
+    const int64_t nsteps_all = (a.K + kBK - 1) / kBK;
+    const int64_t sb = (int64_t)blockIdx.y * a.kchunk;
+    const int64_t se = sb + a.kchunk < nsteps_all ? sb + a.kchunk : nsteps_all;
 
     f32x16 acc[kTilesM][kTilesN];
 #pragma unroll
@@ -173,16 +177,16 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
 #pragma unroll
         for (int j = 0; j < kTilesN; ++j) acc[i][j] = (f32x16){};
 
-    // thread tid stages row tid of both operand tiles (K == 0: nothing to read)
-    const int64_t nsteps = (a.K + kBK - 1) / kBK;
+    // thread tid stages row tid of both operand tiles (no steps: nothing to read)
+    const int64_t nsteps = se > sb ? se - sb : 0;
     const int64_t mrows = nsteps > 0 ? a.M : 0, nrows = nsteps > 0 ? a.N : 0;
-    RowChunk ra = load_chunk<FAST>(a.xc, a.xs, m0 + tid, mrows, a.K, 0);
-    RowChunk rb = load_chunk<FAST>(a.wc, a.ws, n0 + tid, nrows, a.K, 0);
+    RowChunk ra = load_chunk<FAST>(a.xc, a.xs, m0 + tid, mrows, a.K, sb * kBK);
+    RowChunk rb = load_chunk<FAST>(a.wc, a.ws, n0 + tid, nrows, a.K, sb * kBK);
     store_chunk(lds[0] + tid * kLdsStride, ra);
     store_chunk(lds[0] + (kBM + tid) * kLdsStride, rb);
     if (nsteps > 1) {
-        ra = load_chunk<FAST>(a.xc, a.xs, m0 + tid, a.M, a.K, kBK);
-        rb = load_chunk<FAST>(a.wc, a.ws, n0 + tid, a.N, a.K, kBK);
+        ra = load_chunk<FAST>(a.xc, a.xs, m0 + tid, a.M, a.K, (sb + 1) * kBK);
+        rb = load_chunk<FAST>(a.wc, a.ws, n0 + tid, a.N, a.K, (sb + 1) * kBK);
     }
     __syncthreads();
     const int arow = wm * kWaveM, brow = kBM + wn * kWaveN;
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
     for (int64_t s = 0; s < nsteps; ++s) {
         const _Float16* cur = lds[s & 1];
         _Float16* nxt = lds[(s + 1) & 1];
-        const int64_t kn = (s + 2 < nsteps ? s + 2 : nsteps - 1) * kBK;
+        const int64_t kn = (sb + (s + 2 < nsteps ? s + 2 : nsteps - 1)) * kBK;
         const RowChunk na = load_chunk<FAST>(a.xc, a.xs, m0 + tid, a.M, a.K, kn);
         const RowChunk nb = load_chunk<FAST>(a.wc, a.ws, n0 + tid, a.N, a.K, kn);
         auto dequant = [&](int b) {
@@ -269,7 +273,25 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
     }
 
     // epilogue: register r of lane l in a 32 x 32 tile holds row
-    // 8*(r/4) + 4*(l/32) + r%4 and column l%32; Y = acc * (s2x[row] * s2w)
+    // 8*(r/4) + 4*(l/32) + r%4 and column l%32; Y = acc * (s2x[row] * s2w),
+    // or, with the sum split over k ranges, the unscaled partial of range
+    // blockIdx.y
+    if (a.ksplit > 1) {
+        float* part = a.part + (int64_t)blockIdx.y * a.M * a.N;
+#pragma unroll
+        for (int i = 0; i < kTilesM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + wm * kWaveM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (row >= a.M) continue;
+#pragma unroll
+                for (int j = 0; j < kTilesN; ++j) {
+                    const int64_t col = n0 + wn * kWaveN + j * 32 + (lane & 31);
+                    if (col < a.N) part[row * a.N + col] = acc[i][j][r];
+                }
+            }
+        return;
+    }
     const float s2w = a.ws2[0];
 #pragma unroll
     for (int i = 0; i < kTilesM; ++i) {
@@ -391,14 +413,18 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void k_nvfp4_linear_skinny(GemmA
     const int wave = tid >> 6;
     const int r32 = lane & 31, h = lane >> 5;
     const int64_t n0 = (int64_t)blockIdx.x * 32;
-    const int64_t nsteps = (a.K + kBK - 1) / kBK;
+    // this workgroup's range of 64-wide k-steps [sb, se)
+    const int64_t nsteps_all = (a.K + kBK - 1) / kBK;
+    const int64_t sb = (int64_t)blockIdx.y * a.kchunk;
+    const int64_t se = sb + a.kchunk < nsteps_all ? sb + a.kchunk : nsteps_all;
+    const int64_t nsteps = se > sb ? se - sb : 0;
 
     f32x16 acc[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[t] = (f32x16){};
 
-    auto load = [&](int64_t s, LaneChunk& w, LaneChunk (&x)[MT]) {
-        const int64_t k0 = (s < nsteps ? s : nsteps - 1) * kBK;
+    auto load = [&](int64_t s, LaneChunk& w, LaneChunk (&x)[MT]) {  // s: step within the range
+        const int64_t k0 = (sb + (s < nsteps ? s : nsteps - 1)) * kBK;
         w = load_lane<FAST>(a.wc, a.ws, n0 + r32, a.N, a.K, k0, h);
 #pragma unroll
         for (int t = 0; t < MT; ++t) x[t] = load_lane<FAST>(a.xc, a.xs, 32 * t + r32, a.M, a.K, k0, h);
@@ -461,7 +487,9 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void k_nvfp4_linear_skinny(GemmA
 #pragma unroll
         for (int w = 0; w < kSkinnyWaves; ++w) v += red[w][e];
         const int64_t row = e >> 5, col = n0 + (e & 31);
-        if (row < a.M && col < a.N) {
+        if (a.ksplit > 1) {  // unscaled partial of k range blockIdx.y
+            if (row < a.M && col < a.N) a.part[((int64_t)blockIdx.y * a.M + row) * a.N + col] = v;
+        } else if (row < a.M && col < a.N) {
             const float y = v * (a.xs2[a.xs2_per_row ? row : 0] * s2w);
             if (BF16_OUT) {
                 const uint32_t p = bf16_pair(y, 0.0f);
@@ -473,14 +501,89 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void k_nvfp4_linear_skinny(GemmA
     }
 }
 
+// Split sums: Y = (sum over the k ranges, in order, of the partials) *
+// (s2x[row] * s2w), one thread per output.
+template <bool BF16_OUT>
+__global__ __launch_bounds__(256) void k_nvfp4_linear_finalize(GemmArgs a) {
+    const int64_t total = a.M * a.N;
+    const float s2w = a.ws2[0];
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        float v = 0.0f;
+        for (int64_t s = 0; s < a.ksplit; ++s) v += a.part[s * total + e];
+        const int64_t row = e / a.N;
+        const float y = v * (a.xs2[a.xs2_per_row ? row : 0] * s2w);
+        if (BF16_OUT) {
+            const uint32_t p = bf16_pair(y, 0.0f);
+            reinterpret_cast<uint16_t*>(a.y)[e] = (uint16_t)(p & 0xFFFFu);
+        } else {
+            reinterpret_cast<float*>(a.y)[e] = y;
+        }
+    }
+}
+
 }  // namespace
 
 // Up to this many rows of X the few-token kernel is used.
 constexpr int64_t kSkinnyMaxM = 64;
 
-hipError_t launch_nvfp4_linear(const GemmArgs& a, bool fast, bool bf16_out, hipStream_t stream) {
+// Splitting the sum over k.  Each workgroup of either kernel occupies one CU,
+// so a launch of W workgroups runs ceil(W / CUs) rounds.  Splitting k into s
+// ranges multiplies the workgroups by s and divides each one's steps by s,
+// and costs s * M * N * 8 bytes of partial traffic (FP32 written, then read by
+// the finalize kernel) plus a launch.  The split count minimises
+//   rounds * (steps per range * t_step + t_round) + partial bytes / bandwidth,
+// with per-step and per-round times measured on MI355X for each kernel.  A
+// range keeps at least kMinSplitSteps steps (tiled kernel) or one step per
+// wavefront (few-token kernel).
+constexpr int64_t kMinSplitSteps = 4;
+
+static int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 256;
+    return cus;
+}
+
+int64_t nvfp4_linear_splits(int64_t M, int64_t N, int64_t K, int64_t part_bytes) {
+    const int64_t wgs = nvfp4_linear_workgroups(M, N);
+    const int64_t nsteps = (K + kBK - 1) / kBK;
+    if (wgs <= 0 || nsteps == 0) return 1;
+    const bool skinny = M <= kSkinnyMaxM;
+    const double t_step = skinny ? 0.16e-6 : 2.3e-6;   // s per 64-wide k-step of one workgroup
+    const double t_round = skinny ? 4.0e-6 : 3.0e-6;   // s of fixed cost per round
+    const double t_split = 4.0e-6;                      // finalize launch
+    const double bw = 5.0e12;                           // B/s for the partials
+    const int64_t cus = device_cus();
+    if (wgs >= cus) return 1;
+    int64_t smax = nsteps / (skinny ? kSkinnyWaves : kMinSplitSteps);
+    const int64_t per = M * N * 4;
+    if (per > 0 && smax > part_bytes / per) smax = part_bytes / per;
+    int64_t best = 1;
+    double best_t = 0.0;
+    for (int64_t s = 1; s <= smax || s == 1; ++s) {
+        const int64_t chunk = (nsteps + s - 1) / s;
+        const int64_t se = (nsteps + chunk - 1) / chunk;  // ranges actually used
+        const int64_t rounds = (wgs * se + cus - 1) / cus;
+        double t = (double)rounds * ((double)chunk * t_step + t_round);
+        if (se > 1) t += (double)se * (double)M * (double)N * 8.0 / bw + t_split;
+        if (s == 1 || t < best_t) {
+            best_t = t;
+            best = se;
+        }
+        if (s > 4 * (cus / wgs + 1)) break;  // more ranges only add rounds
+    }
+    return best;
+}
+
+hipError_t launch_nvfp4_linear(const GemmArgs& args, bool fast, bool bf16_out, hipStream_t stream) {
+    GemmArgs a = args;
+    const int64_t nsteps = (a.K + kBK - 1) / kBK;
+    a.ksplit = a.part ? nvfp4_linear_splits(a.M, a.N, a.K, a.part_bytes) : 1;
+    a.kchunk = a.ksplit > 1 ? (nsteps + a.ksplit - 1) / a.ksplit : (nsteps > 0 ? nsteps : 1);
+    const unsigned splits = (unsigned)a.ksplit;
     if (a.M <= kSkinnyMaxM) {
-        const dim3 grid((unsigned)((a.N + 31) / 32)), block(64 * kSkinnyWaves);
+        const dim3 grid((unsigned)((a.N + 31) / 32), splits), block(64 * kSkinnyWaves);
 #define FOCUS_SK(F, B)                                                                                 \
     do {                                                                                               \
         if (a.M <= 32) hipLaunchKernelGGL((k_nvfp4_linear_skinny<F, B, 1>), grid, block, 0, stream, a); \
@@ -494,21 +597,29 @@ hipError_t launch_nvfp4_linear(const GemmArgs& a, bool fast, bool bf16_out, hipS
             else FOCUS_SK(false, false);
         }
 #undef FOCUS_SK
-        return hipGetLastError();
-    }
-    const int64_t tiles_m = (a.M + kBM - 1) / kBM, tiles_n = (a.N + kBN - 1) / kBN;
-    const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kGemmThreads);
-    if (fast) {
-        if (bf16_out) hipLaunchKernelGGL((k_nvfp4_linear<true, true>), grid, block, 0, stream, a, tiles_n);
-        else hipLaunchKernelGGL((k_nvfp4_linear<true, false>), grid, block, 0, stream, a, tiles_n);
     } else {
-        if (bf16_out) hipLaunchKernelGGL((k_nvfp4_linear<false, true>), grid, block, 0, stream, a, tiles_n);
-        else hipLaunchKernelGGL((k_nvfp4_linear<false, false>), grid, block, 0, stream, a, tiles_n);
+        const int64_t tiles_m = (a.M + kBM - 1) / kBM, tiles_n = (a.N + kBN - 1) / kBN;
+        const dim3 grid((unsigned)(tiles_m * tiles_n), splits), block(kGemmThreads);
+        if (fast) {
+            if (bf16_out) hipLaunchKernelGGL((k_nvfp4_linear<true, true>), grid, block, 0, stream, a, tiles_n);
+            else hipLaunchKernelGGL((k_nvfp4_linear<true, false>), grid, block, 0, stream, a, tiles_n);
+        } else {
+            if (bf16_out) hipLaunchKernelGGL((k_nvfp4_linear<false, true>), grid, block, 0, stream, a, tiles_n);
+            else hipLaunchKernelGGL((k_nvfp4_linear<false, false>), grid, block, 0, stream, a, tiles_n);
+        }
+    }
+    if (a.ksplit > 1) {
+        const int64_t total = a.M * a.N;
+        int64_t g = (total + 255) / 256;
+        if (g > 65536) g = 65536;
+        if (bf16_out) hipLaunchKernelGGL((k_nvfp4_linear_finalize<true>), dim3((unsigned)g), dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((k_nvfp4_linear_finalize<false>), dim3((unsigned)g), dim3(256), 0, stream, a);
     }
     return hipGetLastError();
 }
 
 int64_t nvfp4_linear_workgroups(int64_t M, int64_t N) {
+    if (M <= kSkinnyMaxM) return (N + 31) / 32;
     return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
 }
 

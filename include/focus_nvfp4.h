@@ -299,7 +299,18 @@ int focus_dequantize_mixfp4(const uint8_t* codes, const uint8_t* scales, const f
  */
 int focus_nvfp4_linear(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_s2,
                        int x_s2_per_row, int64_t M, const uint8_t* w_codes, const uint8_t* w_scales,
-                       const float* w_s2, int64_t N, int64_t K, void* y, int y_dtype, void* stream);
+                       const float* w_s2, int64_t N, int64_t K, void* y, int y_dtype, float* workspace,
+                       int64_t workspace_bytes, void* stream);
+
+/* Workspace for focus_nvfp4_linear.  When an [M, N] output has too few tiles
+ * to fill the GPU, the sum over k is split into ranges whose FP32 partials
+ * [ranges, M, N] go to `workspace` (device memory owned by the caller,
+ * 4-byte aligned), then summed in order, scaled and converted by a second
+ * kernel (deterministic).  The call splits only as far as `workspace_bytes`
+ * allows (NULL or 0: no split; results then differ from a split call only
+ * by the FP32 summation order).  This returns the bytes for the full split
+ * (0 when none helps). */
+int64_t focus_nvfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus
 }

@@ -211,7 +211,10 @@ def test_mixfp4_validation(lib):
 
 
 def test_linear_validation(lib):
-    f = lib.focus_nvfp4_linear
+    g = lib.focus_nvfp4_linear
+
+    def f(*args):  # the calls below: no workspace
+        return g(*args[:-1], None, 0, args[-1])
     #        xc    xs    xs2 per  M   wc    ws    ws2   N   K   y    dt  stream
     assert f(FAKE, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, 40, FAKE, 0, None) == ERR_SHAPE   # K % 16
     assert f(FAKE, FAKE, FAKE, 1, -1, FAKE, FAKE, FAKE, 8, 64, FAKE, 0, None) == ERR_SHAPE
@@ -248,3 +251,16 @@ def test_binding_has_every_call():
     for name in _lib.EXPORTED:
         assert hasattr(focus, name[len("focus_"):]), name
     assert focus.status_string(0) == "ok"
+
+
+def test_linear_workspace(lib):
+    g = lib.focus_nvfp4_linear
+    # a negative size and a misaligned workspace are rejected before any launch
+    assert g(FAKE, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, 64, FAKE, 0, FAKE, -4, None) == ERR_RANGE
+    assert g(FAKE, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, 64, FAKE, 0, FAKE + 2, 64, None) == ERR_ALIGN
+    ws = lib.focus_nvfp4_linear_workspace_bytes
+    assert ws(8192, 14336, 4096) == 0                 # enough tiles: no split
+    assert ws(2048, 1024, 4096) > 0 and ws(2048, 1024, 4096) % (2048 * 1024 * 4) == 0
+    assert ws(16, 4096, 4096) > 0                     # few tokens, few columns
+    assert ws(16, 4096, 64) == 0                      # one k-step: nothing to split
+    assert ws(0, 16, 16) == 0 and ws(16, 16, 0) == 0

@@ -57,10 +57,10 @@ def oracle_linear(orc, xc, xs, s2x, wc, ws, s2w):
     return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
 
 
-def gpu_linear(focus, xc, xs, s2x, wc, ws, s2w, out_dtype):
+def gpu_linear(focus, xc, xs, s2x, wc, ws, s2w, out_dtype, workspace="auto"):
     x = focus.Quantized(xc.to(DEV), xs.to(DEV), None, torch.as_tensor(s2x, dtype=torch.float32).reshape(-1).to(DEV))
     w = focus.Quantized(wc.to(DEV), ws.to(DEV), None, torch.tensor([s2w], dtype=torch.float32, device=DEV))
-    y = focus.nvfp4_linear(x, w, out_dtype=out_dtype)
+    y = focus.nvfp4_linear(x, w, out_dtype=out_dtype, workspace=workspace)
     torch.cuda.synchronize()
     return y.float().cpu().numpy().astype(np.float64)
 
@@ -99,6 +99,9 @@ SHAPES = [(1, 1, 16), (7, 33, 48), (16, 200, 1040), (16, 4096, 4096), (17, 64, 6
 
 @pytest.mark.parametrize("M,N,K", SHAPES, ids=lambda v: str(v))
 def test_linear_within_bound(focus, orc, M, N, K):
+    """Every shape with the split-k workspace (split wherever the output has
+    few tiles) and without it; the split result is also run-to-run
+    identical."""
     xc, xs, wc, ws = operands(M, N, K, M + N + K)
     rng = np.random.default_rng(K)
     s2x = (rng.uniform(0.5, 2.0, M) * 2.0 ** -9).astype(np.float32)
@@ -107,6 +110,10 @@ def test_linear_within_bound(focus, orc, M, N, K):
     for dt in (torch.float32, torch.bfloat16):
         y = gpu_linear(focus, xc, xs, s2x, wc, ws, s2w, dt)
         check_bound(y, ref, refabs, K, dt == torch.bfloat16, f"{(M, N, K)} {dt}")
+        y2 = gpu_linear(focus, xc, xs, s2x, wc, ws, s2w, dt)
+        assert np.array_equal(y, y2), "split-k result differs between runs"
+        y0 = gpu_linear(focus, xc, xs, s2x, wc, ws, s2w, dt, workspace=None)
+        check_bound(y0, ref, refabs, K, dt == torch.bfloat16, f"{(M, N, K)} {dt} no workspace")
 
 
 def test_linear_single_activation_scale_and_wide_scales(focus, orc):
