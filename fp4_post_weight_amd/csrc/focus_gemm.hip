@@ -502,21 +502,50 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void k_nvfp4_linear_skinny(GemmA
 }
 
 // Split sums: Y = (sum over the k ranges, in order, of the partials) *
-// (s2x[row] * s2w), one thread per output.
-template <bool BF16_OUT>
+// (s2x[row] * s2w).  VEC: four consecutive outputs per thread with 16-byte
+// loads of each partial (M * N % 4 == 0, workspace 16-byte and Y 8- or
+// 16-byte aligned); otherwise one output per thread.
+template <bool BF16_OUT, bool VEC>
 __global__ __launch_bounds__(256) void k_nvfp4_linear_finalize(GemmArgs a) {
     const int64_t total = a.M * a.N;
     const float s2w = a.ws2[0];
-    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-        float v = 0.0f;
-        for (int64_t s = 0; s < a.ksplit; ++s) v += a.part[s * total + e];
-        const int64_t row = e / a.N;
-        const float y = v * (a.xs2[a.xs2_per_row ? row : 0] * s2w);
-        if (BF16_OUT) {
-            const uint32_t p = bf16_pair(y, 0.0f);
-            reinterpret_cast<uint16_t*>(a.y)[e] = (uint16_t)(p & 0xFFFFu);
+    constexpr int V = VEC ? 4 : 1;
+    for (int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V; e < total; e += (int64_t)gridDim.x * 256 * V) {
+        float v[V];
+        if (VEC) {
+            float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            for (int64_t s = 0; s < a.ksplit; ++s) {
+                const float4 p = *reinterpret_cast<const float4*>(a.part + s * total + e);
+                acc.x += p.x;
+                acc.y += p.y;
+                acc.z += p.z;
+                acc.w += p.w;
+            }
+            v[0] = acc.x;
+            v[VEC ? 1 : 0] = acc.y;
+            v[VEC ? 2 : 0] = acc.z;
+            v[VEC ? 3 : 0] = acc.w;
         } else {
-            reinterpret_cast<float*>(a.y)[e] = y;
+            float acc = 0.0f;
+            for (int64_t s = 0; s < a.ksplit; ++s) acc += a.part[s * total + e];
+            v[0] = acc;
+        }
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const int64_t row = (e + i) / a.N;
+            v[i] = v[i] * (a.xs2[a.xs2_per_row ? row : 0] * s2w);
+        }
+        if (BF16_OUT) {
+            if (VEC) {
+                const uint2 o = make_uint2(bf16_pair(v[0], v[VEC ? 1 : 0]), bf16_pair(v[VEC ? 2 : 0], v[VEC ? 3 : 0]));
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + e) = o;
+            } else {
+                reinterpret_cast<uint16_t*>(a.y)[e] = (uint16_t)(bf16_pair(v[0], 0.0f) & 0xFFFFu);
+            }
+        } else {
+            if (VEC) *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + e) =
+                make_float4(v[0], v[VEC ? 1 : 0], v[VEC ? 2 : 0], v[VEC ? 3 : 0]);
+            else reinterpret_cast<float*>(a.y)[e] = v[0];
         }
     }
 }
@@ -610,10 +639,18 @@ hipError_t launch_nvfp4_linear(const GemmArgs& args, bool fast, bool bf16_out, h
     }
     if (a.ksplit > 1) {
         const int64_t total = a.M * a.N;
-        int64_t g = (total + 255) / 256;
+        const bool vec = total % 4 == 0 && ((uintptr_t)a.part & 15u) == 0 &&
+                         ((uintptr_t)a.y & (bf16_out ? 7u : 15u)) == 0;
+        int64_t g = (total / (vec ? 4 : 1) + 255) / 256;
         if (g > 65536) g = 65536;
-        if (bf16_out) hipLaunchKernelGGL((k_nvfp4_linear_finalize<true>), dim3((unsigned)g), dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((k_nvfp4_linear_finalize<false>), dim3((unsigned)g), dim3(256), 0, stream, a);
+        const dim3 grid((unsigned)g), block(256);
+        if (vec) {
+            if (bf16_out) hipLaunchKernelGGL((k_nvfp4_linear_finalize<true, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((k_nvfp4_linear_finalize<false, true>), grid, block, 0, stream, a);
+        } else {
+            if (bf16_out) hipLaunchKernelGGL((k_nvfp4_linear_finalize<true, false>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((k_nvfp4_linear_finalize<false, false>), grid, block, 0, stream, a);
+        }
     }
     return hipGetLastError();
 }
