@@ -9,31 +9,34 @@
 // with c an E2M1 value and S an E4M3 block scale.
 //
 // How it maps onto CDNA4:
-//  * Each operand element c*S has at most 5 significant bits (E2M1 has 2,
-//    E4M3 4) and lies in [2^-10, 2688] for normal scales, so it is exact in
-//    FP16, and the product of two such values is exact in FP32.  The
-//    contraction therefore runs on the FP16 matrix cores
-//    (v_mfma_f32_32x32x16_f16) with FP32 accumulation, and s2x*s2w is applied
-//    once per output.  (gfx950's FP4 matrix instructions take one E8M0
-//    scale per 32 elements; NVFP4's E4M3 scale per 16 elements is not
-//    expressible there.)
-//  * Dequantization costs about one vector operation per element and is
-//    done once per workgroup, before LDS: the scale byte is split into
-//    S = 2^E * mu (mu in [1, 2)); v_cvt_scalef32_pk_f16_fp4 with scale 2^E
-//    gives c * 2^E for two codes, and one packed FP16 multiply by mu gives
-//    c * S, both exact.
+//  * Each operand element c*S has at most 6 significant bits (a 2-bit E2M1
+//    significand times a 4-bit E4M3 one) and is 0 or lies in [2^-10, 2688],
+//    so it is exact in FP16, and the product of two such values (at most 12
+//    bits) is exact in FP32.  The contraction therefore runs on the FP16
+//    matrix cores (v_mfma_f32_32x32x16_f16) with FP32 accumulation, and
+//    s2x*s2w is applied once per output.  (gfx950's FP4 matrix instructions
+//    take one E8M0 scale per 32 elements; NVFP4's E4M3 scale per 16
+//    elements is not expressible there.)
+//  * Dequantization costs about one vector operation per element: the
+//    scale bytes become FP16 two at a time (v_cvt_scalef32_pk_f16_fp8; every
+//    E4M3 value is a normal FP16 number), v_cvt_scalef32_pk_f16_fp4 with
+//    scale 1 turns two codes into c, and one packed FP16 multiply gives c*S.
 //  * Workgroup tile 256 x 256 x 64 (4 wavefronts, each 128 x 128 = 4 x 4
 //    MFMA tiles of 32 x 32, 256 FP32 accumulators per lane).  Both operand
-//    tiles are FP16 in LDS (rows padded to 144 bytes) in two stages: while
-//    the matrix cores consume one k-step, the codes of the next step
-//    (loaded into registers one step earlier) are dequantized into the other
-//    stage, and the step after that is being loaded.  Fragments are read two
-//    k16 slices ahead, the dequantization runs in slices 0-1 interleaved with
-//    the matrix instructions, and the one barrier per step sits after slice
-//    1, so slices 2-3 cover the reads of the next step's first fragments.
-//    LDS traffic (about 192 KB per step per CU against an LDS that delivers
-//    about 128 B per clock) is what bounds this kernel below the matrix-core
-//    peak.
+//    tiles are dequantized once per workgroup into FP16 in LDS (rows padded
+//    to 144 bytes) in two stages: while the matrix cores consume one k-step,
+//    the codes of the next step (loaded into registers one step earlier)
+//    are dequantized into the other stage, and the step after that is being
+//    loaded.  Fragments are read two k16 slices ahead, the dequantization
+//    runs in slices 0-1 interleaved with the matrix instructions, and the
+//    one barrier per step sits after slice 1, so slices 2-3 cover the reads
+//    of the next step's first fragments.  Measured, the matrix cores are
+//    busy a little under half of the cycles; LDS traffic (about 192 KB per
+//    step and CU), the dequantization and the waits of a pipeline with one
+//    wavefront per SIMD share the rest.  Keeping codes in LDS and
+//    dequantizing per wavefront cuts LDS traffic four-fold but doubles the
+//    vector work, which lowers the clock under this load; measured, it was
+//    slower.
 //  * Loads are straight-line in the common case (K % 64 == 0, aligned): a
 //    row past the end of X or W reads the last row instead; it only feeds
 //    outputs that are never stored.
@@ -106,40 +109,40 @@ __device__ __forceinline__ RowChunk load_chunk(const uint8_t* __restrict__ codes
     return r;
 }
 
-// c * S for the 16 elements of one block, as FP16, elements 0-7 in lo and
-// 8-15 in hi, branch-free for every scale byte.  With exponent field e and
-// mantissa field m, S = 2^(max(e,1) - 10) * mu, mu = 8 + m (normal, e >= 1)
-// or m (zero and subnormal, e == 0), an integer in [0, 15]; 0x7F / 0xFF are
-// NaN.  v_cvt_scalef32_pk_f16_fp4 with the power of two gives
-// c * 2^(max(e,1) - 10) in [2^-10, 192] and one packed FP16 multiply by mu
-// gives c * S (at most 6 significant bits, at most 2880): both exact.
-__device__ __forceinline__ void dequant_block_f16(uint2 c, uint32_t sbyte, f16x8& lo, f16x8& hi) {
-    const uint32_t ef = (sbyte >> 3) & 15u, mb = sbyte & 7u;
-    const float p2 = __uint_as_float((max(ef, 1u) + 117u) << 23);
-    const _Float16 mag = (_Float16)(uint16_t)(mb | (ef != 0u ? 8u : 0u));
-    uint16_t mu_bits = __builtin_bit_cast(uint16_t, mag) | (uint16_t)((sbyte & 0x80u) << 8);
-    mu_bits = (sbyte & 0x7Fu) == 0x7Fu ? (uint16_t)0x7E00u : mu_bits;
-    const _Float16 mu = __builtin_bit_cast(_Float16, mu_bits);
-    const f16x2 m2 = {mu, mu};
-    const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c.x, p2, 0) * m2;
-    const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c.x, p2, 1) * m2;
-    const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c.x, p2, 2) * m2;
-    const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c.x, p2, 3) * m2;
-    const f16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c.y, p2, 0) * m2;
-    const f16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c.y, p2, 1) * m2;
-    const f16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c.y, p2, 2) * m2;
-    const f16x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c.y, p2, 3) * m2;
-    lo = (f16x8){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-    hi = (f16x8){b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+// E4M3 block scales to FP16, two per instruction: the two bytes of the low
+// (HI = false) or high 16-bit half of a scale dword, lower byte first.
+// Exact: every E4M3 value, subnormals included, is a normal FP16 number, and
+// the NaN bytes 0x7F / 0xFF give NaN.
+template <bool HI>
+__device__ __forceinline__ f16x2 scale_pair(uint32_t s) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, HI);
+}
+
+// c * S for the eight codes of one dword (element 2j in the low nibble of
+// byte j): v_cvt_scalef32_pk_f16_fp4 with scale 1 gives c exactly, and one
+// packed FP16 multiply by S gives c * S, also exact (at most 6 significant
+// bits; 0 or a magnitude in [2^-10, 2688]).
+__device__ __forceinline__ f16x8 codes_times(uint32_t w, _Float16 S) {
+    const f16x2 s2 = {S, S};
+    const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+    const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+    const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+    const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+    return (f16x8){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+}
+
+// Scale of block b (0-3) of a row's k-step from its two scale pairs.
+__device__ __forceinline__ _Float16 block_scale(f16x2 s01, f16x2 s23, int b) {
+    return b == 0 ? s01.x : b == 1 ? s01.y : b == 2 ? s23.x : s23.y;
 }
 
 __device__ __forceinline__ void store_chunk(_Float16* lds_row, const RowChunk& r) {
+    const f16x2 s01 = scale_pair<false>(r.s), s23 = scale_pair<true>(r.s);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        f16x8 lo, hi;
-        dequant_block_f16(r.c[b], (r.s >> (8 * b)) & 0xFFu, lo, hi);
-        *reinterpret_cast<f16x8*>(lds_row + 16 * b) = lo;
-        *reinterpret_cast<f16x8*>(lds_row + 16 * b + 8) = hi;
+        const _Float16 S = block_scale(s01, s23, b);
+        *reinterpret_cast<f16x8*>(lds_row + 16 * b) = codes_times(r.c[b].x, S);
+        *reinterpret_cast<f16x8*>(lds_row + 16 * b + 8) = codes_times(r.c[b].y, S);
     }
 }
 
@@ -215,14 +218,14 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
         const int64_t kn = (sb + (s + 2 < nsteps ? s + 2 : nsteps - 1)) * kBK;
         const RowChunk na = load_chunk<FAST>(a.xc, a.xs, m0 + tid, a.M, a.K, kn);
         const RowChunk nb = load_chunk<FAST>(a.wc, a.ws, n0 + tid, a.N, a.K, kn);
+        const f16x2 xa01 = scale_pair<false>(ra.s), xa23 = scale_pair<true>(ra.s);
+        const f16x2 xb01 = scale_pair<false>(rb.s), xb23 = scale_pair<true>(rb.s);
         auto dequant = [&](int b) {
-            f16x8 lo, hi;
-            dequant_block_f16(ra.c[b], (ra.s >> (8 * b)) & 0xFFu, lo, hi);
-            *reinterpret_cast<f16x8*>(nxt + tid * kLdsStride + 16 * b) = lo;
-            *reinterpret_cast<f16x8*>(nxt + tid * kLdsStride + 16 * b + 8) = hi;
-            dequant_block_f16(rb.c[b], (rb.s >> (8 * b)) & 0xFFu, lo, hi);
-            *reinterpret_cast<f16x8*>(nxt + (kBM + tid) * kLdsStride + 16 * b) = lo;
-            *reinterpret_cast<f16x8*>(nxt + (kBM + tid) * kLdsStride + 16 * b + 8) = hi;
+            const _Float16 sa = block_scale(xa01, xa23, b), sbv = block_scale(xb01, xb23, b);
+            *reinterpret_cast<f16x8*>(nxt + tid * kLdsStride + 16 * b) = codes_times(ra.c[b].x, sa);
+            *reinterpret_cast<f16x8*>(nxt + tid * kLdsStride + 16 * b + 8) = codes_times(ra.c[b].y, sa);
+            *reinterpret_cast<f16x8*>(nxt + (kBM + tid) * kLdsStride + 16 * b) = codes_times(rb.c[b].x, sbv);
+            *reinterpret_cast<f16x8*>(nxt + (kBM + tid) * kLdsStride + 16 * b + 8) = codes_times(rb.c[b].y, sbv);
         };
         // slice 0
         load_frags(fa2, cur, arow, 2, frag_row, frag_k);
@@ -373,34 +376,6 @@ __device__ __forceinline__ LaneChunk load_lane(const uint8_t* __restrict__ codes
     return r;
 }
 
-// 2^E and mu of a scale byte (the decomposition of dequant_block_f16), mu as
-// an FP16 pair.
-struct ScaleParts {
-    float p2;
-    f16x2 mu;
-};
-
-__device__ __forceinline__ ScaleParts split_scale(uint32_t sbyte) {
-    const uint32_t ef = (sbyte >> 3) & 15u, mb = sbyte & 7u;
-    ScaleParts r;
-    r.p2 = __uint_as_float((max(ef, 1u) + 117u) << 23);
-    const _Float16 mag = (_Float16)(uint16_t)(mb | (ef != 0u ? 8u : 0u));
-    uint16_t mu_bits = __builtin_bit_cast(uint16_t, mag) | (uint16_t)((sbyte & 0x80u) << 8);
-    mu_bits = (sbyte & 0x7Fu) == 0x7Fu ? (uint16_t)0x7E00u : mu_bits;
-    const _Float16 mu = __builtin_bit_cast(_Float16, mu_bits);
-    r.mu = (f16x2){mu, mu};
-    return r;
-}
-
-// Eight codes (one dword) -> fragment of c * S.
-__device__ __forceinline__ f16x8 frag_from_codes(uint32_t w, const ScaleParts& sp) {
-    const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sp.p2, 0) * sp.mu;
-    const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sp.p2, 1) * sp.mu;
-    const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sp.p2, 2) * sp.mu;
-    const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sp.p2, 3) * sp.mu;
-    return (f16x8){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-}
-
 __device__ __forceinline__ uint32_t dword_of(const uint4& v, int kk) {
     return kk == 0 ? v.x : kk == 1 ? v.y : kk == 2 ? v.z : v.w;
 }
@@ -430,19 +405,20 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void k_nvfp4_linear_skinny(GemmA
         for (int t = 0; t < MT; ++t) x[t] = load_lane<FAST>(a.xc, a.xs, 32 * t + r32, a.M, a.K, k0, h);
     };
     auto compute = [&](const LaneChunk& w, const LaneChunk (&x)[MT]) {
+        // scales of blocks 2h and 2h + 1 (bits 0-15 of s)
+        const f16x2 pw = scale_pair<false>(w.s);
+        f16x2 px[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) px[t] = scale_pair<false>(x[t].s);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-            const ScaleParts sw = split_scale((w.s >> (8 * half)) & 0xFFu);
-            ScaleParts sx[MT];
-#pragma unroll
-            for (int t = 0; t < MT; ++t) sx[t] = split_scale((x[t].s >> (8 * half)) & 0xFFu);
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int kk = 2 * half + q;
-                const f16x8 fb = frag_from_codes(dword_of(w.c, kk), sw);
+                const f16x8 fb = codes_times(dword_of(w.c, kk), half ? pw.y : pw.x);
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {
-                    const f16x8 fa = frag_from_codes(dword_of(x[t].c, kk), sx[t]);
+                    const f16x8 fa = codes_times(dword_of(x[t].c, kk), half ? px[t].y : px[t].x);
                     acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, fb, acc[t], 0, 0, 0);
                 }
             }
@@ -554,6 +530,7 @@ __global__ __launch_bounds__(256) void k_nvfp4_linear_finalize(GemmArgs a) {
 
 // Up to this many rows of X the few-token kernel is used.
 constexpr int64_t kSkinnyMaxM = 64;
+
 
 // Splitting the sum over k.  Each workgroup of either kernel occupies one CU,
 // so a launch of W workgroups runs ceil(W / CUs) rounds.  Splitting k into s

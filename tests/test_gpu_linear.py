@@ -125,6 +125,32 @@ def test_linear_single_activation_scale_and_wide_scales(focus, orc):
     check_bound(y, ref, refabs, K, False, "one s2x, scale bytes 0x01..0x7E")
 
 
+@pytest.mark.parametrize("M,N,K", [(16, 200, 1024), (130, 300, 512), (70, 90, 1040)], ids=lambda v: str(v))
+def test_linear_signed_and_nan_scales(focus, orc, M, N, K):
+    """Scale bytes with either sign over 0x00..0x7E (zero, subnormal, normal)
+    and the NaN bytes 0x7F / 0xFF planted in a few rows of X and W: an output
+    is NaN exactly where the oracle's is (a NaN block scale poisons its row
+    even against zero codes), and every other output is within the bound.
+    The three shapes take the few-token, tiled and masked-load paths."""
+    xc, xs, wc, ws = operands(M, N, K, 11, scale_lo=0x00, scale_hi=0x7F)
+    g = torch.Generator().manual_seed(M * N + K)
+    xs = xs | (torch.randint(0, 2, xs.shape, generator=g, dtype=torch.uint8) << 7)
+    ws = ws | (torch.randint(0, 2, ws.shape, generator=g, dtype=torch.uint8) << 7)
+    for t, b, v in ((0, 0, 0x7F), (M - 1, K // 16 - 1, 0xFF), (M // 2, 1, 0x7F)):
+        xs[t, b] = v
+    for o, b, v in ((1, K // 16 - 1, 0xFF), (N - 2, 0, 0x7F)):
+        ws[o, b] = v
+    s2x, s2w = np.float32(0.01), np.float32(0.002)
+    ref, refabs = oracle_linear(orc, xc.numpy(), xs.numpy(), s2x, wc.numpy(), ws.numpy(), s2w)
+    nan = np.isnan(ref)
+    assert nan.any() and not nan.all()
+    for dt in (torch.float32, torch.bfloat16):
+        y = gpu_linear(focus, xc, xs, s2x, wc, ws, s2w, dt)
+        assert np.array_equal(np.isnan(y), nan), f"{dt}: NaN pattern differs"
+        check_bound(np.where(nan, 0.0, y), np.where(nan, 0.0, ref), np.where(nan, 0.0, refabs), K,
+                    dt == torch.bfloat16, f"{(M, N, K)} {dt} signed scales")
+
+
 def test_linear_degenerate(focus):
     x = focus.Quantized(torch.zeros((5, 0), dtype=torch.uint8, device=DEV),
                         torch.zeros((5, 0), dtype=torch.uint8, device=DEV), None,
