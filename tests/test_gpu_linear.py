@@ -151,6 +151,50 @@ def test_linear_signed_and_nan_scales(focus, orc, M, N, K):
                     dt == torch.bfloat16, f"{(M, N, K)} {dt} signed scales")
 
 
+@pytest.mark.parametrize("M", [1, 65])
+@pytest.mark.parametrize("nb", [256, 254])
+@pytest.mark.parametrize("side", ["x", "w"])
+def test_linear_every_scale_byte(focus, side, nb, M):
+    """Closed form over every E4M3 scale byte except NaN: one operand's block
+    scales run through all byte values (signed zeros, subnormals, normals up
+    to +-448) and the other operand is one-hot, so each output is exactly
+    one scale's value, Y[t, o] = E4M3(byte of output o), in FP32 and in BF16
+    (at most 4 significant bits; the -0 byte reads as +0 because the FP32
+    sum starts from +0).  Expected values come from torch's
+    float8_e4m3fn decoding.  nb = 256 blocks (K % 64 == 0, the 0x7F / 0xFF
+    slots refilled with 0x38) takes the aligned loads, 254 the masked ones;
+    M = 1 the few-token kernel, 65 the tiled one."""
+    byts = [b for b in range(256) if (b & 0x7F) != 0x7F]
+    if nb == 256:
+        byts = [b if (b & 0x7F) != 0x7F else 0x38 for b in range(256)]
+    K, N = 16 * nb, nb
+    sel = torch.tensor(byts, dtype=torch.uint8)
+    want = sel.view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    one = np.uint8(0x02)  # E2M1 1.0 in the low nibble: element 16 j of byte 8 j
+    if side == "x":
+        # X row: block j has scale byts[j] and a 1.0 at element 16 j; W row o
+        # is 1.0 at element 16 o under unit scales
+        xc = torch.zeros((M, K // 2), dtype=torch.uint8)
+        xc[:, 8 * torch.arange(nb)] = one
+        xs = sel.repeat(M, 1)
+        wc = torch.zeros((N, K // 2), dtype=torch.uint8)
+        wc[torch.arange(N), 8 * torch.arange(N)] = one
+        ws = torch.full((N, nb), 0x38, dtype=torch.uint8)
+    else:
+        # W row o: block 0 has scale byts[o] and a 1.0 at element 0; X row is
+        # 1.0 at element 0 under unit scales
+        xc = torch.zeros((M, K // 2), dtype=torch.uint8)
+        xc[:, 0] = one
+        xs = torch.full((M, nb), 0x38, dtype=torch.uint8)
+        wc = torch.zeros((N, K // 2), dtype=torch.uint8)
+        wc[:, 0] = one
+        ws = torch.full((N, nb), 0x38, dtype=torch.uint8)
+        ws[:, 0] = sel
+    for dt in (torch.float32, torch.bfloat16):
+        y = gpu_linear(focus, xc, xs, np.float32(1.0), wc, ws, np.float32(1.0), dt)
+        assert np.array_equal(y, np.broadcast_to(want, (M, N))), f"{side} {nb} {M} {dt}"
+
+
 def test_linear_degenerate(focus):
     x = focus.Quantized(torch.zeros((5, 0), dtype=torch.uint8, device=DEV),
                         torch.zeros((5, 0), dtype=torch.uint8, device=DEV), None,
