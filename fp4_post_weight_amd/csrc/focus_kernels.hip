@@ -334,8 +334,15 @@ __device__ __forceinline__ int find_tensor(const int64_t* tile_start, int n, int
 // per tile with all loads issued before any arithmetic
 // ---------------------------------------------------------------------------
 
-constexpr int kQuantU = 2;
-constexpr int64_t kQuantTile = (int64_t)kThreads * kQuantU;
+// Blocks per lane per tile (loads in flight per lane).  Measured on the 8B
+// set: plain NVFP4 without w' streams best with 3 (2: 69.6 %, 3: 71.8 %,
+// 4: 70.5 %, 6: 69.1 %, 8: 68.1 % of peak), every other variant with 2 (4
+// costs the w' kernel about 5 % through its larger register file).
+template <bool DEQ, int MODE>
+struct QuantU {
+    static constexpr int value = (DEQ || MODE != 0) ? 2 : 3;
+};
+constexpr int64_t kQuantTile = (int64_t)kThreads * 2;  // the tile of every U = 2 variant
 
 // FlipQuant MixFP4: is block `blk` of tensor j in an E0M3 tile?  block ->
 // (row, block in row) -> (tile row, tile column) with the batch's div_magic
@@ -357,6 +364,7 @@ __device__ __forceinline__ bool mix_block_is_e0m3(const Batch& bt, int j, int64_
 template <bool HAS_M, bool HAS_Q, bool DEQ, int MODE = 0, typename Batch = QuantBatch>
 __global__ __launch_bounds__(kThreads) void k_quantize(Batch bt, int64_t ntiles) {
     constexpr bool FO6 = MODE == 1 || MODE == 3, MX = MODE == 2, MIX = MODE == 3;
+    constexpr int kQuantU = QuantU<DEQ, MODE>::value;
     __shared__ uint4 xch[DEQ ? kThreads / 64 : 1][128];
     constexpr bool kLdsLoadW = LdsLoadW<DEQ>::value;
     __shared__ uint4 xchw[kLdsLoadW ? kThreads / 64 : 1][128];
@@ -374,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize(Batch bt, int64_t ntiles)
         const double rden4 = FO6 ? 1.0 / (double)(4.0f * s2) : 0.0;
         const double rden7 = MIX ? 1.0 / (double)(7.0f * s2) : 0.0;
         const int64_t nblk = bt.nblk[j];
-        const int64_t tile0 = (tile - bt.tile_start[j]) * kQuantTile;
+        const int64_t tile0 = (tile - bt.tile_start[j]) * (int64_t)kThreads * kQuantU;
         uint4 va[kQuantU] = {}, vb[kQuantU] = {};
         float mb[kQuantU];
         float2 qq[kQuantU];
@@ -701,10 +709,12 @@ hipError_t launch_tensor_scale(ScaleBatch& bt, hipStream_t stream) {
 }
 
 hipError_t launch_quantize(QuantBatch& bt, int key, hipStream_t stream) {
+    // keys 0-7: plain NVFP4 (bit 0: w'), 8-9: FourOverSix, 16-23: MXFP4
+    const int64_t tb = (int64_t)kThreads * (key < 8 && !(key & 1) ? QuantU<false, 0>::value : 2);
     int64_t t = 0;
     for (int j = 0; j < bt.n; ++j) {
         bt.tile_start[j] = t;
-        t += (bt.nblk[j] + kQuantTile - 1) / kQuantTile;
+        t += (bt.nblk[j] + tb - 1) / tb;
     }
     bt.tile_start[bt.n] = t;
     const dim3 grid(grid_for_tiles(t)), block(kThreads);
