@@ -76,8 +76,11 @@ def check_bound(y, ref, refabs, K, bf16, label):
     return float(np.max(err / np.maximum(refabs, 1e-300)))
 
 
-def test_exact_when_partial_sums_are_exact(focus, orc):
-    M, N, K = 300, 520, 1024
+@pytest.mark.parametrize("M", [300, 40, 16, 5], ids=lambda v: f"M{v}")
+def test_exact_when_partial_sums_are_exact(focus, orc, M):
+    # M = 300: tiled kernel; 40: few-token kernel with two 32-row X tiles;
+    # 16 and 5: one X tile (operand and output layouts of each)
+    N, K = 520, 1024
     xc, _, wc, _ = operands(M, N, K, 1)
     xs = torch.full((M, K // 16), 0x38, dtype=torch.uint8)
     ws = torch.full((N, K // 16), 0x38, dtype=torch.uint8)
