@@ -285,6 +285,63 @@ def test_full_size_sampled(focus, orc, ws_name, shape, dequant):
 
 
 # ---------------------------------------------------------------------------
+# one tensor past 32-bit offsets
+# ---------------------------------------------------------------------------
+
+BIG = (131075, 16384)  # 2^31 + 49,152 weights; W, w' and the dequantized copy 4.3 GB each
+
+
+def test_beyond_32bit_offsets(focus, orc):
+    """One linear whose element offsets pass 2^31 and whose W, w' and
+    dequantized bytes pass 2^32 (row 131072 starts at element 2^31): s2 of
+    the whole tensor equals the oracle's, rows on both sides of the boundary
+    and the last rows match the oracle, the codes-only call gives the same
+    codes and scales as the call with w', and the stand-alone dequantize
+    equals the fused w' everywhere."""
+    rows, cols = BIG
+    w = synth.weights(BIG, seed=7, tensor_id=900, device=DEV)
+    m = synth.block_factor_lognormal((rows, cols // 16), seed=7, tensor_id=901, device=DEV)
+    q = synth.logits((rows, cols // 8), seed=7, tensor_id=902, device=DEV)
+    s2d, amaxd = focus.tensor_scale(w)
+    res = focus.quantize(w, m, q, s2d, dequant=True)
+    only = focus.quantize(w, m, q, s2d, dequant=False)
+    assert torch.equal(only.codes, res.codes) and torch.equal(only.scales, res.scales)
+    del only
+    deq = focus.dequantize(res.codes, res.scales, s2d)
+    assert torch.equal(deq.view(torch.int16), res.deq.view(torch.int16))
+    del deq
+    torch.cuda.synchronize()
+    wb = np_bits(w)
+    s2_o, amax_o = orc.tensor_scale(wb)
+    assert s2d.item() == float(s2_o) and amaxd.item() == float(amax_o)
+    rng = np.random.default_rng(11)
+    idx = np.unique(np.concatenate([[0, 65535, 65536, 131070, 131071, 131072, 131073, rows - 1],
+                                    rng.integers(0, rows, 24)]))
+    it = torch.from_numpy(idx).to(DEV)
+    st = parity.check_quantized(orc, wb[idx], m[it].cpu().numpy(), q[it].cpu().numpy(), s2_o,
+                                res.codes[it].cpu().numpy(), res.scales[it].cpu().numpy(),
+                                np_bits(res.deq[it]), label=f"{BIG}")
+    print(f"{BIG}: {st}", flush=True)
+
+
+def test_act_beyond_32bit_offsets(focus, orc):
+    """Per-token activations X [262147, 8192] (2^31 + 24,576 elements): the
+    tokens past element 2^31 match the oracle."""
+    t, h = 262147, 8192
+    x = synth.activations((t, h), seed=5, tensor_id=903, device=DEV)
+    res = focus.quantize_act_per_token(x, dequant=True)
+    torch.cuda.synchronize()
+    idx = np.array([0, 131071, 262143, 262144, 262145, t - 1])
+    it = torch.from_numpy(idx).to(DEV)
+    xb = np_bits(x[it])
+    c, s, s2, xd = parity.oracle_act_rows(orc, xb, True)
+    assert np.array_equal(res.s2[it].cpu().numpy().view(np.uint32), s2.view(np.uint32))
+    assert np.array_equal(res.scales[it].cpu().numpy(), s)
+    assert np.array_equal(res.codes[it].cpu().numpy(), c)
+    assert np.array_equal(np_bits(res.deq[it]), xd)
+
+
+# ---------------------------------------------------------------------------
 # batched calls: identical to the single calls, and to the oracle
 # ---------------------------------------------------------------------------
 
