@@ -198,6 +198,24 @@ def test_linear_every_scale_byte(focus, side, nb, M):
         assert np.array_equal(y, np.broadcast_to(want, (M, N))), f"{side} {nb} {M} {dt}"
 
 
+def test_linear_beyond_32bit_outputs(focus, orc):
+    """Y [32770, 65540] (2^31 + 262,312 outputs, 4.3 GB of BF16) with K = 64:
+    whole output rows on both sides of element 2^31 (row 32768 holds it) and
+    the last row match the oracle within the bound."""
+    M, N, K = 32770, 65540, 64
+    xc, xs, wc, ws = operands(M, N, K, 13)
+    s2x = np.full(M, 2.0 ** -9, dtype=np.float32)
+    s2w = np.float32(1.5e-3)
+    x = focus.Quantized(xc.to(DEV), xs.to(DEV), None, torch.from_numpy(s2x).to(DEV))
+    w = focus.Quantized(wc.to(DEV), ws.to(DEV), None, torch.tensor([s2w], dtype=torch.float32, device=DEV))
+    y = focus.nvfp4_linear(x, w, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    idx = np.array([0, 32767, 32768, 32769])
+    ref, refabs = oracle_linear(orc, xc[idx].numpy(), xs[idx].numpy(), s2x[idx], wc.numpy(), ws.numpy(), s2w)
+    got = y[torch.from_numpy(idx).to(DEV)].float().cpu().numpy().astype(np.float64)
+    check_bound(got, ref, refabs, K, True, "Y past 2^31 outputs")
+
+
 def test_linear_degenerate(focus):
     x = focus.Quantized(torch.zeros((5, 0), dtype=torch.uint8, device=DEV),
                         torch.zeros((5, 0), dtype=torch.uint8, device=DEV), None,
