@@ -237,8 +237,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
 #pragma unroll
         for (int g = 0; g < 16; ++g) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-            if (g >= 12) __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            if (g >= 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
         // slice 1
@@ -251,8 +251,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
 #pragma unroll
         for (int g = 0; g < 16; ++g) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-            if (g >= 12) __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            if (g >= 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
         // the other stage is complete and this stage's reads are done
