@@ -36,7 +36,11 @@
 //    wavefront per SIMD share the rest.  Keeping codes in LDS and
 //    dequantizing per wavefront cuts LDS traffic four-fold but doubles the
 //    vector work, which lowers the clock under this load; measured, it was
-//    slower.
+//    slower.  Eight wavefronts of 128 x 64 (two per SIMD, with a prefetch
+//    two steps deep) measured no faster either.
+//  * The step loop runs two steps per iteration with the chunk registers
+//    swapping roles: a register copy of a chunk still being loaded would
+//    make every step wait for the loads it has just issued.
 //  * Loads are straight-line in the common case (K % 64 == 0, aligned): a
 //    row past the end of X or W reads the last row instead; it only feeds
 //    outputs that are never stored.
@@ -63,8 +67,9 @@ constexpr int kLdsStride = kBK + 8;  // halves per LDS row: 144 bytes
 
 // Codes (8 bytes per 16-element block) and scale bytes of one row's k-step:
 // four blocks.  Rows beyond `nrows` and blocks beyond K read as zero.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 struct RowChunk {
-    uint2 c[4];
+    u32x2 c[4];
     uint32_t s;
 };
 
@@ -87,22 +92,22 @@ __device__ __forceinline__ RowChunk load_chunk(const uint8_t* __restrict__ codes
         const uint4 v0 = *reinterpret_cast<const uint4*>(cp);
         const uint4 v1 = *reinterpret_cast<const uint4*>(cp + 16);
         r.s = *reinterpret_cast<const uint32_t*>(scales + rr * (K / 16) + k0 / 16);
-        r.c[0] = make_uint2(v0.x, v0.y);
-        r.c[1] = make_uint2(v0.z, v0.w);
-        r.c[2] = make_uint2(v1.x, v1.y);
-        r.c[3] = make_uint2(v1.z, v1.w);
+        r.c[0] = (u32x2){v0.x, v0.y};
+        r.c[1] = (u32x2){v0.z, v0.w};
+        r.c[2] = (u32x2){v1.x, v1.y};
+        r.c[3] = (u32x2){v1.z, v1.w};
         return r;
     }
     r.s = 0;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) r.c[b] = make_uint2(0, 0);
+    for (int b = 0; b < 4; ++b) r.c[b] = (u32x2){0u, 0u};
     if (row >= nrows) return r;
     const uint8_t* cp = codes + row * (K / 2) + k0 / 2;
     const uint8_t* sp = scales + row * (K / 16) + k0 / 16;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         if (k0 + 16 * b < K) {
-            r.c[b] = *reinterpret_cast<const uint2*>(cp + 8 * b);
+            r.c[b] = *reinterpret_cast<const u32x2*>(cp + 8 * b);
             r.s |= (uint32_t)sp[b] << (8 * b);
         }
     }
@@ -212,12 +217,15 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
     // other stage; after the barrier, slices 2 and 3 read the next step's
     // slices 0 and 1 from it.  Chunk s + 2 is loaded at the start of the
     // step (clamped to the last chunk so the code stays straight-line).
-    for (int64_t s = 0; s < nsteps; ++s) {
+    // The loop runs two steps per iteration with the chunk registers
+    // swapping roles (ra/rb dequantized while na/nb load, then the reverse),
+    // so no register copy waits for a load in flight.
+    auto step = [&](int64_t s, const RowChunk& ra, const RowChunk& rb, RowChunk& na, RowChunk& nb) {
         const _Float16* cur = lds[s & 1];
         _Float16* nxt = lds[(s + 1) & 1];
         const int64_t kn = (sb + (s + 2 < nsteps ? s + 2 : nsteps - 1)) * kBK;
-        const RowChunk na = load_chunk<FAST>(a.xc, a.xs, m0 + tid, a.M, a.K, kn);
-        const RowChunk nb = load_chunk<FAST>(a.wc, a.ws, n0 + tid, a.N, a.K, kn);
+        na = load_chunk<FAST>(a.xc, a.xs, m0 + tid, a.M, a.K, kn);
+        nb = load_chunk<FAST>(a.wc, a.ws, n0 + tid, a.N, a.K, kn);
         const f16x2 xa01 = scale_pair<false>(ra.s), xa23 = scale_pair<true>(ra.s);
         const f16x2 xb01 = scale_pair<false>(rb.s), xb23 = scale_pair<true>(rb.s);
         auto dequant = [&](int b) {
@@ -271,9 +279,14 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
         __builtin_amdgcn_sched_barrier(0);
-        ra = na;
-        rb = nb;
+    };
+    RowChunk na, nb;
+    int64_t s = 0;
+    for (; s + 1 < nsteps; s += 2) {
+        step(s, ra, rb, na, nb);
+        step(s + 1, na, nb, ra, rb);
     }
+    if (s < nsteps) step(s, ra, rb, na, nb);
 
     // epilogue: register r of lane l in a 32 x 32 tile holds row
     // 8*(r/4) + 4*(l/32) + r%4 and column l%32; Y = acc * (s2x[row] * s2w),
