@@ -65,9 +65,10 @@ constexpr int kWaveM = 128, kWaveN = 128;
 constexpr int kTilesM = kWaveM / 32, kTilesN = kWaveN / 32;
 constexpr int kLdsStride = kBK + 8;  // halves per LDS row: 144 bytes
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 // Codes (8 bytes per 16-element block) and scale bytes of one row's k-step:
 // four blocks.  Rows beyond `nrows` and blocks beyond K read as zero.
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 struct RowChunk {
     u32x2 c[4];
     uint32_t s;
