@@ -522,76 +522,76 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return v;
 }
 
-constexpr int kAmaxVecPerThread = 8;                                  // 16-byte vectors per lane per tile
-constexpr int64_t kAmaxTile = (int64_t)kThreads * kAmaxVecPerThread;  // vectors per tile (32 KB)
+constexpr int kAmaxVecPerThread = 4;                                  // 16-byte vectors per lane per tile
+constexpr int64_t kAmaxTile = (int64_t)kThreads * kAmaxVecPerThread;  // vectors per tile (16 KB)
 constexpr int64_t kAmaxGrid = 1024;                                   // workgroups per launch (at most)
 
 __device__ __forceinline__ u16x2 max_mag2(u16x2 acc, uint32_t v) {
     return __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2, v & 0x7FFF7FFFu));
 }
 
-// Combine the lanes' maxima of one tensor and fold them into its
-// accumulator.  Called by every thread of the workgroup (uniform control).
-__device__ __forceinline__ void amax_flush(u16x2 mx, uint32_t* acc, uint32_t* part) {
-    uint32_t mm = wave_max_u32(max((uint32_t)mx[0], (uint32_t)mx[1]));
-    const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) part[wave] = mm;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t r = part[0];
-#pragma unroll
-        for (int k = 1; k < kThreads / 64; ++k) r = max(r, part[k]);
-        atomicMax(acc, r << 16);
-    }
-    __syncthreads();
-}
-
-// Persistent reduction: workgroup g owns the contiguous tile range
-// [g*per, (g+1)*per) of the batch (tiles of all tensors laid end to end),
-// keeps a running maximum in registers, and flushes it (wave reduce, LDS,
-// one atomic max on the tensor's accumulator) only when its range moves on
-// to the next tensor and at the end.  The accumulator is the s2 slot itself,
-// holding the bits of a non-negative binary32 (the BF16 magnitude shifted
-// up); an integer atomic max orders such floats exactly.  Loads are
-// nontemporal: the weights are read once.
+// Grid-stride over the batch's 16 KB tiles laid end to end: workgroup g
+// takes tiles g, g + grid, ..., so the grid sweeps one window of memory at a
+// time (measured: 82 % of peak on the 8B set against 79 % for contiguous
+// per-workgroup ranges) and each workgroup meets the tensors in increasing
+// order.  A wavefront keeps its running maximum in registers and, leaving a
+// tensor, reduces it and parks it in LDS; at the end one thread per tensor
+// combines the four wavefronts and raises the tensor's accumulator -- the s2
+// slot itself, holding the bits of a non-negative binary32 (the BF16
+// magnitude shifted up), which an integer atomic max orders exactly.  The
+// accumulator is read first: it only grows, so any value read is a lower
+// bound, and the atomic is skipped when it cannot raise it (one atomic per
+// tile visit would serialize on the 32 addresses).  Loads are nontemporal:
+// the weights are read once.
 __global__ __launch_bounds__(kThreads) void k_amax(ScaleBatch bt, int64_t ntiles) {
-    __shared__ uint32_t part[kThreads / 64];
-    const int64_t per = (ntiles + gridDim.x - 1) / gridDim.x;
-    const int64_t lo = (int64_t)blockIdx.x * per;
-    const int64_t hi = lo + per < ntiles ? lo + per : ntiles;
-    if (lo >= hi) return;  // whole workgroup
-    int j = find_tensor(bt.tile_start, bt.n, lo);
-    u16x2 mx = {0, 0};
-    for (int64_t tile = lo; tile < hi; ++tile) {
-        if (tile >= bt.tile_start[j + 1]) {
-            amax_flush(mx, reinterpret_cast<uint32_t*>(bt.s2[j]), part);
-            mx = u16x2{0, 0};
-            j = find_tensor(bt.tile_start, bt.n, tile);
-        }
-        const uint16_t* __restrict__ w16 = bt.w[j];
-        const u32x4* __restrict__ w = reinterpret_cast<const u32x4*>(w16);
-        const int64_t numel = bt.numel[j];
-        const int64_t nvec = numel / 8;
-        const int64_t base = (tile - bt.tile_start[j]) * kAmaxTile + threadIdx.x;
-        u32x4 v[kAmaxVecPerThread];
+    constexpr int U = kAmaxVecPerThread;
+    constexpr int64_t kTV = kAmaxTile;
+    __shared__ uint32_t part[kThreads / 64][kBatch];
+    const int wave = threadIdx.x >> 6;
+    for (int j = threadIdx.x; j < (kThreads / 64) * kBatch; j += kThreads) (&part[0][0])[j] = 0;
+    __syncthreads();
+    int64_t tile = blockIdx.x;
+    if (tile < ntiles) {
+        int j = find_tensor(bt.tile_start, bt.n, tile);
+        u16x2 mx = {0, 0};
+        for (; tile < ntiles; tile += gridDim.x) {
+            if (tile >= bt.tile_start[j + 1]) {
+                part[wave][j] = wave_max_u32(max((uint32_t)mx[0], (uint32_t)mx[1])) << 16;
+                mx = u16x2{0, 0};
+                j = find_tensor(bt.tile_start, bt.n, tile);
+            }
+            const uint16_t* __restrict__ w16 = bt.w[j];
+            const u32x4* __restrict__ w = reinterpret_cast<const u32x4*>(w16);
+            const int64_t numel = bt.numel[j];
+            const int64_t nvec = numel / 8;
+            const int64_t base = (tile - bt.tile_start[j]) * kTV + threadIdx.x;
+            u32x4 v[U];
 #pragma unroll
-        for (int k = 0; k < kAmaxVecPerThread; ++k) {
-            const int64_t i = base + (int64_t)k * kThreads;
-            v[k] = i < nvec ? __builtin_nontemporal_load(w + i) : u32x4{0, 0, 0, 0};
-        }
+            for (int k = 0; k < U; ++k) {
+                const int64_t i = base + (int64_t)k * kThreads;
+                v[k] = i < nvec ? __builtin_nontemporal_load(w + i) : u32x4{0, 0, 0, 0};
+            }
 #pragma unroll
-        for (int k = 0; k < kAmaxVecPerThread; ++k)
-            mx = max_mag2(max_mag2(max_mag2(max_mag2(mx, v[k].x), v[k].y), v[k].z), v[k].w);
-        // the last numel % 8 elements: read one by one by the lane that would
-        // have loaded vector nvec
+            for (int k = 0; k < U; ++k)
+                mx = max_mag2(max_mag2(max_mag2(max_mag2(mx, v[k].x), v[k].y), v[k].z), v[k].w);
 #pragma unroll
-        for (int k = 0; k < kAmaxVecPerThread; ++k) {
-            if (base + (int64_t)k * kThreads == nvec) {
-                for (int64_t e = nvec * 8; e < numel; ++e) mx = max_mag2(mx, (uint32_t)w16[e]);
+            for (int k = 0; k < U; ++k) {
+                if (base + (int64_t)k * kThreads == nvec) {
+                    for (int64_t e = nvec * 8; e < numel; ++e) mx = max_mag2(mx, (uint32_t)w16[e]);
+                }
             }
         }
+        part[wave][j] = wave_max_u32(max((uint32_t)mx[0], (uint32_t)mx[1])) << 16;
     }
-    amax_flush(mx, reinterpret_cast<uint32_t*>(bt.s2[j]), part);
+    __syncthreads();
+    if (threadIdx.x < bt.n) {
+        const int j = threadIdx.x;
+        uint32_t m = part[0][j];
+#pragma unroll
+        for (int w = 1; w < kThreads / 64; ++w) m = max(m, part[w][j]);
+        uint32_t* acc = reinterpret_cast<uint32_t*>(bt.s2[j]);
+        if (m > __hip_atomic_load(acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(acc, m);
+    }
 }
 
 __global__ void k_finalize_s2(ScaleBatch bt) {
