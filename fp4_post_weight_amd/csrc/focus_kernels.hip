@@ -534,8 +534,10 @@ __device__ __forceinline__ u16x2 max_mag2(u16x2 acc, uint32_t v) {
 // takes tiles g, g + grid, ..., so the grid sweeps one window of memory at a
 // time (measured: 82 % of peak on the 8B set against 79 % for contiguous
 // per-workgroup ranges) and each workgroup meets the tensors in increasing
-// order.  A wavefront keeps its running maximum in registers and, leaving a
-// tensor, reduces it and parks it in LDS; at the end one thread per tensor
+// order (it walks the tensors in turn and computes its first tile in each,
+// so no tile searches for its tensor).  A wavefront keeps its running
+// maximum in registers and, leaving a tensor, reduces it and parks it in
+// LDS; at the end one thread per tensor
 // combines the four wavefronts and raises the tensor's accumulator -- the s2
 // slot itself, holding the bits of a non-negative binary32 (the BF16
 // magnitude shifted up), which an integer atomic max orders exactly.  The
@@ -543,28 +545,28 @@ __device__ __forceinline__ u16x2 max_mag2(u16x2 acc, uint32_t v) {
 // bound, and the atomic is skipped when it cannot raise it (one atomic per
 // tile visit would serialize on the 32 addresses).  Loads are nontemporal:
 // the weights are read once.
-__global__ __launch_bounds__(kThreads) void k_amax(ScaleBatch bt, int64_t ntiles) {
+__global__ __launch_bounds__(kThreads) void k_amax(ScaleBatch bt) {
     constexpr int U = kAmaxVecPerThread;
     constexpr int64_t kTV = kAmaxTile;
     __shared__ uint32_t part[kThreads / 64][kBatch];
     const int wave = threadIdx.x >> 6;
     for (int j = threadIdx.x; j < (kThreads / 64) * kBatch; j += kThreads) (&part[0][0])[j] = 0;
     __syncthreads();
-    int64_t tile = blockIdx.x;
-    if (tile < ntiles) {
-        int j = find_tensor(bt.tile_start, bt.n, tile);
+    // Workgroup g visits tiles g, g + grid, ... in increasing order, so the
+    // tile where its run in tensor j - 1 stops is its first tile in a later
+    // tensor: walking the tensors in turn, no tile searches for its tensor.
+    const int64_t grid = gridDim.x;
+    int64_t t = blockIdx.x;
+    for (int j = 0; j < bt.n; ++j) {
+        const int64_t t_lo = bt.tile_start[j], t_hi = bt.tile_start[j + 1];
+        if (t >= t_hi) continue;  // uniform per workgroup: no tile of tensor j here
+        const uint16_t* __restrict__ w16 = bt.w[j];
+        const u32x4* __restrict__ w = reinterpret_cast<const u32x4*>(w16);
+        const int64_t numel = bt.numel[j];
+        const int64_t nvec = numel / 8;
         u16x2 mx = {0, 0};
-        for (; tile < ntiles; tile += gridDim.x) {
-            if (tile >= bt.tile_start[j + 1]) {
-                part[wave][j] = wave_max_u32(max((uint32_t)mx[0], (uint32_t)mx[1])) << 16;
-                mx = u16x2{0, 0};
-                j = find_tensor(bt.tile_start, bt.n, tile);
-            }
-            const uint16_t* __restrict__ w16 = bt.w[j];
-            const u32x4* __restrict__ w = reinterpret_cast<const u32x4*>(w16);
-            const int64_t numel = bt.numel[j];
-            const int64_t nvec = numel / 8;
-            const int64_t base = (tile - bt.tile_start[j]) * kTV + threadIdx.x;
+        for (; t < t_hi; t += grid) {
+            const int64_t base = (t - t_lo) * kTV + threadIdx.x;
             u32x4 v[U];
 #pragma unroll
             for (int k = 0; k < U; ++k) {
@@ -574,6 +576,8 @@ __global__ __launch_bounds__(kThreads) void k_amax(ScaleBatch bt, int64_t ntiles
 #pragma unroll
             for (int k = 0; k < U; ++k)
                 mx = max_mag2(max_mag2(max_mag2(max_mag2(mx, v[k].x), v[k].y), v[k].z), v[k].w);
+            // the last numel % 8 elements, by the lane that would have loaded
+            // vector nvec
 #pragma unroll
             for (int k = 0; k < U; ++k) {
                 if (base + (int64_t)k * kThreads == nvec) {
@@ -703,7 +707,7 @@ hipError_t launch_tensor_scale(ScaleBatch& bt, hipStream_t stream) {
     bt.tile_start[bt.n] = t;
     const int64_t g = t < kAmaxGrid ? t : kAmaxGrid;
     hipLaunchKernelGGL(k_clear_acc, dim3(1), dim3(kBatch), 0, stream, bt);
-    hipLaunchKernelGGL(k_amax, dim3((unsigned)g), dim3(kThreads), 0, stream, bt, t);
+    hipLaunchKernelGGL(k_amax, dim3((unsigned)g), dim3(kThreads), 0, stream, bt);
     hipLaunchKernelGGL(k_finalize_s2, dim3(1), dim3(kBatch), 0, stream, bt);
     return hipGetLastError();
 }
