@@ -44,6 +44,11 @@
 //  * Loads are straight-line in the common case (K % 64 == 0, aligned): a
 //    row past the end of X or W reads the last row instead; it only feeds
 //    outputs that are never stored.
+//  * With few tokens the layer is bound by streaming W, and two kernels
+//    without LDS operand tiles take over: a decode kernel for M <= 16 on
+//    v_mfma_f32_16x16x32_f16 and a few-token kernel for M <= 64 on 32 x 32
+//    tiles.  When an output has too few columns to fill the GPU, the sum over
+//    k is split into ranges whose partials a finalize kernel adds in order.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -334,9 +339,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
 }
 
 // ---------------------------------------------------------------------------
-// Few tokens (M <= 64): every weight element is used by at most 64 outputs,
-// so the layer is bound by streaming W, and no operand needs sharing through
-// LDS.  A workgroup of 16 wavefronts owns 32 output columns (32 rows of W)
+// Few tokens (16 < M <= 64): every weight element is used by at most 64
+// outputs, so the layer is bound by streaming W, and no operand needs sharing
+// through LDS.  A workgroup of 16 wavefronts owns 32 output columns (32 rows of W)
 // and all M <= 32 * MT rows of X; the 64-wide k-steps are dealt round-robin
 // to its wavefronts (neighbouring wavefronts read neighbouring bytes of each
 // row), each accumulates a partial 32 x 32 tile per M-tile, and one LDS
@@ -491,6 +496,184 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void k_nvfp4_linear_skinny(GemmA
     }
 }
 
+// ---------------------------------------------------------------------------
+// Decode (M <= 16): v_mfma_f32_16x16x32_f16 fits 16 tokens without padding.
+// A workgroup of WAVES wavefronts owns 16 T output columns (16 T rows of W);
+// the 256-wide k-steps of its k range are dealt round-robin to its
+// wavefronts, each accumulates T partial 16 x 16 tiles (the dequantized X
+// fragment feeds all T), and one LDS reduction sums the WAVES partial tiles
+// in wavefront order (deterministic).
+//
+// Within a step the sum is order-free, so lane group g = lane / 16 takes k in
+// [64g, 64g + 64): 32 contiguous code bytes (blocks 4g..4g+3 of the step) and
+// their 4 contiguous scale bytes, and MFMA j (k-depth 32) takes dword j of
+// them in both operands.  A wavefront's two 16-byte loads per row cover the
+// row's whole 128-byte step; its scale load covers the step's 16 bytes.
+//
+// Measured on MI355X: the launch and load latency of a few-microsecond kernel
+// dominate, so the wavefronts keep one step in flight each and there are
+// many of them (8 per workgroup; 2 or 4 steps in flight per wavefront, or 16
+// wavefronts per workgroup, were slower), and T = 2 pays only where the
+// output still has a workgroup per CU with it (X is then read and
+// dequantized half as often).
+// ---------------------------------------------------------------------------
+
+constexpr int kGemvK = 256;          // k per step
+constexpr int64_t kGemvMaxM = 16;
+
+struct GemvChunk {
+    uint4 c0, c1;  // code bytes [32g, 32g + 32) of the row's step
+    uint32_t s;    // scale bytes of blocks 4g..4g+3, lower block first
+};
+
+// FAST: K % 256 == 0, codes 16-byte and scales 4-byte aligned; rows past
+// `nrows` read the last row (they feed only outputs that are never stored).
+// Otherwise rows past `nrows` and blocks past K read as zero.  (Measured on
+// MI355X: two 16-byte pieces 64 bytes apart per lane, which let each load
+// instruction cover 64 contiguous bytes of a row, and nontemporal loads of
+// W were both slower.)
+template <bool FAST>
+__device__ __forceinline__ GemvChunk load_gemv(const uint8_t* __restrict__ codes,
+                                               const uint8_t* __restrict__ scales, int64_t row,
+                                               int64_t nrows, int64_t K, int64_t k0, int g) {
+    GemvChunk r;
+    if (FAST) {
+        const int64_t rr = row < nrows ? row : nrows - 1;
+        const uint8_t* cp = codes + rr * (K / 2) + k0 / 2 + 32 * g;
+        r.c0 = *reinterpret_cast<const uint4*>(cp);
+        r.c1 = *reinterpret_cast<const uint4*>(cp + 16);
+        r.s = *reinterpret_cast<const uint32_t*>(scales + rr * (K / 16) + k0 / 16 + 4 * g);
+        return r;
+    }
+    r.c0 = make_uint4(0, 0, 0, 0);
+    r.c1 = make_uint4(0, 0, 0, 0);
+    r.s = 0;
+    if (row >= nrows) return r;
+    const uint8_t* cp = codes + row * (K / 2) + k0 / 2 + 32 * g;
+    const uint8_t* sp = scales + row * (K / 16) + k0 / 16 + 4 * g;
+    const int64_t kb = k0 + 64 * g;
+    uint2 v[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        v[b] = make_uint2(0, 0);
+        if (kb + 16 * b < K) {
+            v[b] = *reinterpret_cast<const uint2*>(cp + 8 * b);
+            r.s |= (uint32_t)sp[b] << (8 * b);
+        }
+    }
+    r.c0 = make_uint4(v[0].x, v[0].y, v[1].x, v[1].y);
+    r.c1 = make_uint4(v[2].x, v[2].y, v[3].x, v[3].y);
+    return r;
+}
+
+__device__ __forceinline__ uint32_t gemv_dword(const GemvChunk& c, int j) {
+    return j < 4 ? dword_of(c.c0, j) : dword_of(c.c1, j - 4);
+}
+
+template <bool FAST, bool BF16_OUT, int WAVES, int T, int D>
+__global__ __launch_bounds__(64 * WAVES) void k_nvfp4_linear_gemv(GemmArgs a) {
+    __shared__ float red[WAVES][T * 16 * 16];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int c16 = lane & 15, g = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * (16 * T);
+    const int64_t nsteps_all = (a.K + kGemvK - 1) / kGemvK;
+    const int64_t sb = (int64_t)blockIdx.y * a.kchunk;
+    const int64_t se = sb + a.kchunk < nsteps_all ? sb + a.kchunk : nsteps_all;
+    const int64_t nsteps = se > sb ? se - sb : 0;
+
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    f32x4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = (f32x4){};
+
+    auto load = [&](int64_t s, GemvChunk (&w)[T], GemvChunk& x) {  // s: step within the range
+        const int64_t k0 = (sb + (s < nsteps ? s : nsteps - 1)) * kGemvK;
+#pragma unroll
+        for (int t = 0; t < T; ++t) w[t] = load_gemv<FAST>(a.wc, a.ws, n0 + 16 * t + c16, a.N, a.K, k0, g);
+        x = load_gemv<FAST>(a.xc, a.xs, c16, a.M, a.K, k0, g);
+    };
+    auto compute = [&](const GemvChunk (&w)[T], const GemvChunk& x) {
+        const f16x2 x01 = scale_pair<false>(x.s), x23 = scale_pair<true>(x.s);
+        f16x2 w01[T], w23[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            w01[t] = scale_pair<false>(w[t].s);
+            w23[t] = scale_pair<true>(w[t].s);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const f16x8 fa = codes_times(gemv_dword(x, j), block_scale(x01, x23, j >> 1));
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const f16x8 fb = codes_times(gemv_dword(w[t], j), block_scale(w01[t], w23[t], j >> 1));
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb, acc[t], 0, 0, 0);
+            }
+        }
+    };
+    // this wavefront's steps: wave + WAVES i for i < my, D in flight in
+    // static slots; a slot is refilled only while at least D more steps
+    // remain, so the loads stay straight-line and none is wasted except in
+    // the one partial refill of a count that is not a multiple of D (and in
+    // the first fill when my < D)
+    if (nsteps > 0) {
+        const int64_t my = wave < nsteps ? (nsteps - wave + WAVES - 1) / WAVES : 0;
+        GemvChunk w[D][T], x[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) load(wave + (int64_t)WAVES * d, w[d], x[d]);
+        int64_t i = 0;
+        for (; i + 2 * D <= my; i += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                compute(w[d], x[d]);
+                load(wave + (int64_t)WAVES * (i + D + d), w[d], x[d]);
+            }
+        }
+        const int64_t rest = my - i;  // 0 .. 2D - 1
+        if (rest > D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                compute(w[d], x[d]);
+                load(wave + (int64_t)WAVES * (i + D + d), w[d], x[d]);
+            }
+#pragma unroll
+            for (int d = 0; d < D - 1; ++d)
+                if (rest > D + d) compute(w[d], x[d]);
+        } else {
+#pragma unroll
+            for (int d = 0; d < D; ++d)
+                if (rest > d) compute(w[d], x[d]);
+        }
+    }
+
+    // register r of lane l in tile t: token 4 (l / 16) + r, column 16 t + l % 16
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][t * 256 + (4 * g + r) * 16 + c16] = acc[t][r];
+    __syncthreads();
+    for (int e = tid; e < T * 256; e += 64 * WAVES) {
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) v += red[w][e];
+        const int64_t row = (e >> 4) & 15, col = n0 + 16 * (e >> 8) + (e & 15);
+        if (row < a.M && col < a.N) {
+            if (a.ksplit > 1) {
+                a.part[((int64_t)blockIdx.y * a.M + row) * a.N + col] = v;
+            } else {
+                const float y = v * (a.xs2[a.xs2_per_row ? row : 0] * a.ws2[0]);
+                if (BF16_OUT) {
+                    const uint32_t p = bf16_pair(y, 0.0f);
+                    reinterpret_cast<uint16_t*>(a.y)[row * a.N + col] = (uint16_t)(p & 0xFFFFu);
+                } else {
+                    reinterpret_cast<float*>(a.y)[row * a.N + col] = y;
+                }
+            }
+        }
+    }
+}
+
 // Split sums: Y = (sum over the k ranges, in order, of the partials) *
 // (s2x[row] * s2w).  VEC: four consecutive outputs per thread with 16-byte
 // loads of each partial (M * N % 4 == 0, workspace 16-byte and Y 8- or
@@ -542,19 +725,21 @@ __global__ __launch_bounds__(256) void k_nvfp4_linear_finalize(GemmArgs a) {
 
 }  // namespace
 
-// Up to this many rows of X the few-token kernel is used.
+// Up to this many rows of X the few-token kernel is used (the decode kernel
+// up to kGemvMaxM rows).
 constexpr int64_t kSkinnyMaxM = 64;
 
-
-// Splitting the sum over k.  Each workgroup of either kernel occupies one CU,
-// so a launch of W workgroups runs ceil(W / CUs) rounds.  Splitting k into s
-// ranges multiplies the workgroups by s and divides each one's steps by s,
-// and costs s * M * N * 8 bytes of partial traffic (FP32 written, then read by
-// the finalize kernel) plus a launch.  The split count minimises
+// Splitting the sum over k.  A launch of W workgroups of the tiled or
+// few-token kernel runs ceil(W / CUs) rounds (each such workgroup occupies a
+// CU).  Splitting k into s ranges multiplies the workgroups by s and divides
+// each one's steps by s, and costs s * M * N * 8 bytes of partial traffic
+// (FP32 written, then read by the finalize kernel) plus a launch.  The split
+// count minimises
 //   rounds * (steps per range * t_step + t_round) + partial bytes / bandwidth,
 // with per-step and per-round times measured on MI355X for each kernel.  A
 // range keeps at least kMinSplitSteps steps (tiled kernel) or one step per
-// wavefront (few-token kernel).
+// wavefront (few-token kernel).  The decode kernel's model is its own (in
+// nvfp4_linear_splits): its workgroups are small and all resident at once.
 constexpr int64_t kMinSplitSteps = 4;
 
 static int device_cus() {
@@ -565,19 +750,64 @@ static int device_cus() {
     return cus;
 }
 
+// Decode launch configuration for an output of N columns and `steps`
+// 256-wide k-steps per k range: 16-column tiles per wavefront (2 when that
+// still leaves a workgroup per CU) and wavefronts per workgroup (8, or 4 for
+// fewer than 8 steps).  Each wavefront keeps one step in flight: measured on
+// MI355X, more wavefronts hide the load latency better than deeper
+// per-wavefront prefetch (2 or 4 slots) at the same register budget.
+struct GemvConfig {
+    int t, waves;
+};
+
+static GemvConfig gemv_config(int64_t N, int64_t steps, int64_t cus) {
+    GemvConfig c;
+    c.t = (N + 31) / 32 >= cus ? 2 : 1;
+    c.waves = steps >= 8 ? 8 : 4;
+    return c;
+}
+
 int64_t nvfp4_linear_splits(int64_t M, int64_t N, int64_t K, int64_t part_bytes) {
     const int64_t wgs = nvfp4_linear_workgroups(M, N);
-    const int64_t nsteps = (K + kBK - 1) / kBK;
+    const bool gemv = M <= kGemvMaxM;
+    const int64_t nsteps = gemv ? (K + kGemvK - 1) / kGemvK : (K + kBK - 1) / kBK;
     if (wgs <= 0 || nsteps == 0) return 1;
+    const int64_t cus = device_cus();
+    const int64_t per = M * N * 4;
+    const double t_split = 4.0e-6;  // finalize launch
+    const double bw = 5.0e12;       // B/s for the partials
+    if (gemv) {
+        // decode: a range of c steps on a workgroup of w wavefronts takes
+        // ceil(c / w) rounds of one step per wavefront, each bound by the
+        // load latency or by the grid's W bytes at the streaming rate, plus
+        // a fixed cost per launch
+        const double t_lat = 1.2e-6, t_fix = 2.5e-6, bw_w = 4.0e12;
+        const GemvConfig c1 = gemv_config(N, nsteps, cus);
+        const double wave_bytes = 16.0 * c1.t * (kGemvK / 2 + kGemvK / 16);  // W per wavefront-step
+        int64_t smax = nsteps / 4;
+        if (per > 0 && smax > part_bytes / per) smax = part_bytes / per;
+        int64_t best = 1;
+        double best_t = 0.0;
+        for (int64_t s = 1; s <= smax || s == 1; ++s) {
+            const int64_t chunk = (nsteps + s - 1) / s;
+            const int64_t se = (nsteps + chunk - 1) / chunk;
+            const int64_t w = gemv_config(N, chunk, cus).waves;
+            const double round = (double)(wgs * se * w) * wave_bytes / bw_w;
+            double t = (double)((chunk + w - 1) / w) * (round > t_lat ? round : t_lat) + t_fix;
+            if (se > 1) t += (double)se * (double)M * (double)N * 8.0 / bw + t_split;
+            if (s == 1 || t < best_t) {
+                best_t = t;
+                best = se;
+            }
+            if (wgs * se >= cus) break;  // more ranges only add partial traffic
+        }
+        return best;
+    }
+    if (wgs >= cus) return 1;
     const bool skinny = M <= kSkinnyMaxM;
     const double t_step = skinny ? 0.16e-6 : 2.3e-6;   // s per 64-wide k-step of one workgroup
     const double t_round = skinny ? 4.0e-6 : 3.0e-6;   // s of fixed cost per round
-    const double t_split = 4.0e-6;                      // finalize launch
-    const double bw = 5.0e12;                           // B/s for the partials
-    const int64_t cus = device_cus();
-    if (wgs >= cus) return 1;
     int64_t smax = nsteps / (skinny ? kSkinnyWaves : kMinSplitSteps);
-    const int64_t per = M * N * 4;
     if (per > 0 && smax > part_bytes / per) smax = part_bytes / per;
     int64_t best = 1;
     double best_t = 0.0;
@@ -598,11 +828,33 @@ int64_t nvfp4_linear_splits(int64_t M, int64_t N, int64_t K, int64_t part_bytes)
 
 hipError_t launch_nvfp4_linear(const GemmArgs& args, bool fast, bool bf16_out, hipStream_t stream) {
     GemmArgs a = args;
-    const int64_t nsteps = (a.K + kBK - 1) / kBK;
+    const bool gemv = a.M <= kGemvMaxM;
+    const int64_t nsteps = gemv ? (a.K + kGemvK - 1) / kGemvK : (a.K + kBK - 1) / kBK;
     a.ksplit = a.part ? nvfp4_linear_splits(a.M, a.N, a.K, a.part_bytes) : 1;
     a.kchunk = a.ksplit > 1 ? (nsteps + a.ksplit - 1) / a.ksplit : (nsteps > 0 ? nsteps : 1);
     const unsigned splits = (unsigned)a.ksplit;
-    if (a.M <= kSkinnyMaxM) {
+    if (gemv) {
+        const bool f = fast && a.K % kGemvK == 0;
+        const GemvConfig c = gemv_config(a.N, a.kchunk, device_cus());
+        const int64_t wgs = (a.N + 16 * c.t - 1) / (16 * c.t);
+        const dim3 grid((unsigned)wgs, splits), block(64 * c.waves);
+        const int cfg = c.t * 16 + c.waves;
+#define FOCUS_GV(F, B)                                                                                      \
+    do {                                                                                                    \
+        if (cfg == 0x18) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 8, 1, 1>), grid, block, 0, stream, a); \
+        else if (cfg == 0x14) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 4, 1, 1>), grid, block, 0, stream, a); \
+        else if (cfg == 0x28) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 8, 2, 1>), grid, block, 0, stream, a); \
+        else hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 4, 2, 1>), grid, block, 0, stream, a);             \
+    } while (0)
+        if (f) {
+            if (bf16_out) FOCUS_GV(true, true);
+            else FOCUS_GV(true, false);
+        } else {
+            if (bf16_out) FOCUS_GV(false, true);
+            else FOCUS_GV(false, false);
+        }
+#undef FOCUS_GV
+    } else if (a.M <= kSkinnyMaxM) {
         const dim3 grid((unsigned)((a.N + 31) / 32), splits), block(64 * kSkinnyWaves);
 #define FOCUS_SK(F, B)                                                                                 \
     do {                                                                                               \
@@ -647,6 +899,10 @@ hipError_t launch_nvfp4_linear(const GemmArgs& args, bool fast, bool bf16_out, h
 }
 
 int64_t nvfp4_linear_workgroups(int64_t M, int64_t N) {
+    if (M <= kGemvMaxM) {
+        const int t = gemv_config(N, 1, device_cus()).t;
+        return (N + 16 * t - 1) / (16 * t);
+    }
     if (M <= kSkinnyMaxM) return (N + 31) / 32;
     return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
 }

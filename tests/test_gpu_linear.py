@@ -94,9 +94,11 @@ def test_exact_when_partial_sums_are_exact(focus, orc, M):
     assert np.array_equal(y16, want)
 
 
-# M <= 64 takes the few-token kernel (one or two 32-row tiles of X), larger M
-# the tiled kernel; K % 64 != 0 takes the masked loads.
-SHAPES = [(1, 1, 16), (7, 33, 48), (16, 200, 1040), (16, 4096, 4096), (17, 64, 64), (32, 4096, 4096), (33, 1000, 1040), (64, 512, 8192), (64, 300, 14336),
+# M <= 16 takes the decode kernel (K % 256 != 0: masked loads), M <= 64 the
+# few-token kernel (one or two 32-row tiles of X), larger M the tiled kernel
+# (K % 64 != 0: masked loads); some shapes split k.
+SHAPES = [(1, 1, 16), (3, 17, 256), (7, 33, 48), (12, 4111, 320), (16, 200, 1040), (16, 4096, 4096),
+          (5, 1000, 28672), (16, 1024, 28688), (1, 14336, 512), (3, 8200, 80), (17, 64, 64), (32, 4096, 4096), (33, 1000, 1040), (64, 512, 8192), (64, 300, 14336),
           (65, 130, 192), (255, 257, 64), (257, 255, 1040), (300, 520, 4096), (513, 96, 80)]
 
 
