@@ -44,11 +44,11 @@
 //  * Loads are straight-line in the common case (K % 64 == 0, aligned): a
 //    row past the end of X or W reads the last row instead; it only feeds
 //    outputs that are never stored.
-//  * With few tokens the layer is bound by streaming W, and two kernels
-//    without LDS operand tiles take over: a decode kernel for M <= 16 on
-//    v_mfma_f32_16x16x32_f16 and a few-token kernel for M <= 64 on 32 x 32
-//    tiles.  When an output has too few columns to fill the GPU, the sum over
-//    k is split into ranges whose partials a finalize kernel adds in order.
+//  * With few tokens (M <= 64) the layer is bound by streaming W, and a
+//    decode kernel without LDS operand tiles takes over
+//    (v_mfma_f32_16x16x32_f16, one to four 16-token tiles).  When an output
+//    has too few columns to fill the GPU, the sum over k is split into ranges
+//    whose partials a finalize kernel adds in order.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -339,170 +339,15 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
 }
 
 // ---------------------------------------------------------------------------
-// Few tokens (16 < M <= 64): every weight element is used by at most 64
-// outputs, so the layer is bound by streaming W, and no operand needs sharing
-// through LDS.  A workgroup of 16 wavefronts owns 32 output columns (32 rows of W)
-// and all M <= 32 * MT rows of X; the 64-wide k-steps are dealt round-robin
-// to its wavefronts (neighbouring wavefronts read neighbouring bytes of each
-// row), each accumulates a partial 32 x 32 tile per M-tile, and one LDS
-// reduction sums the 16 partial tiles (deterministic, no workspace).
-//
-// Within a k-step the sum is order-free, so lane group h = lane / 32 takes
-// k in [32h, 32h + 32): one 16-byte load per row and step, and slice kk (one
-// MFMA k-depth of 16) is dword kk of it in both operands.
-// ---------------------------------------------------------------------------
-
-constexpr int kSkinnyWaves = 16;
-
-// A lane's share of one row and k-step: 16 bytes of codes (32 elements,
-// blocks 2h and 2h+1 of the step) and their two scale bytes (bits 0-7 and
-// 8-15).  Rows past `nrows` read the last row (FAST) or zeros; k past K reads
-// zeros.
-struct LaneChunk {
-    uint4 c;
-    uint32_t s;
-};
-
-template <bool FAST>
-__device__ __forceinline__ LaneChunk load_lane(const uint8_t* __restrict__ codes,
-                                               const uint8_t* __restrict__ scales, int64_t row,
-                                               int64_t nrows, int64_t K, int64_t k0, int h) {
-    LaneChunk r;
-    if (FAST) {
-        const int64_t rr = row < nrows ? row : nrows - 1;
-        r.c = *reinterpret_cast<const uint4*>(codes + rr * (K / 2) + k0 / 2 + 16 * h);
-        r.s = *reinterpret_cast<const uint16_t*>(scales + rr * (K / 16) + k0 / 16 + 2 * h);
-        return r;
-    }
-    r.c = make_uint4(0, 0, 0, 0);
-    r.s = 0;
-    if (row >= nrows || k0 < 0) return r;
-    const uint8_t* cp = codes + row * (K / 2) + k0 / 2 + 16 * h;
-    const uint8_t* sp = scales + row * (K / 16) + k0 / 16 + 2 * h;
-    const int64_t kb = k0 + 32 * h;
-    if (kb < K) {
-        const uint2 v = *reinterpret_cast<const uint2*>(cp);
-        r.c.x = v.x;
-        r.c.y = v.y;
-        r.s = sp[0];
-    }
-    if (kb + 16 < K) {
-        const uint2 v = *reinterpret_cast<const uint2*>(cp + 8);
-        r.c.z = v.x;
-        r.c.w = v.y;
-        r.s |= (uint32_t)sp[1] << 8;
-    }
-    return r;
-}
-
-__device__ __forceinline__ uint32_t dword_of(const uint4& v, int kk) {
-    return kk == 0 ? v.x : kk == 1 ? v.y : kk == 2 ? v.z : v.w;
-}
-
-template <bool FAST, bool BF16_OUT, int MT>
-__global__ __launch_bounds__(64 * kSkinnyWaves) void k_nvfp4_linear_skinny(GemmArgs a) {
-    __shared__ float red[kSkinnyWaves][MT * 32 * 32];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int r32 = lane & 31, h = lane >> 5;
-    const int64_t n0 = (int64_t)blockIdx.x * 32;
-    // this workgroup's range of 64-wide k-steps [sb, se)
-    const int64_t nsteps_all = (a.K + kBK - 1) / kBK;
-    const int64_t sb = (int64_t)blockIdx.y * a.kchunk;
-    const int64_t se = sb + a.kchunk < nsteps_all ? sb + a.kchunk : nsteps_all;
-    const int64_t nsteps = se > sb ? se - sb : 0;
-
-    f32x16 acc[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = (f32x16){};
-
-    auto load = [&](int64_t s, LaneChunk& w, LaneChunk (&x)[MT]) {  // s: step within the range
-        const int64_t k0 = (sb + (s < nsteps ? s : nsteps - 1)) * kBK;
-        w = load_lane<FAST>(a.wc, a.ws, n0 + r32, a.N, a.K, k0, h);
-#pragma unroll
-        for (int t = 0; t < MT; ++t) x[t] = load_lane<FAST>(a.xc, a.xs, 32 * t + r32, a.M, a.K, k0, h);
-    };
-    auto compute = [&](const LaneChunk& w, const LaneChunk (&x)[MT]) {
-        // scales of blocks 2h and 2h + 1 (bits 0-15 of s)
-        const f16x2 pw = scale_pair<false>(w.s);
-        f16x2 px[MT];
-#pragma unroll
-        for (int t = 0; t < MT; ++t) px[t] = scale_pair<false>(x[t].s);
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int kk = 2 * half + q;
-                const f16x8 fb = codes_times(dword_of(w.c, kk), half ? pw.y : pw.x);
-#pragma unroll
-                for (int t = 0; t < MT; ++t) {
-                    const f16x8 fa = codes_times(dword_of(x[t].c, kk), half ? px[t].y : px[t].x);
-                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, fb, acc[t], 0, 0, 0);
-                }
-            }
-        }
-    };
-    // this wavefront's steps: wave + 16 i for i < my; four in flight in
-    // static slots, refilled four steps ahead in full rounds (straight-line,
-    // so the load counters are exact); the last 0-3 steps need no refill
-    if (nsteps > 0) {  // K == 0: nothing to load (and no step to clamp to)
-        const int64_t my = wave < nsteps ? (nsteps - wave + kSkinnyWaves - 1) / kSkinnyWaves : 0;
-        LaneChunk w[4], x[4][MT];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) load(wave + (int64_t)kSkinnyWaves * d, w[d], x[d]);
-        int64_t i = 0;
-        for (; i + 4 <= my; i += 4) {
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                compute(w[d], x[d]);
-                load(wave + (int64_t)kSkinnyWaves * (i + 4 + d), w[d], x[d]);
-            }
-        }
-        const int64_t rest = my - i;
-        if (rest > 0) compute(w[0], x[0]);
-        if (rest > 1) compute(w[1], x[1]);
-        if (rest > 2) compute(w[2], x[2]);
-    }
-
-    // partial tiles to LDS (register r of lane l: row 8*(r/4) + 4*(l/32) +
-    // r%4, column l%32), then one thread per output sums the 16 wavefronts
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-            red[wave][row * 32 + r32] = acc[t][r];
-        }
-    __syncthreads();
-    const float s2w = a.ws2[0];
-#pragma unroll
-    for (int e = tid; e < MT * 32 * 32; e += 64 * kSkinnyWaves) {
-        float v = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kSkinnyWaves; ++w) v += red[w][e];
-        const int64_t row = e >> 5, col = n0 + (e & 31);
-        if (a.ksplit > 1) {  // unscaled partial of k range blockIdx.y
-            if (row < a.M && col < a.N) a.part[((int64_t)blockIdx.y * a.M + row) * a.N + col] = v;
-        } else if (row < a.M && col < a.N) {
-            const float y = v * (a.xs2[a.xs2_per_row ? row : 0] * s2w);
-            if (BF16_OUT) {
-                const uint32_t p = bf16_pair(y, 0.0f);
-                reinterpret_cast<uint16_t*>(a.y)[row * a.N + col] = (uint16_t)(p & 0xFFFFu);
-            } else {
-                reinterpret_cast<float*>(a.y)[row * a.N + col] = y;
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Decode (M <= 16): v_mfma_f32_16x16x32_f16 fits 16 tokens without padding.
-// A workgroup of WAVES wavefronts owns 16 T output columns (16 T rows of W);
+// Decode (M <= 64): v_mfma_f32_16x16x32_f16 on MT = 1, 2 or 4 tiles of 16
+// tokens (every weight element feeds at most 64 outputs, so the layer is
+// bound by streaming W and no operand needs sharing through LDS).  A
+// workgroup of WAVES wavefronts owns 16 T output columns (16 T rows of W);
 // the 256-wide k-steps of its k range are dealt round-robin to its
-// wavefronts, each accumulates T partial 16 x 16 tiles (the dequantized X
-// fragment feeds all T), and one LDS reduction sums the WAVES partial tiles
-// in wavefront order (deterministic).
+// wavefronts, each accumulates MT x T partial 16 x 16 tiles (a dequantized W
+// fragment feeds all MT token tiles, an X fragment all T column tiles), and
+// one LDS reduction sums the WAVES partial tiles in wavefront order
+// (deterministic).
 //
 // Within a step the sum is order-free, so lane group g = lane / 16 takes k in
 // [64g, 64g + 64): 32 contiguous code bytes (blocks 4g..4g+3 of the step) and
@@ -515,11 +360,13 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void k_nvfp4_linear_skinny(GemmA
 // many of them (8 per workgroup; 2 or 4 steps in flight per wavefront, or 16
 // wavefronts per workgroup, were slower), and T = 2 pays only where the
 // output still has a workgroup per CU with it (X is then read and
-// dequantized half as often).
+// dequantized half as often).  Against 32 x 32 tiles with four steps in
+// flight per wavefront (its predecessor for 16 < M <= 64), 17 to 64 tokens
+// through the Llama-3.1-8B layer shapes took 36-72 us instead of 58-96 us.
 // ---------------------------------------------------------------------------
 
 constexpr int kGemvK = 256;          // k per step
-constexpr int64_t kGemvMaxM = 16;
+constexpr int64_t kGemvMaxM = 64;
 
 struct GemvChunk {
     uint4 c0, c1;  // code bytes [32g, 32g + 32) of the row's step
@@ -566,13 +413,17 @@ __device__ __forceinline__ GemvChunk load_gemv(const uint8_t* __restrict__ codes
     return r;
 }
 
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int kk) {
+    return kk == 0 ? v.x : kk == 1 ? v.y : kk == 2 ? v.z : v.w;
+}
+
 __device__ __forceinline__ uint32_t gemv_dword(const GemvChunk& c, int j) {
     return j < 4 ? dword_of(c.c0, j) : dword_of(c.c1, j - 4);
 }
 
-template <bool FAST, bool BF16_OUT, int WAVES, int T, int D>
+template <bool FAST, bool BF16_OUT, int WAVES, int T, int MT>
 __global__ __launch_bounds__(64 * WAVES) void k_nvfp4_linear_gemv(GemmArgs a) {
-    __shared__ float red[WAVES][T * 16 * 16];
+    __shared__ float red[WAVES][MT * T * 16 * 16];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -584,80 +435,64 @@ __global__ __launch_bounds__(64 * WAVES) void k_nvfp4_linear_gemv(GemmArgs a) {
     const int64_t nsteps = se > sb ? se - sb : 0;
 
     typedef float f32x4 __attribute__((ext_vector_type(4)));
-    f32x4 acc[T];
+    f32x4 acc[MT][T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) acc[t] = (f32x4){};
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int t = 0; t < T; ++t) acc[m][t] = (f32x4){};
 
-    auto load = [&](int64_t s, GemvChunk (&w)[T], GemvChunk& x) {  // s: step within the range
-        const int64_t k0 = (sb + (s < nsteps ? s : nsteps - 1)) * kGemvK;
+    // this wavefront's steps: wave + WAVES i for i < my, one in flight
+    const int64_t my = wave < nsteps ? (nsteps - wave + WAVES - 1) / WAVES : 0;
+    if (my > 0) {
+        GemvChunk w[T], x[MT];
+        for (int64_t i = 0; i < my; ++i) {
+            const int64_t k0 = (sb + wave + (int64_t)WAVES * i) * kGemvK;
 #pragma unroll
-        for (int t = 0; t < T; ++t) w[t] = load_gemv<FAST>(a.wc, a.ws, n0 + 16 * t + c16, a.N, a.K, k0, g);
-        x = load_gemv<FAST>(a.xc, a.xs, c16, a.M, a.K, k0, g);
-    };
-    auto compute = [&](const GemvChunk (&w)[T], const GemvChunk& x) {
-        const f16x2 x01 = scale_pair<false>(x.s), x23 = scale_pair<true>(x.s);
-        f16x2 w01[T], w23[T];
+            for (int t = 0; t < T; ++t) w[t] = load_gemv<FAST>(a.wc, a.ws, n0 + 16 * t + c16, a.N, a.K, k0, g);
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            w01[t] = scale_pair<false>(w[t].s);
-            w23[t] = scale_pair<true>(w[t].s);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const f16x8 fa = codes_times(gemv_dword(x, j), block_scale(x01, x23, j >> 1));
+            for (int m = 0; m < MT; ++m) x[m] = load_gemv<FAST>(a.xc, a.xs, 16 * m + c16, a.M, a.K, k0, g);
+            f16x2 w01[T], w23[T], x01[MT], x23[MT];
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                const f16x8 fb = codes_times(gemv_dword(w[t], j), block_scale(w01[t], w23[t], j >> 1));
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa, fb, acc[t], 0, 0, 0);
-            }
-        }
-    };
-    // this wavefront's steps: wave + WAVES i for i < my, D in flight in
-    // static slots; a slot is refilled only while at least D more steps
-    // remain, so the loads stay straight-line and none is wasted except in
-    // the one partial refill of a count that is not a multiple of D (and in
-    // the first fill when my < D)
-    if (nsteps > 0) {
-        const int64_t my = wave < nsteps ? (nsteps - wave + WAVES - 1) / WAVES : 0;
-        GemvChunk w[D][T], x[D];
-#pragma unroll
-        for (int d = 0; d < D; ++d) load(wave + (int64_t)WAVES * d, w[d], x[d]);
-        int64_t i = 0;
-        for (; i + 2 * D <= my; i += D) {
-#pragma unroll
-            for (int d = 0; d < D; ++d) {
-                compute(w[d], x[d]);
-                load(wave + (int64_t)WAVES * (i + D + d), w[d], x[d]);
-            }
-        }
-        const int64_t rest = my - i;  // 0 .. 2D - 1
-        if (rest > D) {
-#pragma unroll
-            for (int d = 0; d < D; ++d) {
-                compute(w[d], x[d]);
-                load(wave + (int64_t)WAVES * (i + D + d), w[d], x[d]);
+                w01[t] = scale_pair<false>(w[t].s);
+                w23[t] = scale_pair<true>(w[t].s);
             }
 #pragma unroll
-            for (int d = 0; d < D - 1; ++d)
-                if (rest > D + d) compute(w[d], x[d]);
-        } else {
+            for (int m = 0; m < MT; ++m) {
+                x01[m] = scale_pair<false>(x[m].s);
+                x23[m] = scale_pair<true>(x[m].s);
+            }
 #pragma unroll
-            for (int d = 0; d < D; ++d)
-                if (rest > d) compute(w[d], x[d]);
+            for (int j = 0; j < 8; ++j) {
+                f16x8 fa[MT];
+#pragma unroll
+                for (int m = 0; m < MT; ++m) fa[m] = codes_times(gemv_dword(x[m], j), block_scale(x01[m], x23[m], j >> 1));
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const f16x8 fb = codes_times(gemv_dword(w[t], j), block_scale(w01[t], w23[t], j >> 1));
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+                        acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[m], fb, acc[m][t], 0, 0, 0);
+                }
+            }
         }
     }
 
-    // register r of lane l in tile t: token 4 (l / 16) + r, column 16 t + l % 16
+    // register r of lane l in tile (m, t): token 16 m + 4 (l / 16) + r,
+    // column 16 t + l % 16; red holds (m, t, token % 16, column % 16)
 #pragma unroll
-    for (int t = 0; t < T; ++t)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][t * 256 + (4 * g + r) * 16 + c16] = acc[t][r];
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][((m * T + t) * 16 + 4 * g + r) * 16 + c16] = acc[m][t][r];
     __syncthreads();
-    for (int e = tid; e < T * 256; e += 64 * WAVES) {
+    for (int e = tid; e < MT * T * 256; e += 64 * WAVES) {
         float v = 0.0f;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) v += red[w][e];
-        const int64_t row = (e >> 4) & 15, col = n0 + 16 * (e >> 8) + (e & 15);
+        const int mt = e >> 8;
+        const int64_t row = 16 * (mt / T) + ((e >> 4) & 15), col = n0 + 16 * (mt % T) + (e & 15);
         if (row < a.M && col < a.N) {
             if (a.ksplit > 1) {
                 a.part[((int64_t)blockIdx.y * a.M + row) * a.N + col] = v;
@@ -725,20 +560,14 @@ __global__ __launch_bounds__(256) void k_nvfp4_linear_finalize(GemmArgs a) {
 
 }  // namespace
 
-// Up to this many rows of X the few-token kernel is used (the decode kernel
-// up to kGemvMaxM rows).
-constexpr int64_t kSkinnyMaxM = 64;
-
-// Splitting the sum over k.  A launch of W workgroups of the tiled or
-// few-token kernel runs ceil(W / CUs) rounds (each such workgroup occupies a
-// CU).  Splitting k into s ranges multiplies the workgroups by s and divides
-// each one's steps by s, and costs s * M * N * 8 bytes of partial traffic
-// (FP32 written, then read by the finalize kernel) plus a launch.  The split
-// count minimises
+// Splitting the sum over k.  A launch of W workgroups of the tiled kernel
+// runs ceil(W / CUs) rounds (each workgroup occupies a CU).  Splitting k into
+// s ranges multiplies the workgroups by s and divides each one's steps by s,
+// and costs s * M * N * 8 bytes of partial traffic (FP32 written, then read
+// by the finalize kernel) plus a launch.  The split count minimises
 //   rounds * (steps per range * t_step + t_round) + partial bytes / bandwidth,
-// with per-step and per-round times measured on MI355X for each kernel.  A
-// range keeps at least kMinSplitSteps steps (tiled kernel) or one step per
-// wavefront (few-token kernel).  The decode kernel's model is its own (in
+// with the per-step and per-round times measured on MI355X; a range keeps at
+// least kMinSplitSteps steps.  The decode kernel's model is its own (in
 // nvfp4_linear_splits): its workgroups are small and all resident at once.
 constexpr int64_t kMinSplitSteps = 4;
 
@@ -750,20 +579,20 @@ static int device_cus() {
     return cus;
 }
 
-// Decode launch configuration for an output of N columns and `steps`
-// 256-wide k-steps per k range: 16-column tiles per wavefront (2 when that
-// still leaves a workgroup per CU) and wavefronts per workgroup (8, or 4 for
-// fewer than 8 steps).  Each wavefront keeps one step in flight: measured on
-// MI355X, more wavefronts hide the load latency better than deeper
-// per-wavefront prefetch (2 or 4 slots) at the same register budget.
+// Decode launch configuration for an [M, N] output and `steps` 256-wide
+// k-steps per k range: 16-column tiles per wavefront (2 when that still
+// leaves a workgroup per CU), wavefronts per workgroup (8; 4 for fewer than
+// 8 steps, and for four token tiles on 32 columns, where 8 measured slower)
+// and 16-token tiles (1, 2 or 4).
 struct GemvConfig {
-    int t, waves;
+    int t, waves, mt;
 };
 
-static GemvConfig gemv_config(int64_t N, int64_t steps, int64_t cus) {
+static GemvConfig gemv_config(int64_t M, int64_t N, int64_t steps, int64_t cus) {
     GemvConfig c;
     c.t = (N + 31) / 32 >= cus ? 2 : 1;
-    c.waves = steps >= 8 ? 8 : 4;
+    c.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+    c.waves = steps >= 8 && !(c.mt == 4 && c.t == 2) ? 8 : 4;
     return c;
 }
 
@@ -781,9 +610,12 @@ int64_t nvfp4_linear_splits(int64_t M, int64_t N, int64_t K, int64_t part_bytes)
         // ceil(c / w) rounds of one step per wavefront, each bound by the
         // load latency or by the grid's W bytes at the streaming rate, plus
         // a fixed cost per launch
-        const double t_lat = 1.2e-6, t_fix = 2.5e-6, bw_w = 4.0e12;
-        const GemvConfig c1 = gemv_config(N, nsteps, cus);
+        const double t_lat = 1.2e-6, t_fix = 2.5e-6, bw_w = 4.0e12, clock = 2.4e9;
+        const GemvConfig c1 = gemv_config(M, N, nsteps, cus);
         const double wave_bytes = 16.0 * c1.t * (kGemvK / 2 + kGemvK / 16);  // W per wavefront-step
+        // vector instructions per wavefront-step: about 8 per 16 x 32 operand
+        // fragment (W and X) and one issue slot per MFMA, 4 cycles each
+        const double wave_valu = 4.0 * (64.0 * (c1.t + c1.mt) + 8.0 * c1.t * c1.mt);
         int64_t smax = nsteps / 4;
         if (per > 0 && smax > part_bytes / per) smax = part_bytes / per;
         int64_t best = 1;
@@ -791,8 +623,10 @@ int64_t nvfp4_linear_splits(int64_t M, int64_t N, int64_t K, int64_t part_bytes)
         for (int64_t s = 1; s <= smax || s == 1; ++s) {
             const int64_t chunk = (nsteps + s - 1) / s;
             const int64_t se = (nsteps + chunk - 1) / chunk;
-            const int64_t w = gemv_config(N, chunk, cus).waves;
-            const double round = (double)(wgs * se * w) * wave_bytes / bw_w;
+            const int64_t w = gemv_config(M, N, chunk, cus).waves;
+            double round = (double)(wgs * se * w) * wave_bytes / bw_w;
+            const double valu = (double)(wgs * se * w) / (4.0 * cus) * wave_valu / clock;
+            if (valu > round) round = valu;
             double t = (double)((chunk + w - 1) / w) * (round > t_lat ? round : t_lat) + t_fix;
             if (se > 1) t += (double)se * (double)M * (double)N * 8.0 / bw + t_split;
             if (s == 1 || t < best_t) {
@@ -804,10 +638,9 @@ int64_t nvfp4_linear_splits(int64_t M, int64_t N, int64_t K, int64_t part_bytes)
         return best;
     }
     if (wgs >= cus) return 1;
-    const bool skinny = M <= kSkinnyMaxM;
-    const double t_step = skinny ? 0.16e-6 : 2.3e-6;   // s per 64-wide k-step of one workgroup
-    const double t_round = skinny ? 4.0e-6 : 3.0e-6;   // s of fixed cost per round
-    int64_t smax = nsteps / (skinny ? kSkinnyWaves : kMinSplitSteps);
+    const double t_step = 2.3e-6;   // s per 64-wide k-step of one workgroup
+    const double t_round = 3.0e-6;  // s of fixed cost per round
+    int64_t smax = nsteps / kMinSplitSteps;
     if (per > 0 && smax > part_bytes / per) smax = part_bytes / per;
     int64_t best = 1;
     double best_t = 0.0;
@@ -835,16 +668,22 @@ hipError_t launch_nvfp4_linear(const GemmArgs& args, bool fast, bool bf16_out, h
     const unsigned splits = (unsigned)a.ksplit;
     if (gemv) {
         const bool f = fast && a.K % kGemvK == 0;
-        const GemvConfig c = gemv_config(a.N, a.kchunk, device_cus());
+        const GemvConfig c = gemv_config(a.M, a.N, a.kchunk, device_cus());
         const int64_t wgs = (a.N + 16 * c.t - 1) / (16 * c.t);
         const dim3 grid((unsigned)wgs, splits), block(64 * c.waves);
-        const int cfg = c.t * 16 + c.waves;
-#define FOCUS_GV(F, B)                                                                                      \
-    do {                                                                                                    \
-        if (cfg == 0x18) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 8, 1, 1>), grid, block, 0, stream, a); \
-        else if (cfg == 0x14) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 4, 1, 1>), grid, block, 0, stream, a); \
-        else if (cfg == 0x28) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 8, 2, 1>), grid, block, 0, stream, a); \
-        else hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 4, 2, 1>), grid, block, 0, stream, a);             \
+        const int cfg = c.mt * 256 + c.t * 16 + c.waves;
+#define FOCUS_GV1(F, B, MT)                                                                                     \
+    do {                                                                                                        \
+        if (cfg == 256 * MT + 0x18) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 8, 1, MT>), grid, block, 0, stream, a); \
+        else if (cfg == 256 * MT + 0x14) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 4, 1, MT>), grid, block, 0, stream, a); \
+        else if (cfg == 256 * MT + 0x28) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 8, 2, MT>), grid, block, 0, stream, a); \
+        else if (cfg == 256 * MT + 0x24) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 4, 2, MT>), grid, block, 0, stream, a); \
+    } while (0)
+#define FOCUS_GV(F, B)         \
+    do {                       \
+        FOCUS_GV1(F, B, 1);    \
+        FOCUS_GV1(F, B, 2);    \
+        FOCUS_GV1(F, B, 4);    \
     } while (0)
         if (f) {
             if (bf16_out) FOCUS_GV(true, true);
@@ -853,22 +692,8 @@ hipError_t launch_nvfp4_linear(const GemmArgs& args, bool fast, bool bf16_out, h
             if (bf16_out) FOCUS_GV(false, true);
             else FOCUS_GV(false, false);
         }
+#undef FOCUS_GV1
 #undef FOCUS_GV
-    } else if (a.M <= kSkinnyMaxM) {
-        const dim3 grid((unsigned)((a.N + 31) / 32), splits), block(64 * kSkinnyWaves);
-#define FOCUS_SK(F, B)                                                                                 \
-    do {                                                                                               \
-        if (a.M <= 32) hipLaunchKernelGGL((k_nvfp4_linear_skinny<F, B, 1>), grid, block, 0, stream, a); \
-        else hipLaunchKernelGGL((k_nvfp4_linear_skinny<F, B, 2>), grid, block, 0, stream, a);          \
-    } while (0)
-        if (fast) {
-            if (bf16_out) FOCUS_SK(true, true);
-            else FOCUS_SK(true, false);
-        } else {
-            if (bf16_out) FOCUS_SK(false, true);
-            else FOCUS_SK(false, false);
-        }
-#undef FOCUS_SK
     } else {
         const int64_t tiles_m = (a.M + kBM - 1) / kBM, tiles_n = (a.N + kBN - 1) / kBN;
         const dim3 grid((unsigned)(tiles_m * tiles_n), splits), block(kGemmThreads);
@@ -900,10 +725,9 @@ hipError_t launch_nvfp4_linear(const GemmArgs& args, bool fast, bool bf16_out, h
 
 int64_t nvfp4_linear_workgroups(int64_t M, int64_t N) {
     if (M <= kGemvMaxM) {
-        const int t = gemv_config(N, 1, device_cus()).t;
+        const int t = gemv_config(M, N, 1, device_cus()).t;
         return (N + 16 * t - 1) / (16 * t);
     }
-    if (M <= kSkinnyMaxM) return (N + 31) / 32;
     return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
 }
 

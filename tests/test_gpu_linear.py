@@ -76,10 +76,10 @@ def check_bound(y, ref, refabs, K, bf16, label):
     return float(np.max(err / np.maximum(refabs, 1e-300)))
 
 
-@pytest.mark.parametrize("M", [300, 40, 16, 5], ids=lambda v: f"M{v}")
+@pytest.mark.parametrize("M", [300, 40, 32, 16, 5], ids=lambda v: f"M{v}")
 def test_exact_when_partial_sums_are_exact(focus, orc, M):
-    # M = 300: tiled kernel; 40: few-token kernel with two 32-row X tiles;
-    # 16 and 5: one X tile (operand and output layouts of each)
+    # M = 300: tiled kernel; 40: decode kernel with four 16-token X tiles,
+    # 32 with two, 16 and 5 with one (operand and output layouts of each)
     N, K = 520, 1024
     xc, _, wc, _ = operands(M, N, K, 1)
     xs = torch.full((M, K // 16), 0x38, dtype=torch.uint8)
@@ -94,11 +94,12 @@ def test_exact_when_partial_sums_are_exact(focus, orc, M):
     assert np.array_equal(y16, want)
 
 
-# M <= 16 takes the decode kernel (K % 256 != 0: masked loads), M <= 64 the
-# few-token kernel (one or two 32-row tiles of X), larger M the tiled kernel
-# (K % 64 != 0: masked loads); some shapes split k.
+# M <= 64 takes the decode kernel (one, two or four 16-token tiles; K % 256
+# != 0: masked loads), larger M the tiled kernel (K % 64 != 0: masked loads);
+# some shapes split k.
 SHAPES = [(1, 1, 16), (3, 17, 256), (7, 33, 48), (12, 4111, 320), (16, 200, 1040), (16, 4096, 4096),
-          (5, 1000, 28672), (16, 1024, 28688), (1, 14336, 512), (3, 8200, 80), (17, 64, 64), (32, 4096, 4096), (33, 1000, 1040), (64, 512, 8192), (64, 300, 14336),
+          (5, 1000, 28672), (16, 1024, 28688), (1, 14336, 512), (3, 8200, 80), (20, 8192, 256), (50, 8200, 512),
+          (17, 64, 64), (32, 4096, 4096), (33, 1000, 1040), (64, 512, 8192), (64, 300, 14336),
           (65, 130, 192), (255, 257, 64), (257, 255, 1040), (300, 520, 4096), (513, 96, 80)]
 
 
@@ -136,7 +137,7 @@ def test_linear_signed_and_nan_scales(focus, orc, M, N, K):
     and the NaN bytes 0x7F / 0xFF planted in a few rows of X and W: an output
     is NaN exactly where the oracle's is (a NaN block scale poisons its row
     even against zero codes), and every other output is within the bound.
-    The three shapes take the few-token, tiled and masked-load paths."""
+    The three shapes take the decode, tiled and masked-load paths."""
     xc, xs, wc, ws = operands(M, N, K, 11, scale_lo=0x00, scale_hi=0x7F)
     g = torch.Generator().manual_seed(M * N + K)
     xs = xs | (torch.randint(0, 2, xs.shape, generator=g, dtype=torch.uint8) << 7)
@@ -156,7 +157,7 @@ def test_linear_signed_and_nan_scales(focus, orc, M, N, K):
                     dt == torch.bfloat16, f"{(M, N, K)} {dt} signed scales")
 
 
-@pytest.mark.parametrize("M", [1, 65])
+@pytest.mark.parametrize("M", [1, 33, 65])
 @pytest.mark.parametrize("nb", [256, 254])
 @pytest.mark.parametrize("side", ["x", "w"])
 def test_linear_every_scale_byte(focus, side, nb, M):
@@ -168,7 +169,8 @@ def test_linear_every_scale_byte(focus, side, nb, M):
     sum starts from +0).  Expected values come from torch's
     float8_e4m3fn decoding.  nb = 256 blocks (K % 64 == 0, the 0x7F / 0xFF
     slots refilled with 0x38) takes the aligned loads, 254 the masked ones;
-    M = 1 the few-token kernel, 65 the tiled one."""
+    M = 1 and 33 the decode kernel (one and four token tiles), 65 the tiled
+    one."""
     byts = [b for b in range(256) if (b & 0x7F) != 0x7F]
     if nb == 256:
         byts = [b if (b & 0x7F) != 0x7F else 0x38 for b in range(256)]
