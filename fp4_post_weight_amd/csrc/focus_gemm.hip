@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
 // output still has a workgroup per CU with it (X is then read and
 // dequantized half as often).  Against 32 x 32 tiles with four steps in
 // flight per wavefront (its predecessor for 16 < M <= 64), 17 to 64 tokens
-// through the Llama-3.1-8B layer shapes took 36-72 us instead of 58-96 us.
+// through the Llama-3.1-8B layer shapes took 36-68 us instead of 58-96 us.
 // ---------------------------------------------------------------------------
 
 constexpr int kGemvK = 256;          // k per step
@@ -608,8 +608,8 @@ int64_t nvfp4_linear_splits(int64_t M, int64_t N, int64_t K, int64_t part_bytes)
     if (gemv) {
         // decode: a range of c steps on a workgroup of w wavefronts takes
         // ceil(c / w) rounds of one step per wavefront, each bound by the
-        // load latency or by the grid's W bytes at the streaming rate, plus
-        // a fixed cost per launch
+        // load latency, by the grid's W bytes at the streaming rate or by
+        // the vector instructions per SIMD, plus a fixed cost per launch
         const double t_lat = 1.2e-6, t_fix = 2.5e-6, bw_w = 4.0e12, clock = 2.4e9;
         const GemvConfig c1 = gemv_config(M, N, nsteps, cus);
         const double wave_bytes = 16.0 * c1.t * (kGemvK / 2 + kGemvK / 16);  // W per wavefront-step
