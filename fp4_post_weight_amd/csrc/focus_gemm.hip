@@ -31,9 +31,14 @@
 //    runs in slices 0-1 interleaved with the matrix instructions, and the
 //    one barrier per step sits after slice 1, so slices 2-3 cover the reads
 //    of the next step's first fragments.  Measured, the matrix cores are
-//    busy a little under half of the cycles; LDS traffic (about 192 KB per
-//    step and CU), the dequantization and the waits of a pipeline with one
-//    wavefront per SIMD share the rest.  Keeping codes in LDS and
+//    busy a little under half of the cycles, and the LDS operand traffic
+//    (about 192 KB per step and CU) is the main limit: timing-only copies of
+//    this kernel without the dequantization, the streaming loads and the
+//    barrier were only 9 % faster, without any LDS access 30 % faster still,
+//    while bare back-to-back matrix instructions of one wavefront per SIMD
+//    reach about 87 % of the FP16 peak.  Taking W's fragments straight from
+//    global memory into each wavefront (half the LDS traffic, twice the
+//    dequantization of W) was 12 % slower.  Keeping codes in LDS and
 //    dequantizing per wavefront cuts LDS traffic four-fold but doubles the
 //    vector work, which lowers the clock under this load; measured, it was
 //    slower.  Eight wavefronts of 128 x 64 (two per SIMD, with a prefetch
@@ -145,6 +150,11 @@ __device__ __forceinline__ f16x8 codes_times(uint32_t w, _Float16 S) {
 // Scale of block b (0-3) of a row's k-step from its two scale pairs.
 __device__ __forceinline__ _Float16 block_scale(f16x2 s01, f16x2 s23, int b) {
     return b == 0 ? s01.x : b == 1 ? s01.y : b == 2 ? s23.x : s23.y;
+}
+
+// Dword kk (0-3) of a 16-byte vector.
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int kk) {
+    return kk == 0 ? v.x : kk == 1 ? v.y : kk == 2 ? v.z : v.w;
 }
 
 __device__ __forceinline__ void store_chunk(_Float16* lds_row, const RowChunk& r) {
@@ -411,10 +421,6 @@ __device__ __forceinline__ GemvChunk load_gemv(const uint8_t* __restrict__ codes
     r.c0 = make_uint4(v[0].x, v[0].y, v[1].x, v[1].y);
     r.c1 = make_uint4(v[2].x, v[2].y, v[3].x, v[3].y);
     return r;
-}
-
-__device__ __forceinline__ uint32_t dword_of(const uint4& v, int kk) {
-    return kk == 0 ? v.x : kk == 1 ? v.y : kk == 2 ? v.z : v.w;
 }
 
 __device__ __forceinline__ uint32_t gemv_dword(const GemvChunk& c, int j) {
