@@ -49,9 +49,9 @@
 //  * Loads are straight-line in the common case (K % 64 == 0, aligned): a
 //    row past the end of X or W reads the last row instead; it only feeds
 //    outputs that are never stored.
-//  * With few tokens (M <= 64) the layer is bound by streaming W, and a
+//  * With few tokens (M <= 128) the layer is bound by streaming W, and a
 //    decode kernel without LDS operand tiles takes over
-//    (v_mfma_f32_16x16x32_f16, one to four 16-token tiles).  When an output
+//    (v_mfma_f32_16x16x32_f16, 1, 2, 4 or 8 tiles of 16 tokens).  When an output
 //    has too few columns to fill the GPU, the sum over k is split into ranges
 //    whose partials a finalize kernel adds in order.
 
@@ -349,15 +349,15 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
 }
 
 // ---------------------------------------------------------------------------
-// Decode (M <= 64): v_mfma_f32_16x16x32_f16 on MT = 1, 2 or 4 tiles of 16
-// tokens (every weight element feeds at most 64 outputs, so the layer is
-// bound by streaming W and no operand needs sharing through LDS).  A
-// workgroup of WAVES wavefronts owns 16 T output columns (16 T rows of W);
-// the 256-wide k-steps of its k range are dealt round-robin to its
-// wavefronts, each accumulates MT x T partial 16 x 16 tiles (a dequantized W
-// fragment feeds all MT token tiles, an X fragment all T column tiles), and
-// one LDS reduction sums the WAVES partial tiles in wavefront order
-// (deterministic).
+// Decode (M <= 128): v_mfma_f32_16x16x32_f16 on MT = 1, 2, 4 or 8 tiles of
+// 16 tokens (every weight element feeds at most 128 outputs, so the layer is
+// bound by streaming W, or by the vector work of dequantizing X, and no
+// operand needs sharing through LDS).  A workgroup of WAVES wavefronts owns
+// 16 T output columns (16 T rows of W); the 256-wide k-steps of its k range
+// are dealt round-robin to its wavefronts, each accumulates MT x T partial
+// 16 x 16 tiles (a dequantized W fragment feeds all MT token tiles, an X
+// fragment all T column tiles), and one LDS reduction sums the WAVES partial
+// tiles in wavefront order (deterministic).
 //
 // Within a step the sum is order-free, so lane group g = lane / 16 takes k in
 // [64g, 64g + 64): 32 contiguous code bytes (blocks 4g..4g+3 of the step) and
@@ -372,11 +372,13 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
 // output still has a workgroup per CU with it (X is then read and
 // dequantized half as often).  Against 32 x 32 tiles with four steps in
 // flight per wavefront (its predecessor for 16 < M <= 64), 17 to 64 tokens
-// through the Llama-3.1-8B layer shapes took 36-68 us instead of 58-96 us.
+// through the Llama-3.1-8B layer shapes took 36-68 us instead of 58-96 us;
+// 65 to 128 tokens take about 15 % less time than the tiled kernel's
+// 256-row tiles.
 // ---------------------------------------------------------------------------
 
 constexpr int kGemvK = 256;          // k per step
-constexpr int64_t kGemvMaxM = 64;
+constexpr int64_t kGemvMaxM = 128;
 
 struct GemvChunk {
     uint4 c0, c1;  // code bytes [32g, 32g + 32) of the row's step
@@ -588,8 +590,8 @@ static int device_cus() {
 // Decode launch configuration for an [M, N] output and `steps` 256-wide
 // k-steps per k range: 16-column tiles per wavefront (2 when that still
 // leaves a workgroup per CU), wavefronts per workgroup (8; 4 for fewer than
-// 8 steps, and for four token tiles on 32 columns, where 8 measured slower)
-// and 16-token tiles (1, 2 or 4).
+// 8 steps, for eight token tiles, and for four on 32 columns, where 8
+// measured slower) and 16-token tiles (1, 2, 4 or 8).
 struct GemvConfig {
     int t, waves, mt;
 };
@@ -597,8 +599,8 @@ struct GemvConfig {
 static GemvConfig gemv_config(int64_t M, int64_t N, int64_t steps, int64_t cus) {
     GemvConfig c;
     c.t = (N + 31) / 32 >= cus ? 2 : 1;
-    c.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
-    c.waves = steps >= 8 && !(c.mt == 4 && c.t == 2) ? 8 : 4;
+    c.mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
+    c.waves = steps >= 8 && c.mt < 8 && !(c.mt == 4 && c.t == 2) ? 8 : 4;
     return c;
 }
 
@@ -685,11 +687,13 @@ hipError_t launch_nvfp4_linear(const GemmArgs& args, bool fast, bool bf16_out, h
         else if (cfg == 256 * MT + 0x28) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 8, 2, MT>), grid, block, 0, stream, a); \
         else if (cfg == 256 * MT + 0x24) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 4, 2, MT>), grid, block, 0, stream, a); \
     } while (0)
-#define FOCUS_GV(F, B)         \
-    do {                       \
-        FOCUS_GV1(F, B, 1);    \
-        FOCUS_GV1(F, B, 2);    \
-        FOCUS_GV1(F, B, 4);    \
+#define FOCUS_GV(F, B)                                                                                  \
+    do {                                                                                                \
+        FOCUS_GV1(F, B, 1);                                                                             \
+        FOCUS_GV1(F, B, 2);                                                                             \
+        FOCUS_GV1(F, B, 4);                                                                             \
+        if (cfg == 256 * 8 + 0x14) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 4, 1, 8>), grid, block, 0, stream, a); \
+        else if (cfg == 256 * 8 + 0x24) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 4, 2, 8>), grid, block, 0, stream, a); \
     } while (0)
         if (f) {
             if (bf16_out) FOCUS_GV(true, true);

@@ -76,10 +76,11 @@ def check_bound(y, ref, refabs, K, bf16, label):
     return float(np.max(err / np.maximum(refabs, 1e-300)))
 
 
-@pytest.mark.parametrize("M", [300, 40, 32, 16, 5], ids=lambda v: f"M{v}")
+@pytest.mark.parametrize("M", [300, 100, 40, 32, 16, 5], ids=lambda v: f"M{v}")
 def test_exact_when_partial_sums_are_exact(focus, orc, M):
-    # M = 300: tiled kernel; 40: decode kernel with four 16-token X tiles,
-    # 32 with two, 16 and 5 with one (operand and output layouts of each)
+    # M = 300: tiled kernel; 100: decode kernel with eight 16-token X tiles,
+    # 40 with four, 32 with two, 16 and 5 with one (operand and output
+    # layouts of each)
     N, K = 520, 1024
     xc, _, wc, _ = operands(M, N, K, 1)
     xs = torch.full((M, K // 16), 0x38, dtype=torch.uint8)
@@ -94,13 +95,14 @@ def test_exact_when_partial_sums_are_exact(focus, orc, M):
     assert np.array_equal(y16, want)
 
 
-# M <= 64 takes the decode kernel (one, two or four 16-token tiles; K % 256
+# M <= 128 takes the decode kernel (1, 2, 4 or 8 tiles of 16 tokens; K % 256
 # != 0: masked loads), larger M the tiled kernel (K % 64 != 0: masked loads);
 # some shapes split k.
 SHAPES = [(1, 1, 16), (3, 17, 256), (7, 33, 48), (12, 4111, 320), (16, 200, 1040), (16, 4096, 4096),
           (5, 1000, 28672), (16, 1024, 28688), (1, 14336, 512), (3, 8200, 80), (20, 8192, 256), (50, 8200, 512),
           (17, 64, 64), (32, 4096, 4096), (33, 1000, 1040), (64, 512, 8192), (64, 300, 14336),
-          (65, 130, 192), (255, 257, 64), (257, 255, 1040), (300, 520, 4096), (513, 96, 80)]
+          (65, 130, 192), (100, 8200, 512), (128, 1000, 4160), (129, 130, 192), (255, 257, 64), (257, 255, 1040),
+          (300, 520, 4096), (513, 96, 80)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES, ids=lambda v: str(v))
@@ -131,7 +133,7 @@ def test_linear_single_activation_scale_and_wide_scales(focus, orc):
     check_bound(y, ref, refabs, K, False, "one s2x, scale bytes 0x01..0x7E")
 
 
-@pytest.mark.parametrize("M,N,K", [(16, 200, 1024), (130, 300, 512), (70, 90, 1040)], ids=lambda v: str(v))
+@pytest.mark.parametrize("M,N,K", [(16, 200, 1024), (130, 300, 512), (140, 90, 1040)], ids=lambda v: str(v))
 def test_linear_signed_and_nan_scales(focus, orc, M, N, K):
     """Scale bytes with either sign over 0x00..0x7E (zero, subnormal, normal)
     and the NaN bytes 0x7F / 0xFF planted in a few rows of X and W: an output
@@ -157,7 +159,7 @@ def test_linear_signed_and_nan_scales(focus, orc, M, N, K):
                     dt == torch.bfloat16, f"{(M, N, K)} {dt} signed scales")
 
 
-@pytest.mark.parametrize("M", [1, 33, 65])
+@pytest.mark.parametrize("M", [1, 33, 129])
 @pytest.mark.parametrize("nb", [256, 254])
 @pytest.mark.parametrize("side", ["x", "w"])
 def test_linear_every_scale_byte(focus, side, nb, M):
@@ -169,7 +171,7 @@ def test_linear_every_scale_byte(focus, side, nb, M):
     sum starts from +0).  Expected values come from torch's
     float8_e4m3fn decoding.  nb = 256 blocks (K % 64 == 0, the 0x7F / 0xFF
     slots refilled with 0x38) takes the aligned loads, 254 the masked ones;
-    M = 1 and 33 the decode kernel (one and four token tiles), 65 the tiled
+    M = 1 and 33 the decode kernel (one and four token tiles), 129 the tiled
     one."""
     byts = [b for b in range(256) if (b & 0x7F) != 0x7F]
     if nb == 256:
@@ -253,7 +255,7 @@ def test_linear_full_size_sampled(focus, orc, N, K):
     check_bound(got, ref, refabs, K, True, f"8192 x {N} x {K}")
 
 
-@pytest.mark.parametrize("M", [1, 16, 64])
+@pytest.mark.parametrize("M", [1, 16, 64, 128])
 @pytest.mark.parametrize("N,K", sorted(set(synth.LLAMA_8B.layer_shapes())), ids=lambda v: str(v))
 def test_linear_few_tokens_full_size(focus, orc, M, N, K):
     """Decode-sized activations through every 8B linear shape at full size;
