@@ -309,7 +309,8 @@ int focus_nvfp4_linear(const uint8_t* x_codes, const uint8_t* x_scales, const fl
  * kernel (deterministic).  The call splits only as far as `workspace_bytes`
  * allows (NULL or 0: no split; results then differ from a split call only
  * by the FP32 summation order).  This returns the bytes for the full split
- * (0 when none helps). */
+ * on the current device (0 when none helps); the split depends on the
+ * device's compute-unit count. */
 int64_t focus_nvfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus
