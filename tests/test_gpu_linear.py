@@ -124,6 +124,19 @@ def test_linear_within_bound(focus, orc, M, N, K):
         check_bound(y0, ref, refabs, K, dt == torch.bfloat16, f"{(M, N, K)} {dt} no workspace")
 
 
+@pytest.mark.parametrize("M,N,K", [(16, 1024, 28672), (100, 520, 28672), (8, 14336, 512), (2048, 1024, 4096)],
+                         ids=lambda v: str(v))
+def test_linear_deterministic(focus, M, N, K):
+    """Repeated calls give bit-identical outputs on every path, the split ones
+    included (partials are summed in range order, workgroup partial tiles in
+    wavefront order; no atomics)."""
+    xc, xs, wc, ws = operands(M, N, K, 17)
+    s2x = np.full(M, 1e-3, dtype=np.float32)
+    assert focus.nvfp4_linear_workspace_bytes(M, N, K) > 0 or N == 14336  # the split paths split
+    ys = [gpu_linear(focus, xc, xs, s2x, wc, ws, np.float32(1e-3), torch.float32) for _ in range(3)]
+    assert all(np.array_equal(ys[0].view(np.uint64), y.view(np.uint64)) for y in ys[1:])
+
+
 def test_linear_single_activation_scale_and_wide_scales(focus, orc):
     M, N, K = 130, 200, 512
     xc, xs, wc, ws = operands(M, N, K, 5, scale_lo=0x01, scale_hi=0x7F)  # subnormal to 448
