@@ -125,7 +125,7 @@ int focus_dequantize(const uint8_t* codes, const uint8_t* scales,
  *   scales  [tokens, hidden/16] out.
  *   s2_out  [tokens] FP32 out.
  *   x_deq   [tokens, hidden] BF16 out, 16-byte aligned, or NULL.
- * One kernel launch (one wavefront per token).
+ * One kernel launch (each wavefront quantizes whole token rows).
  */
 int focus_quantize_act_per_token(const uint16_t* x_bf16, int64_t tokens, int64_t hidden,
                                  uint8_t* codes, uint8_t* scales, float* s2_out,
