@@ -241,8 +241,11 @@ def test_act_per_token_full(focus, orc):
     check_act(focus, orc, synth.make_activations(), False, "act [8192,4096]")
 
 
+# 5000 and 8197 tokens: workgroups take one or two rows in turn (the grid
+# stops at 1024 workgroups below 8192 tokens, two rows per wavefront above)
 @pytest.mark.parametrize("shape", [(1, 16), (5, 1024), (6, 2048), (7, 4096), (9, 8192), (3, 16400),
-                                   (13, 48), (2, 4112)], ids=lambda s: f"{s[0]}x{s[1]}")
+                                   (13, 48), (2, 4112), (5000, 4096), (8197, 1040)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
 def test_act_per_token_shapes(focus, orc, shape):
     x = synth.activations(shape, seed=shape[0] * 31 + shape[1], tensor_id=0)
     x[0, :16] = 0.0
