@@ -248,7 +248,8 @@ def test_linear_degenerate(focus):
     assert torch.equal(y, torch.zeros((5, 3), device=DEV))  # K = 0: the empty sum
 
 
-@pytest.mark.parametrize("N,K", sorted(set(synth.LLAMA_8B.layer_shapes())), ids=lambda v: str(v))
+@pytest.mark.parametrize("N,K", sorted(set(synth.LLAMA_8B.layer_shapes())) + [(28672, 8192), (8192, 28672)],
+                         ids=lambda v: str(v))
 def test_linear_full_size_sampled(focus, orc, N, K):
     """8192 tokens through every 8B linear shape at full size (the launch the
     benchmark times); sampled rows and columns against the oracle."""
@@ -270,7 +271,8 @@ def test_linear_full_size_sampled(focus, orc, N, K):
 
 
 @pytest.mark.parametrize("M", [1, 16, 64, 128])
-@pytest.mark.parametrize("N,K", sorted(set(synth.LLAMA_8B.layer_shapes())), ids=lambda v: str(v))
+@pytest.mark.parametrize("N,K", sorted(set(synth.LLAMA_8B.layer_shapes() + synth.LLAMA_70B.layer_shapes())),
+                         ids=lambda v: str(v))
 def test_linear_few_tokens_full_size(focus, orc, M, N, K):
     """Decode-sized activations through every 8B linear shape at full size;
     all rows, sampled columns against the oracle."""
