@@ -325,6 +325,7 @@ def main():
     rows["device copy 2 GiB (streaming ceiling, after the steps)"] = row(t_cp, 2.0 * (1 << 31), 1 << 31)
     if extra_rows:
         rows.update(linear_rows(focus, synth, ws, dev, stream))
+        rows.update(decode_graph_row(focus, synth, ws, dev))
 
     # ---- CPU baseline: the oracle on a bounded sample ----------------------
     cpu = None
@@ -420,6 +421,60 @@ def linear_rows(focus, synth, ws, dev, stream):
                     "frac_mfma_f16_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
                     "GB_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
     return out
+
+
+def decode_graph_row(focus, synth, ws, dev, m_tok=16, reps=50):
+    """The 16-token linear layer on the distinct layer shapes, the four calls
+    captured once in sequence in a HIP graph and replayed: unlike the row
+    above, which times each shape over repeated identical calls (whose
+    launches overlap a little), every kernel here follows a different one,
+    as in a decode pass through the layers."""
+    import torch
+    lib = focus._lib.lib()
+    shapes = sorted(set(ws.layer_shapes()))
+    keep = []
+    for n, k in shapes:
+        xc, xs = synth.nvfp4_operand(m_tok, k, seed=3, tensor_id=60, device=dev)
+        wc, wsc = synth.nvfp4_operand(n, k, seed=3, tensor_id=61, device=dev)
+        s2x = torch.full((m_tok,), 1e-3, dtype=torch.float32, device=dev)
+        s2w = torch.full((1,), 1e-3, dtype=torch.float32, device=dev)
+        y = torch.empty((m_tok, n), dtype=torch.bfloat16, device=dev)
+        nws = int(lib.focus_nvfp4_linear_workspace_bytes(m_tok, n, k))
+        wsp = torch.empty(max(nws // 4, 1), dtype=torch.float32, device=dev)
+        keep.append((xc, xs, s2x, wc, wsc, s2w, y, wsp, n, k, nws))
+
+    def calls(stream_handle):
+        for xc, xs, s2x, wc, wsc, s2w, y, wsp, n, k, nws in keep:
+            focus._lib.check(lib.focus_nvfp4_linear(xc.data_ptr(), xs.data_ptr(), s2x.data_ptr(), 1, m_tok,
+                                                    wc.data_ptr(), wsc.data_ptr(), s2w.data_ptr(), n, k,
+                                                    y.data_ptr(), 1, wsp.data_ptr(), nws, stream_handle))
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        calls(side.cuda_stream)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls(torch.cuda.current_stream(dev).cuda_stream)
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flop = sum(2.0 * m_tok * n * k for n, k in shapes)
+    byts = sum((m_tok + n) * k * 0.5625 + 2.0 * m_tok * n for n, k in shapes)
+    key = (f"NVFP4 linear Y = X' W'^T, {m_tok} tokens, the {len(shapes)} layer shapes in sequence, "
+           "one HIP graph replay (after the steps)")
+    del graph, keep
+    return {key: {"ms": round(ms, 4), "TFLOP_s": round(flop / (ms * 1e-3) / 1e12, 1),
+                  "GB_s": round(byts / (ms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
 
 
 def cpu_baseline(lins, W, M, Q, X, budget):
