@@ -84,6 +84,44 @@ def _p(t: Optional[torch.Tensor]) -> int:
     return 0 if t is None else t.data_ptr()
 
 
+def _check_buf(name, t, dtype, device, numel):
+    """A caller-supplied buffer: a contiguous tensor of `dtype` on `device`
+    holding exactly `numel` elements.  Raises before anything is launched."""
+    _check_dev(name, t, dtype, device)
+    if t.numel() != numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, expected {numel}")
+
+
+def _quant_outs(out, rows, cols, dev, dequant, s2=None, s2_rows=0, scale_block=16, label="out"):
+    """Output buffers of a quantizer call: allocated when `out` is None,
+    otherwise checked (codes [rows, cols/2], scales [rows, cols/scale_block],
+    deq [rows, cols] when dequant, and s2 [s2_rows] FP32 when s2_rows > 0).
+    Returns (codes, scales, deq or None, s2)."""
+    if out is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, cols // scale_block), dtype=torch.uint8, device=dev)
+        deq = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) if dequant else None
+        if s2_rows:
+            s2 = torch.empty((s2_rows,), dtype=torch.float32, device=dev)
+        return codes, scales, deq, s2
+    if not isinstance(out, Quantized):
+        raise TypeError(f"{label} must be a Quantized tuple of buffers")
+    _check_buf(f"{label}.codes", out.codes, torch.uint8, dev, rows * cols // 2)
+    _check_buf(f"{label}.scales", out.scales, torch.uint8, dev, rows * cols // scale_block)
+    deq = None
+    if dequant:
+        if out.deq is None:
+            raise ValueError(f"dequant=True needs {label}.deq")
+        _check_buf(f"{label}.deq", out.deq, torch.bfloat16, dev, rows * cols)
+        deq = out.deq
+    if s2_rows:
+        if out.s2 is None:
+            raise ValueError(f"{label}.s2 is required")
+        _check_buf(f"{label}.s2", out.s2, torch.float32, dev, s2_rows)
+        s2 = out.s2
+    return out.codes, out.scales, deq, s2
+
+
 def tensor_scale(w: torch.Tensor, s2_out: Optional[torch.Tensor] = None,
                  amax_out: Optional[torch.Tensor] = None):
     """s2 = amax|W| / (6*448) (and amax) as one-element FP32 device tensors."""
@@ -95,6 +133,8 @@ def tensor_scale(w: torch.Tensor, s2_out: Optional[torch.Tensor] = None,
         amax_out = torch.empty(1, dtype=torch.float32, device=dev)
     _check_dev("s2_out", s2_out, torch.float32, dev)
     _check_dev("amax_out", amax_out, torch.float32, dev)
+    if s2_out.numel() < 1 or amax_out.numel() < 1:
+        raise ValueError("s2_out and amax_out must hold one float each")
     _lib.check(_lib.lib().focus_tensor_scale(_p(w), w.numel(), _p(s2_out), _p(amax_out),
                                              _stream(w)))
     return s2_out, amax_out
@@ -126,20 +166,7 @@ def quantize(w: torch.Tensor, m: Optional[torch.Tensor] = None, q: Optional[torc
     _check_dev("s2", s2, torch.float32, dev)
     if s2.numel() < 1:
         raise ValueError("s2 must hold one float")
-    if out is None:
-        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
-        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
-        deq = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) if dequant else None
-    else:
-        codes, scales, deq = out.codes, out.scales, (out.deq if dequant else None)
-        _check_dev("codes", codes, torch.uint8, dev)
-        _check_dev("scales", scales, torch.uint8, dev)
-        if codes.numel() != rows * cols // 2 or scales.numel() != rows * cols // 16:
-            raise ValueError("output buffers have the wrong size")
-        if deq is not None:
-            _check_dev("deq", deq, torch.bfloat16, dev)
-            if deq.numel() != rows * cols:
-                raise ValueError("deq buffer has the wrong size")
+    codes, scales, deq, _ = _quant_outs(out, rows, cols, dev, dequant)
     _lib.check(_lib.lib().focus_quantize(_p(w), rows, cols, _p(m), _p(q), _p(s2), _p(codes),
                                          _p(scales), _p(deq), _stream(w)))
     return Quantized(codes, scales, deq, s2)
@@ -160,7 +187,7 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, s2: torch.Tensor,
         raise ValueError("s2 too small")
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
-    _check_dev("out", out, torch.bfloat16, dev)
+    _check_buf("out", out, torch.bfloat16, dev, rows * cols)
     _lib.check(_lib.lib().focus_dequantize(_p(codes), _p(scales), _p(s2), 1 if s2_per_row else 0,
                                            rows, cols, _p(out), _stream(codes)))
     return out
@@ -176,13 +203,7 @@ def quantize_act_per_token(x: torch.Tensor, dequant: bool = False,
     if h % 16:
         raise ValueError("hidden must be a multiple of 16")
     dev = x.device
-    if out is None:
-        codes = torch.empty((t, h // 2), dtype=torch.uint8, device=dev)
-        scales = torch.empty((t, h // 16), dtype=torch.uint8, device=dev)
-        s2 = torch.empty((t,), dtype=torch.float32, device=dev)
-        deq = torch.empty((t, h), dtype=torch.bfloat16, device=dev) if dequant else None
-    else:
-        codes, scales, s2, deq = out.codes, out.scales, out.s2, (out.deq if dequant else None)
+    codes, scales, deq, s2 = _quant_outs(out, t, h, dev, dequant, s2_rows=t)
     _lib.check(_lib.lib().focus_quantize_act_per_token(_p(x), t, h, _p(codes), _p(scales), _p(s2),
                                                        _p(deq), _stream(x)))
     return Quantized(codes, scales, deq, s2)
@@ -206,15 +227,12 @@ def quantize_fo6(w: torch.Tensor, s2: Optional[torch.Tensor] = None, dequant: bo
     if s2 is None:
         s2, _ = tensor_scale(w)
     _check_dev("s2", s2, torch.float32, dev)
-    if out is None:
-        out = Quantized(torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
-                        torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
-                        torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) if dequant else None,
-                        s2)
-    deq = out.deq if dequant else None
-    _lib.check(_lib.lib().focus_quantize_fo6(_p(w), rows, cols, _p(s2), _p(out.codes), _p(out.scales),
+    if s2.numel() < 1:
+        raise ValueError("s2 must hold one float")
+    codes, scales, deq, _ = _quant_outs(out, rows, cols, dev, dequant)
+    _lib.check(_lib.lib().focus_quantize_fo6(_p(w), rows, cols, _p(s2), _p(codes), _p(scales),
                                              _p(deq), _stream(w)))
-    return Quantized(out.codes, out.scales, deq, s2)
+    return Quantized(codes, scales, deq, s2)
 
 
 def quantize_act_per_token_fo6(x: torch.Tensor, dequant: bool = False,
@@ -227,26 +245,19 @@ def quantize_act_per_token_fo6(x: torch.Tensor, dequant: bool = False,
     if h % 16:
         raise ValueError("hidden must be a multiple of 16")
     dev = x.device
-    if out is None:
-        out = Quantized(torch.empty((t, h // 2), dtype=torch.uint8, device=dev),
-                        torch.empty((t, h // 16), dtype=torch.uint8, device=dev),
-                        torch.empty((t, h), dtype=torch.bfloat16, device=dev) if dequant else None,
-                        torch.empty((t,), dtype=torch.float32, device=dev))
-    deq = out.deq if dequant else None
-    _lib.check(_lib.lib().focus_quantize_act_per_token_fo6(_p(x), t, h, _p(out.codes), _p(out.scales),
-                                                           _p(out.s2), _p(deq), _stream(x)))
-    return Quantized(out.codes, out.scales, deq, out.s2)
+    codes, scales, deq, s2 = _quant_outs(out, t, h, dev, dequant, s2_rows=t)
+    _lib.check(_lib.lib().focus_quantize_act_per_token_fo6(_p(x), t, h, _p(codes), _p(scales),
+                                                           _p(s2), _p(deq), _stream(x)))
+    return Quantized(codes, scales, deq, s2)
 
 
 # ---------------------------------------------------------------------------
 # FOCUS on MXFP4
 # ---------------------------------------------------------------------------
 
-def _mx_outs(rows, cols, dev, dequant):
-    return Quantized(torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
-                     torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev),
-                     torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) if dequant else None,
-                     None)
+def _mx_outs(out, rows, cols, dev, dequant, label="out"):
+    codes, scales, deq, _ = _quant_outs(out, rows, cols, dev, dequant, scale_block=32, label=label)
+    return Quantized(codes, scales, deq, None)
 
 
 def quantize_mx(w: torch.Tensor, m: Optional[torch.Tensor] = None, q: Optional[torch.Tensor] = None,
@@ -269,12 +280,10 @@ def quantize_mx(w: torch.Tensor, m: Optional[torch.Tensor] = None, q: Optional[t
         _check_dev("q", q, torch.float32, dev)
         if tuple(q.shape) != (rows, cols // 8):
             raise ValueError(f"q must be [{rows}, {cols // 8}]")
-    if out is None:
-        out = _mx_outs(rows, cols, dev, dequant)
-    deq = out.deq if dequant else None
+    out = _mx_outs(out, rows, cols, dev, dequant)
     _lib.check(_lib.lib().focus_quantize_mx(_p(w), rows, cols, _p(m), _p(q), _p(out.codes),
-                                            _p(out.scales), _p(deq), _stream(w)))
-    return Quantized(out.codes, out.scales, deq, None)
+                                            _p(out.scales), _p(out.deq), _stream(w)))
+    return out
 
 
 def dequantize_mx(codes: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -287,7 +296,7 @@ def dequantize_mx(codes: torch.Tensor, scales: torch.Tensor, out: Optional[torch
         raise ValueError(f"scales must be [{rows}, {cols // 32}]")
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
-    _check_dev("out", out, torch.bfloat16, dev)
+    _check_buf("out", out, torch.bfloat16, dev, rows * cols)
     _lib.check(_lib.lib().focus_dequantize_mx(_p(codes), _p(scales), rows, cols, _p(out), _stream(codes)))
     return out
 
@@ -295,25 +304,32 @@ def dequantize_mx(codes: torch.Tensor, scales: torch.Tensor, out: Optional[torch
 def quantize_mx_many(ws, ms, qs, outs=None, dequant: bool = True, run: bool = True) -> Batch:
     """Batched FOCUS on MXFP4 (m [rows, cols/32] entries may be None)."""
     n = len(ws)
+    if not (len(ms) == len(qs) == n) or (outs is not None and len(outs) != n):
+        raise ValueError("ws, ms, qs (and outs) must have the same length")
+    if n == 0:
+        raise ValueError("no tensors")
     dev = ws[0].device
     arr = (_lib.QuantDesc * n)()
     res = []
     for i in range(n):
         w, m, q = ws[i], ms[i], qs[i]
         _check_dev(f"ws[{i}]", w, torch.bfloat16, dev)
+        if w.dim() != 2:
+            raise ValueError(f"ws[{i}] must be 2-D [rows, cols]")
         rows, cols = w.shape
         if cols % 32:
             raise ValueError("cols must be a multiple of 32")
         if m is not None:
             _check_dev(f"ms[{i}]", m, torch.float32, dev)
-            assert tuple(m.shape) == (rows, cols // 32)
+            if tuple(m.shape) != (rows, cols // 32):
+                raise ValueError(f"ms[{i}] must be [{rows}, {cols // 32}]")
         if q is not None:
             _check_dev(f"qs[{i}]", q, torch.float32, dev)
-            assert tuple(q.shape) == (rows, cols // 8)
-        o = outs[i] if outs is not None else _mx_outs(rows, cols, dev, dequant)
-        deq = o.deq if dequant else None
-        res.append(Quantized(o.codes, o.scales, deq, None))
-        arr[i] = _lib.QuantDesc(_p(w), rows, cols, _p(m), _p(q), 0, _p(o.codes), _p(o.scales), _p(deq))
+            if tuple(q.shape) != (rows, cols // 8):
+                raise ValueError(f"qs[{i}] must be [{rows}, {cols // 8}]")
+        o = _mx_outs(None if outs is None else outs[i], rows, cols, dev, dequant, label=f"outs[{i}]")
+        res.append(o)
+        arr[i] = _lib.QuantDesc(_p(w), rows, cols, _p(m), _p(q), 0, _p(o.codes), _p(o.scales), _p(o.deq))
     b = Batch("focus_quantize_mx_many", arr, (list(ws), list(ms), list(qs), res), dev)
     b.outs = res
     return b.run() if run else b
@@ -334,17 +350,12 @@ def _mix_desc(i, w, tile_map, tile_rows, tile_cols, s2, dev, dequant, out):
     if tuple(tile_map.shape) != (rows // tile_rows, cols // tile_cols) or not tile_map.is_contiguous():
         raise ValueError(f"map must be a contiguous [{rows // tile_rows}, {cols // tile_cols}] uint8 tensor")
     _check_dev(f"s2s[{i}]", s2, torch.float32, dev)
-    if out is None:
-        out = Quantized(torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
-                        torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
-                        torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) if dequant else None,
-                        s2)
-    elif out.codes.numel() != rows * cols // 2 or out.scales.numel() != rows * cols // 16:
-        raise ValueError(f"outs[{i}] has the wrong size")
-    deq = out.deq if dequant else None
-    res = Quantized(out.codes, out.scales, deq, s2)
-    return res, _lib.MixDesc(_p(w), rows, cols, _p(s2), _p(tile_map), tile_rows, tile_cols, _p(out.codes),
-                             _p(out.scales), _p(deq))
+    if s2.numel() < 1:
+        raise ValueError(f"s2s[{i}] must hold one float")
+    codes, scales, deq, _ = _quant_outs(out, rows, cols, dev, dequant, label=f"outs[{i}]")
+    res = Quantized(codes, scales, deq, s2)
+    return res, _lib.MixDesc(_p(w), rows, cols, _p(s2), _p(tile_map), tile_rows, tile_cols, _p(codes),
+                             _p(scales), _p(deq))
 
 
 def quantize_mixfp4(w: torch.Tensor, tile_map: torch.Tensor, tile_rows: int, tile_cols: int = 64,
@@ -397,6 +408,7 @@ def dequantize_mixfp4(codes: torch.Tensor, scales: torch.Tensor, s2: torch.Tenso
         raise ValueError("tile_map must be a contiguous [rows/tile_rows, cols/tile_cols] uint8 tensor")
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    _check_buf("out", out, torch.bfloat16, dev, rows * cols)
     _lib.check(_lib.lib().focus_dequantize_mixfp4(_p(codes), _p(scales), _p(s2), _p(tile_map), rows, cols, tile_rows,
                                                   tile_cols, _p(out), _stream(codes)))
     return out
@@ -408,7 +420,10 @@ def dequantize_mixfp4(codes: torch.Tensor, scales: torch.Tensor, s2: torch.Tenso
 
 def nvfp4_linear_workspace_bytes(M: int, N: int, K: int) -> int:
     """Workspace bytes for ``nvfp4_linear`` to split the sum over k (0: none)."""
-    return int(_lib.lib().focus_nvfp4_linear_workspace_bytes(M, N, K))
+    n = int(_lib.lib().focus_nvfp4_linear_workspace_bytes(M, N, K))
+    if n < 0:
+        raise FocusError(4, "the device query of the split model failed")
+    return n
 
 
 def nvfp4_linear(x: Quantized, w: Quantized, out_dtype: torch.dtype = torch.bfloat16,
@@ -522,33 +537,36 @@ def quantize_many(ws, ms, qs, s2s, outs=None, dequant: bool = True, run: bool = 
     n = len(ws)
     if not (len(ms) == len(qs) == len(s2s) == n):
         raise ValueError("ws, ms, qs, s2s must have the same length")
+    if outs is not None and len(outs) != n:
+        raise ValueError("outs must have one entry per tensor")
+    if n == 0:
+        raise ValueError("no tensors")
     dev = ws[0].device
     arr = (_lib.QuantDesc * n)()
     res = []
     for i in range(n):
         w, m, q, s2 = ws[i], ms[i], qs[i], s2s[i]
         _check_dev(f"ws[{i}]", w, torch.bfloat16, dev)
+        if w.dim() != 2:
+            raise ValueError(f"ws[{i}] must be 2-D [rows, cols]")
         rows, cols = w.shape
+        if cols % 16:
+            raise ValueError(f"ws[{i}]: cols must be a multiple of 16")
         if m is not None:
             _check_dev(f"ms[{i}]", m, torch.float32, dev)
-            assert tuple(m.shape) == (rows, cols // 16)
+            if tuple(m.shape) != (rows, cols // 16):
+                raise ValueError(f"ms[{i}] must be [{rows}, {cols // 16}]")
         if q is not None:
             _check_dev(f"qs[{i}]", q, torch.float32, dev)
-            assert tuple(q.shape) == (rows, cols // 8)
+            if tuple(q.shape) != (rows, cols // 8):
+                raise ValueError(f"qs[{i}] must be [{rows}, {cols // 8}]")
         _check_dev(f"s2s[{i}]", s2, torch.float32, dev)
-        if outs is None:
-            o = Quantized(torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
-                          torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
-                          torch.empty((rows, cols), dtype=torch.bfloat16, device=dev) if dequant else None,
-                          s2)
-        else:
-            o = outs[i]
-            if o.codes.numel() != rows * cols // 2 or o.scales.numel() != rows * cols // 16:
-                raise ValueError(f"outs[{i}] has the wrong size")
-        deq = o.deq if dequant else None
-        res.append(Quantized(o.codes, o.scales, deq, s2))
-        arr[i] = _lib.QuantDesc(_p(w), rows, cols, _p(m), _p(q), _p(s2), _p(o.codes), _p(o.scales),
-                                _p(deq))
+        if s2.numel() < 1:
+            raise ValueError(f"s2s[{i}] must hold one float")
+        codes, scales, deq, _ = _quant_outs(None if outs is None else outs[i], rows, cols, dev, dequant,
+                                            label=f"outs[{i}]")
+        res.append(Quantized(codes, scales, deq, s2))
+        arr[i] = _lib.QuantDesc(_p(w), rows, cols, _p(m), _p(q), _p(s2), _p(codes), _p(scales), _p(deq))
     b = Batch("focus_quantize_many", arr, (list(ws), list(ms), list(qs), list(s2s), res), dev)
     b.outs = res
     return b.run() if run else b
@@ -557,6 +575,11 @@ def quantize_many(ws, ms, qs, s2s, outs=None, dequant: bool = True, run: bool = 
 def dequantize_many(codes, scales, s2s, outs=None, s2_per_row=None, run: bool = True) -> Batch:
     """Dequantize several stored tensors; the result's ``outs`` holds them."""
     n = len(codes)
+    if len(scales) != n or len(s2s) != n or (outs is not None and len(outs) != n) or \
+            (s2_per_row is not None and len(s2_per_row) != n):
+        raise ValueError("codes, scales, s2s (and outs, s2_per_row) must have the same length")
+    if n == 0:
+        raise ValueError("no tensors")
     dev = codes[0].device
     arr = (_lib.DequantDesc * n)()
     res = []
@@ -565,13 +588,19 @@ def dequantize_many(codes, scales, s2s, outs=None, s2_per_row=None, run: bool = 
         _check_dev(f"codes[{i}]", c, torch.uint8, dev)
         _check_dev(f"scales[{i}]", s, torch.uint8, dev)
         _check_dev(f"s2s[{i}]", s2, torch.float32, dev)
+        if c.dim() != 2:
+            raise ValueError(f"codes[{i}] must be 2-D [rows, cols/2]")
         rows, half = c.shape
         cols = 2 * half
+        if cols % 16:
+            raise ValueError(f"codes[{i}]: cols must be a multiple of 16")
+        if s.numel() != rows * cols // 16:
+            raise ValueError(f"scales[{i}] must hold [{rows}, {cols // 16}] bytes")
         pr = bool(s2_per_row[i]) if s2_per_row is not None else False
         if s2.numel() < (rows if pr else 1):
             raise ValueError(f"s2s[{i}] too small")
         o = outs[i] if outs is not None else torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
-        _check_dev(f"outs[{i}]", o, torch.bfloat16, dev)
+        _check_buf(f"outs[{i}]", o, torch.bfloat16, dev, rows * cols)
         res.append(o)
         arr[i] = _lib.DequantDesc(_p(c), _p(s), _p(s2), 1 if pr else 0, rows, cols, _p(o))
     b = Batch("focus_dequantize_many", arr, (list(codes), list(scales), list(s2s), res), dev)

@@ -423,33 +423,56 @@ int focus_dequantize_mixfp4(const uint8_t* codes, const uint8_t* scales, const f
 int64_t focus_nvfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0 || K <= 0 || M > kMaxTokens || N > kMaxTokens || K > ((int64_t)1 << 40)) return 0;
     if (N > kMaxElems / M / 4) return 0;
-    const int64_t splits = focus::nvfp4_linear_splits(M, N, K, INT64_MAX);
+    int64_t cus = 0;
+    if (focus::nvfp4_linear_cus(cus) != hipSuccess) return -1;
+    const int64_t splits = focus::nvfp4_linear_splits(M, N, K, INT64_MAX, cus);
     return splits > 1 ? splits * M * N * 4 : 0;
 }
 
-int focus_nvfp4_linear(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_s2,
-                       int x_s2_per_row, int64_t M, const uint8_t* w_codes, const uint8_t* w_scales,
-                       const float* w_s2, int64_t N, int64_t K, void* y, int y_dtype, float* workspace,
-                       int64_t workspace_bytes, void* stream) {
+namespace {
+
+int check_linear(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_s2, int x_s2_per_row,
+                 int64_t M, const uint8_t* w_codes, const uint8_t* w_scales, const float* w_s2, int64_t N,
+                 int64_t K, const void* y, int y_dtype) {
     if (M < 0 || N < 0 || K < 0 || K % 16 != 0) return FOCUS_ERR_SHAPE;
     if (M > kMaxTokens || N > kMaxTokens || K > ((int64_t)1 << 40)) return FOCUS_ERR_SHAPE;
     if ((M != 0 && K > kMaxElems / M) || (N != 0 && K > kMaxElems / N) ||
         (M != 0 && N > kMaxElems / M))
         return FOCUS_ERR_SHAPE;
-    if ((x_s2_per_row != 0 && x_s2_per_row != 1) || (y_dtype != 0 && y_dtype != 1) || workspace_bytes < 0)
-        return FOCUS_ERR_RANGE;
+    if ((x_s2_per_row != 0 && x_s2_per_row != 1) || (y_dtype != 0 && y_dtype != 1)) return FOCUS_ERR_RANGE;
     if (M == 0 || N == 0) return FOCUS_OK;
-    if (focus::nvfp4_linear_workgroups(M, N) >= ((int64_t)1 << 24)) return FOCUS_ERR_RANGE;
+    if (focus::nvfp4_linear_workgroups(M, N, INT64_MAX) >= ((int64_t)1 << 24)) return FOCUS_ERR_RANGE;
     if (!x_s2 || !w_s2 || !y || (K > 0 && (!x_codes || !x_scales || !w_codes || !w_scales)))
         return FOCUS_ERR_NULL;
     if (!aligned(x_codes, 8) || !aligned(w_codes, 8) || !aligned(x_s2, 4) || !aligned(w_s2, 4) ||
-        !aligned(y, y_dtype == 0 ? 4 : 2) || !aligned(workspace, 4))
+        !aligned(y, y_dtype == 0 ? 4 : 2))
         return FOCUS_ERR_ALIGN;
+    return FOCUS_OK;
+}
+
+int run_linear(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_s2, int x_s2_per_row, int64_t M,
+               const uint8_t* w_codes, const uint8_t* w_scales, const float* w_s2, int64_t N, int64_t K, void* y,
+               int y_dtype, float* workspace, int64_t workspace_bytes, hipStream_t stream) {
     const focus::GemmArgs a = {x_codes, x_scales, x_s2, x_s2_per_row, M,    w_codes, w_scales, w_s2,
                                N,       K,        y,    workspace,    workspace ? workspace_bytes : 0, 1, 1};
     const bool fast = K > 0 && K % 64 == 0 && aligned(x_codes, 16) && aligned(w_codes, 16) && aligned(x_scales, 4) &&
                       aligned(w_scales, 4);
-    return hip_status(focus::launch_nvfp4_linear(a, fast, y_dtype == 1, (hipStream_t)stream));
+    return hip_status(focus::launch_nvfp4_linear(a, fast, y_dtype == 1, stream));
+}
+
+}  // namespace
+
+int focus_nvfp4_linear(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_s2,
+                       int x_s2_per_row, int64_t M, const uint8_t* w_codes, const uint8_t* w_scales,
+                       const float* w_s2, int64_t N, int64_t K, void* y, int y_dtype, float* workspace,
+                       int64_t workspace_bytes, void* stream) {
+    int st = check_linear(x_codes, x_scales, x_s2, x_s2_per_row, M, w_codes, w_scales, w_s2, N, K, y, y_dtype);
+    if (st != FOCUS_OK) return st;
+    if (workspace_bytes < 0) return FOCUS_ERR_RANGE;
+    if (M == 0 || N == 0) return FOCUS_OK;
+    if (!aligned(workspace, 4)) return FOCUS_ERR_ALIGN;
+    return run_linear(x_codes, x_scales, x_s2, x_s2_per_row, M, w_codes, w_scales, w_s2, N, K, y, y_dtype,
+                      workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -28,12 +28,16 @@ struct GemmArgs {
 // aligned.
 hipError_t launch_nvfp4_linear(const GemmArgs& a, bool fast, bool bf16_out, hipStream_t stream);
 
-// Workgroups one launch uses for an [M, N] output (per k range).
-int64_t nvfp4_linear_workgroups(int64_t M, int64_t N);
+// Compute units of the current device (the split model depends on them).
+hipError_t nvfp4_linear_cus(int64_t& cus);
+
+// Workgroups one launch uses for an [M, N] output (per k range) on a device
+// of `cus` compute units; INT64_MAX gives the largest count of any device.
+int64_t nvfp4_linear_workgroups(int64_t M, int64_t N, int64_t cus);
 
 // k ranges the launcher splits the sum into for [M, N, K] given `part_bytes`
-// of workspace (1 = no split); the workspace it uses is ksplit * M * N * 4
-// bytes.
-int64_t nvfp4_linear_splits(int64_t M, int64_t N, int64_t K, int64_t part_bytes);
+// of workspace and `cus` compute units (1 = no split); the workspace it uses
+// is ksplit * M * N * 4 bytes.
+int64_t nvfp4_linear_splits(int64_t M, int64_t N, int64_t K, int64_t part_bytes, int64_t cus);
 
 }  // namespace focus

@@ -59,6 +59,7 @@
 #include <stdint.h>
 
 #include "focus_gemm.h"
+#include "focus_launch.h"
 #include "focus_numerics.h"
 
 namespace focus {
@@ -579,13 +580,18 @@ __global__ __launch_bounds__(256) void k_nvfp4_linear_finalize(GemmArgs a) {
 // nvfp4_linear_splits): its workgroups are small and all resident at once.
 constexpr int64_t kMinSplitSteps = 4;
 
-static int device_cus() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return 256;
-    return cus;
+// Compute units of the current device.  A failed query is returned (and
+// is the caller's to report); it is never replaced by a guess.
+static hipError_t device_cus(int64_t& cus) {
+    int dev = 0, n = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess && n <= 0) e = hipErrorInvalidDevice;
+    cus = e == hipSuccess ? n : 0;
+    return e;
 }
+
+hipError_t nvfp4_linear_cus(int64_t& cus) { return device_cus(cus); }
 
 // Decode launch configuration for an [M, N] output and `steps` 256-wide
 // k-steps per k range: 16-column tiles per wavefront (2 when that still
@@ -604,12 +610,11 @@ static GemvConfig gemv_config(int64_t M, int64_t N, int64_t steps, int64_t cus) 
     return c;
 }
 
-int64_t nvfp4_linear_splits(int64_t M, int64_t N, int64_t K, int64_t part_bytes) {
-    const int64_t wgs = nvfp4_linear_workgroups(M, N);
+int64_t nvfp4_linear_splits(int64_t M, int64_t N, int64_t K, int64_t part_bytes, int64_t cus) {
+    const int64_t wgs = nvfp4_linear_workgroups(M, N, cus);
     const bool gemv = M <= kGemvMaxM;
     const int64_t nsteps = gemv ? (K + kGemvK - 1) / kGemvK : (K + kBK - 1) / kBK;
     if (wgs <= 0 || nsteps == 0) return 1;
-    const int64_t cus = device_cus();
     const int64_t per = M * N * 4;
     const double t_split = 4.0e-6;  // finalize launch
     const double bw = 5.0e12;       // B/s for the partials
@@ -667,75 +672,63 @@ int64_t nvfp4_linear_splits(int64_t M, int64_t N, int64_t K, int64_t part_bytes)
     return best;
 }
 
+template <bool F, bool B>
+static hipError_t launch_gemv(const GemvConfig& c, dim3 grid, dim3 block, hipStream_t stream, const GemmArgs& a) {
+#define FOCUS_GV(MT, W, T) \
+    case 256 * MT + 16 * T + W: return launch(&k_nvfp4_linear_gemv<F, B, W, T, MT>, grid, block, stream, a);
+    switch (c.mt * 256 + c.t * 16 + c.waves) {
+        FOCUS_GV(1, 8, 1) FOCUS_GV(1, 4, 1) FOCUS_GV(1, 8, 2) FOCUS_GV(1, 4, 2)
+        FOCUS_GV(2, 8, 1) FOCUS_GV(2, 4, 1) FOCUS_GV(2, 8, 2) FOCUS_GV(2, 4, 2)
+        FOCUS_GV(4, 8, 1) FOCUS_GV(4, 4, 1) FOCUS_GV(4, 8, 2) FOCUS_GV(4, 4, 2)
+        FOCUS_GV(8, 4, 1) FOCUS_GV(8, 4, 2)
+    }
+#undef FOCUS_GV
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_nvfp4_linear(const GemmArgs& args, bool fast, bool bf16_out, hipStream_t stream) {
+    int64_t cus = 0;
+    hipError_t e = device_cus(cus);
+    if (e != hipSuccess) return e;
     GemmArgs a = args;
     const bool gemv = a.M <= kGemvMaxM;
     const int64_t nsteps = gemv ? (a.K + kGemvK - 1) / kGemvK : (a.K + kBK - 1) / kBK;
-    a.ksplit = a.part ? nvfp4_linear_splits(a.M, a.N, a.K, a.part_bytes) : 1;
+    a.ksplit = a.part ? nvfp4_linear_splits(a.M, a.N, a.K, a.part_bytes, cus) : 1;
     a.kchunk = a.ksplit > 1 ? (nsteps + a.ksplit - 1) / a.ksplit : (nsteps > 0 ? nsteps : 1);
     const unsigned splits = (unsigned)a.ksplit;
     if (gemv) {
         const bool f = fast && a.K % kGemvK == 0;
-        const GemvConfig c = gemv_config(a.M, a.N, a.kchunk, device_cus());
+        const GemvConfig c = gemv_config(a.M, a.N, a.kchunk, cus);
         const int64_t wgs = (a.N + 16 * c.t - 1) / (16 * c.t);
         const dim3 grid((unsigned)wgs, splits), block(64 * c.waves);
-        const int cfg = c.mt * 256 + c.t * 16 + c.waves;
-#define FOCUS_GV1(F, B, MT)                                                                                     \
-    do {                                                                                                        \
-        if (cfg == 256 * MT + 0x18) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 8, 1, MT>), grid, block, 0, stream, a); \
-        else if (cfg == 256 * MT + 0x14) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 4, 1, MT>), grid, block, 0, stream, a); \
-        else if (cfg == 256 * MT + 0x28) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 8, 2, MT>), grid, block, 0, stream, a); \
-        else if (cfg == 256 * MT + 0x24) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 4, 2, MT>), grid, block, 0, stream, a); \
-    } while (0)
-#define FOCUS_GV(F, B)                                                                                  \
-    do {                                                                                                \
-        FOCUS_GV1(F, B, 1);                                                                             \
-        FOCUS_GV1(F, B, 2);                                                                             \
-        FOCUS_GV1(F, B, 4);                                                                             \
-        if (cfg == 256 * 8 + 0x14) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 4, 1, 8>), grid, block, 0, stream, a); \
-        else if (cfg == 256 * 8 + 0x24) hipLaunchKernelGGL((k_nvfp4_linear_gemv<F, B, 4, 2, 8>), grid, block, 0, stream, a); \
-    } while (0)
-        if (f) {
-            if (bf16_out) FOCUS_GV(true, true);
-            else FOCUS_GV(true, false);
-        } else {
-            if (bf16_out) FOCUS_GV(false, true);
-            else FOCUS_GV(false, false);
-        }
-#undef FOCUS_GV1
-#undef FOCUS_GV
+        if (f) e = bf16_out ? launch_gemv<true, true>(c, grid, block, stream, a)
+                            : launch_gemv<true, false>(c, grid, block, stream, a);
+        else e = bf16_out ? launch_gemv<false, true>(c, grid, block, stream, a)
+                          : launch_gemv<false, false>(c, grid, block, stream, a);
     } else {
         const int64_t tiles_m = (a.M + kBM - 1) / kBM, tiles_n = (a.N + kBN - 1) / kBN;
         const dim3 grid((unsigned)(tiles_m * tiles_n), splits), block(kGemmThreads);
-        if (fast) {
-            if (bf16_out) hipLaunchKernelGGL((k_nvfp4_linear<true, true>), grid, block, 0, stream, a, tiles_n);
-            else hipLaunchKernelGGL((k_nvfp4_linear<true, false>), grid, block, 0, stream, a, tiles_n);
-        } else {
-            if (bf16_out) hipLaunchKernelGGL((k_nvfp4_linear<false, true>), grid, block, 0, stream, a, tiles_n);
-            else hipLaunchKernelGGL((k_nvfp4_linear<false, false>), grid, block, 0, stream, a, tiles_n);
-        }
+        if (fast) e = bf16_out ? launch(&k_nvfp4_linear<true, true>, grid, block, stream, a, tiles_n)
+                               : launch(&k_nvfp4_linear<true, false>, grid, block, stream, a, tiles_n);
+        else e = bf16_out ? launch(&k_nvfp4_linear<false, true>, grid, block, stream, a, tiles_n)
+                          : launch(&k_nvfp4_linear<false, false>, grid, block, stream, a, tiles_n);
     }
-    if (a.ksplit > 1) {
-        const int64_t total = a.M * a.N;
-        const bool vec = total % 4 == 0 && ((uintptr_t)a.part & 15u) == 0 &&
-                         ((uintptr_t)a.y & (bf16_out ? 7u : 15u)) == 0;
-        int64_t g = (total / (vec ? 4 : 1) + 255) / 256;
-        if (g > 65536) g = 65536;
-        const dim3 grid((unsigned)g), block(256);
-        if (vec) {
-            if (bf16_out) hipLaunchKernelGGL((k_nvfp4_linear_finalize<true, true>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((k_nvfp4_linear_finalize<false, true>), grid, block, 0, stream, a);
-        } else {
-            if (bf16_out) hipLaunchKernelGGL((k_nvfp4_linear_finalize<true, false>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((k_nvfp4_linear_finalize<false, false>), grid, block, 0, stream, a);
-        }
-    }
-    return hipGetLastError();
+    if (e != hipSuccess || a.ksplit <= 1) return e;
+    const int64_t total = a.M * a.N;
+    const bool vec = total % 4 == 0 && ((uintptr_t)a.part & 15u) == 0 &&
+                     ((uintptr_t)a.y & (bf16_out ? 7u : 15u)) == 0;
+    int64_t g = (total / (vec ? 4 : 1) + 255) / 256;
+    if (g > 65536) g = 65536;
+    const dim3 grid((unsigned)g), block(256);
+    if (vec) return bf16_out ? launch(&k_nvfp4_linear_finalize<true, true>, grid, block, stream, a)
+                             : launch(&k_nvfp4_linear_finalize<false, true>, grid, block, stream, a);
+    return bf16_out ? launch(&k_nvfp4_linear_finalize<true, false>, grid, block, stream, a)
+                    : launch(&k_nvfp4_linear_finalize<false, false>, grid, block, stream, a);
 }
 
-int64_t nvfp4_linear_workgroups(int64_t M, int64_t N) {
+int64_t nvfp4_linear_workgroups(int64_t M, int64_t N, int64_t cus) {
     if (M <= kGemvMaxM) {
-        const int t = gemv_config(M, N, 1, device_cus()).t;
+        const int t = gemv_config(M, N, 1, cus).t;
         return (N + 16 * t - 1) / (16 * t);
     }
     return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);

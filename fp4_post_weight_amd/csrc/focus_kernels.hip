@@ -59,6 +59,7 @@
 #include <stdint.h>
 
 #include "focus_internal.h"
+#include "focus_launch.h"
 #include "focus_numerics.h"
 
 namespace focus {
@@ -730,10 +731,10 @@ hipError_t launch_tensor_scale(ScaleBatch& bt, hipStream_t stream) {
     }
     bt.tile_start[bt.n] = t;
     const int64_t g = t < kAmaxGrid ? t : kAmaxGrid;
-    hipLaunchKernelGGL(k_clear_acc, dim3(1), dim3(kBatch), 0, stream, bt);
-    hipLaunchKernelGGL(k_amax, dim3((unsigned)g), dim3(kThreads), 0, stream, bt);
-    hipLaunchKernelGGL(k_finalize_s2, dim3(1), dim3(kBatch), 0, stream, bt);
-    return hipGetLastError();
+    hipError_t e = launch(k_clear_acc, dim3(1), dim3(kBatch), stream, bt);
+    if (e == hipSuccess) e = launch(k_amax, dim3((unsigned)g), dim3(kThreads), stream, bt);
+    if (e == hipSuccess) e = launch(k_finalize_s2, dim3(1), dim3(kBatch), stream, bt);
+    return e;
 }
 
 hipError_t launch_quantize(QuantBatch& bt, int key, hipStream_t stream) {
@@ -747,10 +748,8 @@ hipError_t launch_quantize(QuantBatch& bt, int key, hipStream_t stream) {
     bt.tile_start[bt.n] = t;
     const dim3 grid(grid_for_tiles(t)), block(kThreads);
     switch (key) {
-#define FOCUS_Q_CASE(K, HM, HQ, DQ)                                                            \
-    case K:                                                                                    \
-        hipLaunchKernelGGL((k_quantize<HM, HQ, DQ>), grid, block, 0, stream, bt, t);          \
-        break;
+#define FOCUS_Q_CASE(K, HM, HQ, DQ) \
+    case K: return launch(&k_quantize<HM, HQ, DQ>, grid, block, stream, bt, t);
         FOCUS_Q_CASE(0, false, false, false)
         FOCUS_Q_CASE(1, false, false, true)
         FOCUS_Q_CASE(2, false, true, false)
@@ -760,16 +759,10 @@ hipError_t launch_quantize(QuantBatch& bt, int key, hipStream_t stream) {
         FOCUS_Q_CASE(6, true, true, false)
         FOCUS_Q_CASE(7, true, true, true)
 #undef FOCUS_Q_CASE
-        case 8:
-            hipLaunchKernelGGL((k_quantize<false, false, false, 1>), grid, block, 0, stream, bt, t);
-            break;
-        case 9:
-            hipLaunchKernelGGL((k_quantize<false, false, true, 1>), grid, block, 0, stream, bt, t);
-            break;
-#define FOCUS_MX_CASE(K, HM, HQ, DQ)                                                            \
-    case 16 + K:                                                                                \
-        hipLaunchKernelGGL((k_quantize<HM, HQ, DQ, 2>), grid, block, 0, stream, bt, t);        \
-        break;
+        case 8: return launch(&k_quantize<false, false, false, 1>, grid, block, stream, bt, t);
+        case 9: return launch(&k_quantize<false, false, true, 1>, grid, block, stream, bt, t);
+#define FOCUS_MX_CASE(K, HM, HQ, DQ) \
+    case 16 + K: return launch(&k_quantize<HM, HQ, DQ, 2>, grid, block, stream, bt, t);
         FOCUS_MX_CASE(0, false, false, false)
         FOCUS_MX_CASE(1, false, false, true)
         FOCUS_MX_CASE(2, false, true, false)
@@ -780,7 +773,7 @@ hipError_t launch_quantize(QuantBatch& bt, int key, hipStream_t stream) {
         FOCUS_MX_CASE(7, true, true, true)
 #undef FOCUS_MX_CASE
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_quantize_mix(MixBatch& bt, bool deq, hipStream_t stream) {
@@ -791,11 +784,8 @@ hipError_t launch_quantize_mix(MixBatch& bt, bool deq, hipStream_t stream) {
     }
     bt.tile_start[bt.n] = t;
     const dim3 grid(grid_for_tiles(t)), block(kThreads);
-    if (deq)
-        hipLaunchKernelGGL((k_quantize<false, false, true, 3, MixBatch>), grid, block, 0, stream, bt, t);
-    else
-        hipLaunchKernelGGL((k_quantize<false, false, false, 3, MixBatch>), grid, block, 0, stream, bt, t);
-    return hipGetLastError();
+    if (deq) return launch(&k_quantize<false, false, true, 3, MixBatch>, grid, block, stream, bt, t);
+    return launch(&k_quantize<false, false, false, 3, MixBatch>, grid, block, stream, bt, t);
 }
 
 hipError_t launch_dequantize(DequantBatch& bt, bool mx, hipStream_t stream) {
@@ -805,11 +795,9 @@ hipError_t launch_dequantize(DequantBatch& bt, bool mx, hipStream_t stream) {
         t += (bt.nblk[j] + kDeqTile - 1) / kDeqTile;
     }
     bt.tile_start[bt.n] = t;
-    if (mx)
-        hipLaunchKernelGGL(k_dequantize<1>, dim3(grid_for_tiles(t)), dim3(kThreads), 0, stream, bt, t);
-    else
-        hipLaunchKernelGGL(k_dequantize<0>, dim3(grid_for_tiles(t)), dim3(kThreads), 0, stream, bt, t);
-    return hipGetLastError();
+    const dim3 grid(grid_for_tiles(t)), block(kThreads);
+    if (mx) return launch(&k_dequantize<1>, grid, block, stream, bt, t);
+    return launch(&k_dequantize<0>, grid, block, stream, bt, t);
 }
 
 hipError_t launch_dequantize_mix(MixDequantBatch& bt, hipStream_t stream) {
@@ -819,9 +807,7 @@ hipError_t launch_dequantize_mix(MixDequantBatch& bt, hipStream_t stream) {
         t += (bt.nblk[j] + kDeqTile - 1) / kDeqTile;
     }
     bt.tile_start[bt.n] = t;
-    hipLaunchKernelGGL((k_dequantize<2, MixDequantBatch>), dim3(grid_for_tiles(t)), dim3(kThreads), 0, stream,
-                       bt, t);
-    return hipGetLastError();
+    return launch(&k_dequantize<2, MixDequantBatch>, dim3(grid_for_tiles(t)), dim3(kThreads), stream, bt, t);
 }
 
 hipError_t launch_act_per_token(const uint16_t* x, int64_t tokens, int64_t hidden, uint8_t* codes,
@@ -840,28 +826,21 @@ hipError_t launch_act_per_token(const uint16_t* x, int64_t tokens, int64_t hidde
     auto X = reinterpret_cast<const uint4*>(x);
     auto C = reinterpret_cast<uint2*>(codes);
     auto D = reinterpret_cast<uint4*>(xdeq);
-#define FOCUS_ACT_F(RB, F)                                                                     \
-    do {                                                                                       \
-        if (xdeq)                                                                              \
-            hipLaunchKernelGGL((k_act<RB, true, F>), grid, block, 0, stream, X, tokens, nb, C, \
-                               scales, s2_out, D);                                             \
-        else                                                                                   \
-            hipLaunchKernelGGL((k_act<RB, false, F>), grid, block, 0, stream, X, tokens, nb,   \
-                               C, scales, s2_out, D);                                          \
-    } while (0)
-#define FOCUS_ACT(RB)                 \
-    do {                              \
-        if (fo6) FOCUS_ACT_F(RB, true);  \
-        else FOCUS_ACT_F(RB, false);     \
+#define FOCUS_ACT_F(RB, F)                                                                          \
+    return xdeq ? launch(&k_act<RB, true, F>, grid, block, stream, X, tokens, nb, C, scales, s2_out, D) \
+                : launch(&k_act<RB, false, F>, grid, block, stream, X, tokens, nb, C, scales, s2_out, D)
+#define FOCUS_ACT(RB)                      \
+    do {                                   \
+        if (fo6) FOCUS_ACT_F(RB, true);    \
+        FOCUS_ACT_F(RB, false);            \
     } while (0)
     if (nb <= 64) FOCUS_ACT(1);
-    else if (nb <= 128) FOCUS_ACT(2);
-    else if (nb <= 256) FOCUS_ACT(4);
-    else if (nb <= 512) FOCUS_ACT(8);
-    else FOCUS_ACT(0);
+    if (nb <= 128) FOCUS_ACT(2);
+    if (nb <= 256) FOCUS_ACT(4);
+    if (nb <= 512) FOCUS_ACT(8);
+    FOCUS_ACT(0);
 #undef FOCUS_ACT
 #undef FOCUS_ACT_F
-    return hipGetLastError();
 }
 
 }  // namespace focus

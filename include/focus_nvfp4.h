@@ -39,7 +39,9 @@
  *     asynchronous and stream-ordered; none synchronizes.
  *   - Arguments are validated on the host before any HIP call.  A failed
  *     check returns an error status and leaves every output untouched.
- *     FOCUS_ERR_HIP reports a failed kernel launch.
+ *     FOCUS_ERR_HIP reports a failed kernel launch (or a failed device
+ *     query): each launch's own status is checked, so an error left by an
+ *     earlier, unrelated HIP call is neither reported nor cleared.
  *   - Value preconditions are documented, not checked (a check would need a
  *     device-to-host round trip): inputs finite; s2 finite and >= 0; the
  *     denominators (S_b*sigmoid(q_k))*s2 nonzero, which holds for
@@ -309,8 +311,9 @@ int focus_nvfp4_linear(const uint8_t* x_codes, const uint8_t* x_scales, const fl
  * kernel (deterministic).  The call splits only as far as `workspace_bytes`
  * allows (NULL or 0: no split; results then differ from a split call only
  * by the FP32 summation order).  This returns the bytes for the full split
- * on the current device (0 when none helps); the split depends on the
- * device's compute-unit count. */
+ * on the current device (0 when none helps, or when a size is out of range);
+ * the split depends on the device's compute-unit count, and -1 means the
+ * query of that count failed (the HIP error is left for the caller to read). */
 int64_t focus_nvfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus

@@ -259,8 +259,10 @@ def test_linear_workspace(lib):
     assert g(FAKE, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, 64, FAKE, 0, FAKE, -4, None) == ERR_RANGE
     assert g(FAKE, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, 64, FAKE, 0, FAKE + 2, 64, None) == ERR_ALIGN
     ws = lib.focus_nvfp4_linear_workspace_bytes
-    assert ws(8192, 14336, 4096) == 0                 # enough tiles: no split
-    assert ws(2048, 1024, 4096) > 0 and ws(2048, 1024, 4096) % (2048 * 1024 * 4) == 0
-    assert ws(16, 1024, 28672) > 0                    # few tokens, few columns, long rows
-    assert ws(16, 4096, 64) == 0                      # one k-step: nothing to split
-    assert ws(0, 16, 16) == 0 and ws(16, 16, 0) == 0
+    assert ws(0, 16, 16) == 0 and ws(16, 16, 0) == 0  # empty: no query needed
+    # the split depends on the device's compute units; with no device the
+    # query fails and is reported (-1), never replaced by a guess (the split
+    # model itself is checked on the GPU, tests/test_gpu_linear.py)
+    import torch
+    if not torch.cuda.is_available():
+        assert ws(8192, 14336, 4096) == -1

@@ -288,3 +288,14 @@ def test_linear_few_tokens_full_size(focus, orc, M, N, K):
                                 ws[ci].cpu().numpy(), np.float32(3.0e-4))
     got = y[:, torch.from_numpy(ci).to(DEV)].cpu().numpy().astype(np.float64)
     check_bound(got, ref, refabs, K, False, f"{M} x {N} x {K}")
+
+
+def test_split_model_workspace(focus):
+    """The split-k cost model on this GPU's compute units: outputs with enough
+    tiles, or a single k-step, never split; few tiles with long rows do."""
+    ws = focus.nvfp4_linear_workspace_bytes
+    assert ws(8192, 14336, 4096) == 0                 # enough tiles: no split
+    assert ws(2048, 1024, 4096) > 0 and ws(2048, 1024, 4096) % (2048 * 1024 * 4) == 0
+    assert ws(16, 1024, 28672) > 0                    # few tokens, few columns, long rows
+    assert ws(16, 4096, 64) == 0                      # one k-step: nothing to split
+    assert ws(0, 16, 16) == 0 and ws(16, 16, 0) == 0
