@@ -14,15 +14,25 @@ generated on the GPU before the timed region (seeded, synthetic; see
 ``synth``) and stay resident in HBM.
 
 ``value`` is whole-step throughput in Gweights/s (weights of the set per
-second of step time).  ``roofline`` reports the dominant kernel,
+second of step time); ``quantize_gweights_s`` is the quantize + w' phase
+alone (the quantize+pack figure), ``quantize_codes_only_gweights_s`` the
+quantizer without w'.  ``roofline`` reports the dominant kernel,
 focus_quantize with w', against the 8 TB/s HBM peak: algorithmic bytes
 (5.3125 B per weight) / mean launch duration, every launch bracketed by HIP
-events on the stream it runs on.  ``rows`` breaks the step down per call and
-adds the codes-only quantize (3.3125 B per weight) timed after the steps.
-``cpu_baseline`` times the CPU oracle on a bounded sample of the same
-workload on the host's cores.
+events on the stream it runs on, and against a hand-written streaming
+kernel that moves one launch's read and write bytes in the same process.
+``rows`` breaks the step down per call and adds rows timed after the steps
+(codes-only quantize, the adjacent formats, the linear layer, and the
+Llama-3.2-1B-shaped set's step).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8b|1b]
+``parity``: right after the timed steps, every output of the last step
+(s2, amax, scale bytes, codes, w' and the dequantized copy of all 224
+linears, and the per-token activations) is compared with the CPU oracle run
+on the same input bytes; ``parity_1b`` does the same for the 1B set.  The
+oracle's timed quantize passes over the whole set are ``cpu_baseline``.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8b|1b|70b]
+                       [--no-parity] [--no-1b]
 """
 from __future__ import annotations
 
@@ -60,9 +70,13 @@ def parse():
                     help="8b (default): the Llama-3.1-8B-shaped set; 1b: Llama-3.2-1B-shaped; "
                          "70b: Llama-3.1-70B-shaped, processed layer by layer with w' and the "
                          "dequantized copy written to one reused per-layer buffer")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-weights", type=float, default=1.6e9,
-                    help="weights of the set (in linear order) the CPU oracle quantizes")
+    ap.add_argument("--no-parity", "--no-cpu-baseline", dest="no_parity", action="store_true",
+                    help="skip the oracle pass (parity of every output and the CPU baseline), e.g. "
+                         "for profiled runs")
+    ap.add_argument("--no-1b", action="store_true",
+                    help="skip the Llama-3.2-1B-shaped set's step row (8b workload)")
+    ap.add_argument("--cpu-weights", type=float, default=0,
+                    help="stop the oracle pass after this many weights (0: the whole set)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="before the steps, copy a buffer of BYTES bytes three times (a plain copy "
                          "kernel of known traffic, to scale hardware byte counters)")
@@ -104,6 +118,124 @@ def measured_traffic():
     return d.get("bytes_per_launch")
 
 
+def log(msg):
+    print(f"# {msg}", file=sys.stderr, flush=True)
+
+
+class WeightSetRun:
+    """One weight set resident in HBM with its outputs and the prepared
+    batched calls of a step: tensor scale, quantize with w', dequantize (one
+    launch per run of up to 32 linears; per layer for the layered 70B set,
+    whose w' and dequantized copy go to one reused per-layer buffer)."""
+
+    def __init__(self, focus, synth, ws, dev, layered=False):
+        import torch
+        self.ws, self.layered = ws, layered
+        self.lins = ws.linears()
+        self.n_weights = sum(l.numel for l in self.lins)
+        lins = self.lins
+        self.W, self.M, self.Q = [], [], []
+        for lin in lins:
+            w, m, q = synth.make_linear(ws, lin, device=dev)
+            self.W.append(w)
+            self.M.append(m)
+            self.Q.append(q)
+        n = len(lins)
+        self.S2 = torch.empty((n, 1), dtype=torch.float32, device=dev)
+        self.AMAX = torch.empty((n, 1), dtype=torch.float32, device=dev)
+        if layered:
+            per_layer = max(sum(l.numel for l in lins if l.layer == k) for k in range(ws.layers))
+            wdq_buf = torch.empty(per_layer, dtype=torch.bfloat16, device=dev)
+            deq_buf = torch.empty(per_layer, dtype=torch.bfloat16, device=dev)
+            self.WDQ, self.DEQ, off = [], [], {}
+            for l in lins:
+                o = off.get(l.layer, 0)
+                self.WDQ.append(wdq_buf[o:o + l.numel].view(l.rows, l.cols))
+                self.DEQ.append(deq_buf[o:o + l.numel].view(l.rows, l.cols))
+                off[l.layer] = o + l.numel
+            self.chunks = [[i for i, l in enumerate(lins) if l.layer == k] for k in range(ws.layers)]
+        else:
+            self.WDQ = [torch.empty((l.rows, l.cols), dtype=torch.bfloat16, device=dev) for l in lins]
+            self.DEQ = [torch.empty((l.rows, l.cols), dtype=torch.bfloat16, device=dev) for l in lins]
+            self.chunks = [list(range(i, min(i + 32, n))) for i in range(0, n, 32)]
+        self.OUT = [focus.Quantized(torch.empty((l.rows, l.cols // 2), dtype=torch.uint8, device=dev),
+                                    torch.empty((l.rows, l.cols // 16), dtype=torch.uint8, device=dev),
+                                    self.WDQ[i], self.S2[i]) for i, l in enumerate(lins)]
+        c_ = self.chunks
+        W, M, Q, S2, OUT = self.W, self.M, self.Q, self.S2, self.OUT
+        self.TS = [focus.tensor_scale_many([W[i] for i in c], S2[c[0]:c[-1] + 1], self.AMAX[c[0]:c[-1] + 1],
+                                           run=False) for c in c_]
+        self.QB = [focus.quantize_many([W[i] for i in c], [M[i] for i in c], [Q[i] for i in c],
+                                       [S2[i] for i in c], outs=[OUT[i] for i in c], dequant=True, run=False)
+                   for c in c_]
+        self.QB_nodq = [focus.quantize_many([W[i] for i in c], [M[i] for i in c], [Q[i] for i in c],
+                                            [S2[i] for i in c], outs=[OUT[i] for i in c], dequant=False,
+                                            run=False) for c in c_]
+        self.DB = [focus.dequantize_many([OUT[i].codes for i in c], [OUT[i].scales for i in c],
+                                         [S2[i] for i in c], outs=[self.DEQ[i] for i in c], run=False)
+                   for c in c_]
+
+    def step(self, rec=None, q_rec=None):
+        """tensor scale -> quantize + w' -> dequantize of every linear;
+        rec(k) records phase boundary k (0: start, 1: scales done, 2:
+        quantize done, 3: dequantize done); q_rec(i, 0/1) brackets quantize
+        launch i."""
+        rec = rec or (lambda k: None)
+        rec(0)
+        for b in self.TS:
+            b.run()
+        rec(1)
+        for i, b in enumerate(self.QB):
+            if q_rec:
+                q_rec(i, 0)
+            b.run()
+            if q_rec:
+                q_rec(i, 1)
+        rec(2)
+        for b in self.DB:
+            b.run()
+        rec(3)
+
+
+def stream_ceiling(dev, read_bytes, write_bytes, reps=5):
+    """The hand-written streaming kernel (tests/hip/focus_stream.hip) moving
+    `read_bytes` in and `write_bytes` out in one launch, timed with HIP
+    events on the stream it runs on; the faster of plain and nontemporal
+    loads.  Returns (ms, GB/s)."""
+    import ctypes as ct
+
+    import torch
+    path = os.path.join(ROOT, "tests", "hip", "libfocus_stream.so")
+    lib = ct.CDLL(path)
+    lib.focus_stream.restype = ct.c_int
+    lib.focus_stream.argtypes = [ct.c_void_p, ct.c_int64, ct.c_void_p, ct.c_int64, ct.c_void_p, ct.c_int,
+                                 ct.c_int64, ct.c_void_p]
+    nr, nw = int(read_bytes) // 16, int(write_bytes) // 16
+    src = torch.ones(nr * 4, dtype=torch.int32, device=dev)
+    dst = torch.empty(nw * 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    best = None
+    for nt in (0, 1):
+        def call():
+            st = lib.focus_stream(src.data_ptr(), nr, dst.data_ptr(), nw, sink.data_ptr(), nt, 0,
+                                  stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"focus_stream failed with HIP error {st}")
+        call()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        best = ms if best is None else min(best, ms)
+    del src, dst, sink
+    return best, (nr + nw) * 16 / (best * 1e-3) / 1e9
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -122,41 +254,15 @@ def main():
     torch.cuda.set_device(dev)
     ws = {"8b": synth.LLAMA_8B, "1b": synth.LLAMA_1B, "70b": synth.LLAMA_70B}[args.workload]
     layered = args.workload == "70b"
-    lins = ws.linears()
-    n_weights = sum(l.numel for l in lins)
 
     # ---- inputs (resident in HBM) and outputs ----------------------------
     t0 = time.time()
-    W, M, Q = [], [], []
-    for lin in lins:
-        w, m, q = synth.make_linear(ws, lin, device=dev)
-        W.append(w)
-        M.append(m)
-        Q.append(q)
+    R = WeightSetRun(focus, synth, ws, dev, layered)
+    lins, n_weights, nlin = R.lins, R.n_weights, len(R.lins)
+    W, M, Q, S2, OUT = R.W, R.M, R.Q, R.S2, R.OUT
     X = synth.make_activations(device=dev)
-    S2 = torch.empty((len(lins), 1), dtype=torch.float32, device=dev)
-    AMAX = torch.empty((len(lins), 1), dtype=torch.float32, device=dev)
-    if layered:
-        # w' and the dequantized copy of one layer at a time: every layer's
-        # linears are views of one reused buffer each
-        per_layer = max(sum(l.numel for l in lins if l.layer == k) for k in range(ws.layers))
-        wdq_buf = torch.empty(per_layer, dtype=torch.bfloat16, device=dev)
-        deq_buf = torch.empty(per_layer, dtype=torch.bfloat16, device=dev)
-        WDQ, DEQ, off = [], [], {}
-        for l in lins:
-            o = off.get(l.layer, 0)
-            WDQ.append(wdq_buf[o:o + l.numel].view(l.rows, l.cols))
-            DEQ.append(deq_buf[o:o + l.numel].view(l.rows, l.cols))
-            off[l.layer] = o + l.numel
-    else:
-        WDQ = [torch.empty((l.rows, l.cols), dtype=torch.bfloat16, device=dev) for l in lins]
-        DEQ = [torch.empty((l.rows, l.cols), dtype=torch.bfloat16, device=dev) for l in lins]
-    OUT = [focus.Quantized(torch.empty((l.rows, l.cols // 2), dtype=torch.uint8, device=dev),
-                           torch.empty((l.rows, l.cols // 16), dtype=torch.uint8, device=dev),
-                           WDQ[i], S2[i]) for i, l in enumerate(lins)]
     ACT = focus.quantize_act_per_token(X)
     torch.cuda.synchronize()
-    gen_s = time.time() - t0
     if args.copy_calibration > 0:
         src = torch.ones(args.copy_calibration, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -164,50 +270,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    print(f"# generated {ws.name}: {n_weights} weights in {gen_s:.1f} s", file=sys.stderr, flush=True)
+    log(f"generated {ws.name}: {n_weights} weights in {time.time() - t0:.1f} s")
 
     stream = torch.cuda.current_stream(dev)
-    nlin = len(lins)
-
-    # Prepared batched calls, 32 linears each: every quantize / dequantize
-    # batch is exactly one kernel launch, every tensor-scale batch three.
-    if layered:
-        chunks = [[i for i, l in enumerate(lins) if l.layer == k] for k in range(ws.layers)]
-    else:
-        chunks = [list(range(i, min(i + 32, nlin))) for i in range(0, nlin, 32)]
-    TS = [focus.tensor_scale_many([W[i] for i in c], S2[c[0]:c[-1] + 1], AMAX[c[0]:c[-1] + 1], run=False)
-          for c in chunks]
-    QB = [focus.quantize_many([W[i] for i in c], [M[i] for i in c], [Q[i] for i in c], [S2[i] for i in c],
-                              outs=[OUT[i] for i in c], dequant=True, run=False) for c in chunks]
-    QB_nodq = [focus.quantize_many([W[i] for i in c], [M[i] for i in c], [Q[i] for i in c],
-                                   [S2[i] for i in c], outs=[OUT[i] for i in c], dequant=False, run=False)
-               for c in chunks]
-    extra_rows = not layered
-    FB = [] if not extra_rows else [focus.quantize_fo6_many([W[i] for i in c], [S2[i] for i in c], outs=[OUT[i] for i in c],
-                                  dequant=False, run=False) for c in chunks]
-    M32 = [] if not extra_rows else [
-        synth.block_factor_lognormal((l.rows, l.cols // 32), seed=42, tensor_id=l.tid(1), device=dev)
-        for l in lins]
-    MXB = [] if not extra_rows else [focus.quantize_mx_many([W[i] for i in c], [M32[i] for i in c], [Q[i] for i in c],
-                                  outs=[focus.Quantized(OUT[i].codes, OUT[i].scales.view(-1)[:lins[i].numel // 32]
-                                                        .view(lins[i].rows, lins[i].cols // 32), OUT[i].deq, None)
-                                        for i in c], dequant=True, run=False) for c in chunks]
-    MXB_nodq = [] if not extra_rows else [focus.quantize_mx_many([W[i] for i in c], [M32[i] for i in c], [Q[i] for i in c],
-                                       outs=[focus.Quantized(OUT[i].codes,
-                                                             OUT[i].scales.view(-1)[:lins[i].numel // 32]
-                                                             .view(lins[i].rows, lins[i].cols // 32), None, None)
-                                             for i in c], dequant=False, run=False) for c in chunks]
-    MIX_TILES = [(8, 64), (16, 64), (256, 64)]
-    MAPS = {} if not extra_rows else {
-        t: [synth.tile_map(l.rows, l.cols, t, frac=synth.MIXFP4_FRAC[t], seed=42, tensor_id=l.tid(3), device=dev)
-            for l in lins] for t in MIX_TILES}
-    MIXB = {} if not extra_rows else {
-        t: [focus.quantize_mixfp4_many([W[i] for i in c], [MAPS[t][i] for i in c], [t] * len(c),
-                                       [S2[i] for i in c], outs=[OUT[i] for i in c], dequant=True, run=False)
-            for c in chunks] for t in MIX_TILES}
-    DB = [focus.dequantize_many([OUT[i].codes for i in c], [OUT[i].scales for i in c], [S2[i] for i in c],
-                                outs=[DEQ[i] for i in c], run=False) for c in chunks]
-    nq = len(QB)
+    nq = len(R.QB)
 
     # events of one step: [0] start, [1] tensor scales done, a pair around
     # each quantize launch, quantize phase done, dequantize done, act done
@@ -215,21 +281,14 @@ def main():
     E_TS, E_Q0, E_QEND, E_DQ, E_ACT = 1, 2, 2 + 2 * nq, 3 + 2 * nq, 4 + 2 * nq
 
     def step(ev=None):
-        rec = (lambda j: ev[j].record(stream)) if ev is not None else (lambda j: None)
-        rec(0)
-        for b in TS:
-            b.run()
-        rec(E_TS)
-        for i, b in enumerate(QB):
-            rec(E_Q0 + 2 * i)
-            b.run()
-            rec(E_Q0 + 2 * i + 1)
-        rec(E_QEND)
-        for b in DB:
-            b.run()
-        rec(E_DQ)
+        if ev is None:
+            R.step()
+        else:
+            pos = {0: 0, 1: E_TS, 2: E_QEND, 3: E_DQ}
+            R.step(lambda k: ev[pos[k]].record(stream), lambda i, e: ev[E_Q0 + 2 * i + e].record(stream))
         focus.quantize_act_per_token(X, out=ACT)
-        rec(E_ACT)
+        if ev is not None:
+            ev[E_ACT].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -245,6 +304,7 @@ def main():
     wall = time.perf_counter() - t_wall
     gpu_ms = events[0][0].elapsed_time(events[-1][E_ACT])
     ms_step = max(gpu_ms, wall * 1e3) / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms per step")
 
     q_launch_ms = []
     phase = {"tensor_scale": 0.0, "quantize_dq": 0.0, "dequantize": 0.0, "act": 0.0}
@@ -261,6 +321,13 @@ def main():
     bytes_per_launch = B_QUANT_DQ * n_weights / nq
     achieved = bytes_per_launch / (mean_launch_ms * 1e-3) / 1e9
 
+    # ---- parity of every output of the timed steps against the oracle -----
+    # (before any later row overwrites the output buffers); its oracle pass
+    # is also the CPU baseline
+    par, cpu = None, None
+    if not args.no_parity:
+        par, cpu = check_set(R, X, ACT, args, layered)
+
     # ---- per-call rows outside the steps: each call alone, same buffers ----
     def time_calls(fn, reps=5):
         fn()
@@ -273,26 +340,12 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
-    t_q = time_calls(lambda: [b.run() for b in QB_nodq])
-    if extra_rows:
-        t_f6 = time_calls(lambda: [b.run() for b in FB])
-        t_mx = time_calls(lambda: [b.run() for b in MXB])
-        t_mxn = time_calls(lambda: [b.run() for b in MXB_nodq])
-        ACT6 = focus.quantize_act_per_token_fo6(X)
-        t_a6 = time_calls(lambda: focus.quantize_act_per_token_fo6(X, out=ACT6), reps=20)
-        t_mix = {t: time_calls(lambda t=t: [b.run() for b in MIXB[t]]) for t in MIX_TILES}
-        # per-token activations on a tensor too large for any cache (1 GiB)
-        XL = synth.make_activations((131072, 4096), device=dev)
-        ACTL = focus.quantize_act_per_token(XL)
-        t_al = time_calls(lambda: focus.quantize_act_per_token(XL, out=ACTL), reps=10)
-        del XL, ACTL
-    torch.cuda.synchronize()
-
     def row(ms, nbytes, units):
         gbs = nbytes / (ms * 1e-3) / 1e9
         return {"ms": round(ms, 4), "GB_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                 "Gunits_s": round(units / (ms * 1e-3) / 1e9, 2)}
 
+    t_q = time_calls(lambda: [b.run() for b in R.QB_nodq])
     rows = {
         "tensor_scale (step phase)": row(phase["tensor_scale"], B_TENSOR_SCALE * n_weights, n_weights),
         "quantize + w' (step phase)": row(phase["quantize_dq"], B_QUANT_DQ * n_weights, n_weights),
@@ -301,36 +354,103 @@ def main():
                                                       X.numel()),
         "quantize codes only (after the steps)": row(t_q, B_QUANT * n_weights, n_weights),
     }
+    extra_rows = not layered
     if extra_rows:
+        chunks = R.chunks
+        FB = [focus.quantize_fo6_many([W[i] for i in c], [S2[i] for i in c], outs=[OUT[i] for i in c],
+                                      dequant=False, run=False) for c in chunks]
+        M32 = [synth.block_factor_lognormal((l.rows, l.cols // 32), seed=42, tensor_id=l.tid(1), device=dev)
+               for l in lins]
+
+        def mx_out(i, dq):
+            sc = OUT[i].scales.view(-1)[:lins[i].numel // 32].view(lins[i].rows, lins[i].cols // 32)
+            return focus.Quantized(OUT[i].codes, sc, OUT[i].deq if dq else None, None)
+
+        MXB = [focus.quantize_mx_many([W[i] for i in c], [M32[i] for i in c], [Q[i] for i in c],
+                                      outs=[mx_out(i, True) for i in c], dequant=True, run=False) for c in chunks]
+        MXB_nodq = [focus.quantize_mx_many([W[i] for i in c], [M32[i] for i in c], [Q[i] for i in c],
+                                           outs=[mx_out(i, False) for i in c], dequant=False, run=False)
+                    for c in chunks]
+        MIX_TILES = [(8, 64), (16, 64), (256, 64)]
+        MAPS = {t: [synth.tile_map(l.rows, l.cols, t, frac=synth.MIXFP4_FRAC[t], seed=42, tensor_id=l.tid(3),
+                                   device=dev) for l in lins] for t in MIX_TILES}
+        MIXB = {t: [focus.quantize_mixfp4_many([W[i] for i in c], [MAPS[t][i] for i in c], [t] * len(c),
+                                               [S2[i] for i in c], outs=[OUT[i] for i in c], dequant=True,
+                                               run=False) for c in chunks] for t in MIX_TILES}
+        t_f6 = time_calls(lambda: [b.run() for b in FB])
+        t_mx = time_calls(lambda: [b.run() for b in MXB])
+        t_mxn = time_calls(lambda: [b.run() for b in MXB_nodq])
+        ACT6 = focus.quantize_act_per_token_fo6(X)
+        t_a6 = time_calls(lambda: focus.quantize_act_per_token_fo6(X, out=ACT6), reps=20)
+        t_mix = {t: time_calls(lambda t=t: [b.run() for b in MIXB[t]]) for t in MIX_TILES}
+        del MAPS, MIXB, M32, MXB, MXB_nodq, FB
+        # per-token activations on a tensor too large for any cache (1 GiB)
+        XL = synth.make_activations((131072, 4096), device=dev)
+        ACTL = focus.quantize_act_per_token(XL)
+        t_al = time_calls(lambda: focus.quantize_act_per_token(XL, out=ACTL), reps=10)
+        ACT6L = focus.quantize_act_per_token_fo6(XL)
+        t_a6l = time_calls(lambda: focus.quantize_act_per_token_fo6(XL, out=ACT6L), reps=10)
+        del XL, ACTL, ACT6L
         rows.update({
             "FourOverSix weights, codes only (after the steps)": row(t_f6, B_ACT * n_weights, n_weights),
             "FOCUS on MXFP4 + w' (after the steps)": row(t_mx, (B_MX + 2.0) * n_weights, n_weights),
             "FOCUS on MXFP4 codes only (after the steps)": row(t_mxn, B_MX * n_weights, n_weights),
             "FourOverSix act per token [8192,4096] (after the steps, cache-resident)":
                 row(t_a6, B_ACT * X.numel() + 4 * X.shape[0], X.numel()),
+            "act per token [131072,4096] (after the steps)":
+                row(t_al, B_ACT * 131072 * 4096 + 4 * 131072, 131072 * 4096),
+            "FourOverSix act per token [131072,4096] (after the steps)":
+                row(t_a6l, B_ACT * 131072 * 4096 + 4 * 131072, 131072 * 4096),
         })
-        rows["act per token [131072,4096] (after the steps)"] = row(t_al, B_ACT * 131072 * 4096 + 4 * 131072,
-                                                                     131072 * 4096)
         for (th, tw) in MIX_TILES:
             share = synth.MIXFP4_FRAC[(th, tw)]
             rows[f"FlipQuant MixFP4 {th}x{tw} map ({100 * share:.2f}% E0M3 tiles) + w' (after the steps)"] = \
                 row(t_mix[(th, tw)], (B_ACT + 2.0 + 1.0 / (th * tw)) * n_weights, n_weights)
+    torch.cuda.synchronize()
+    log("rows after the steps done")
 
-    # streaming ceiling on this GPU: a plain device copy of 2 GiB (read + write)
+    # ---- streaming ceiling: a hand-written kernel moving the bytes of one
+    # quantize + w' launch (W, m, q in; codes, scales, w' out), same process
+    per_launch_w = n_weights / nq
+    rd, wr = (2.0 + 0.25 + 0.5) * per_launch_w, (0.5 + 0.0625 + 2.0) * per_launch_w
+    t_sc, ceil_gbs = stream_ceiling(dev, rd, wr)
+    rows["streaming kernel at one quantize + w' launch's read and write bytes (ceiling, after the steps)"] = \
+        row(t_sc, rd + wr, per_launch_w)
     csrc = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
     cdst = torch.empty_like(csrc)
     t_cp = time_calls(lambda: cdst.copy_(csrc), reps=5)
     del csrc, cdst
-    copy_gbs = 2.0 * (1 << 31) / (t_cp * 1e-3) / 1e9
-    rows["device copy 2 GiB (streaming ceiling, after the steps)"] = row(t_cp, 2.0 * (1 << 31), 1 << 31)
+    rows["runtime device copy 2 GiB (after the steps)"] = row(t_cp, 2.0 * (1 << 31), 1 << 31)
+
     if extra_rows:
         rows.update(linear_rows(focus, synth, ws, dev, stream))
         rows.update(decode_graph_row(focus, synth, ws, dev))
+        log("linear-layer rows done")
 
-    # ---- CPU baseline: the oracle on a bounded sample ----------------------
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(lins, W, M, Q, X, args.cpu_weights)
+    # ---- the Llama-3.2-1B-shaped set: the same step, with parity --------------
+    par_1b = None
+    if args.workload == "8b" and not args.no_1b:
+        R1 = WeightSetRun(focus, synth, synth.LLAMA_1B, dev)
+        for _ in range(args.warmup):
+            R1.step()
+        torch.cuda.synchronize()
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(4 * args.steps)]
+        for k in range(args.steps):
+            R1.step(lambda j, k=k: e1[4 * k + j].record(stream))
+        torch.cuda.synchronize()
+        ph1 = [sum(e1[4 * k + j].elapsed_time(e1[4 * k + j + 1]) for k in range(args.steps)) / args.steps
+               for j in range(3)]
+        step1 = sum(e1[4 * k].elapsed_time(e1[4 * k + 3]) for k in range(args.steps)) / args.steps
+        n1 = R1.n_weights
+        r1 = row(step1, (B_TENSOR_SCALE + B_QUANT_DQ + B_DEQUANT) * n1, n1)
+        r1["quantize + w' ms"] = round(ph1[1], 4)
+        r1["quantize + w' frac_hbm_peak"] = round(B_QUANT_DQ * n1 / (ph1[1] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        rows[f"{synth.LLAMA_1B.name} step: tensor_scale + quantize + w' + dequantize "
+             f"(after the 8B rows)"] = r1
+        log(f"1B set step {step1:.3f} ms")
+        if not args.no_parity:
+            par_1b, _ = check_set(R1, None, None, args, False, label="1B")
+        del R1
 
     line = {
         "metric": METRIC if args.workload == "8b" else METRIC.replace("8B set", f"{args.workload.upper()} set"),
@@ -354,6 +474,8 @@ def main():
             "linears": nlin,
             "m": "LogNormal(0, 0.1)", "q": "N(6, 2)", "W": "N(0, %g) + 0.1%% outliers x20" % ws.std,
         },
+        "quantize_gweights_s": round(n_weights / (phase["quantize_dq"] * 1e-3) / 1e9, 2),
+        "quantize_codes_only_gweights_s": round(n_weights / (t_q * 1e-3) / 1e9, 2),
         "roofline": {
             "kernel": "focus_quantize (codes + scales + w')",
             "bound": "hbm",
@@ -363,18 +485,182 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic() if args.workload == "8b" else None,
             "bytes_per_weight": B_QUANT_DQ,
+            "weights_per_launch": round(n_weights / nq),
             "mean_launch_ms": round(mean_launch_ms, 5),
             "launches": len(q_launch_ms),
             "launches_per_step": nq,
-            "copy_ceiling_GB_s": round(copy_gbs, 1),
-            "frac_of_copy_ceiling": round(achieved / copy_gbs, 4),
+            "timed_launches_in_trace": [args.warmup * nq, (args.warmup + args.steps) * nq],
+            "stream_ceiling_GB_s": round(ceil_gbs, 1),
+            "frac_of_ceiling": round(achieved / ceil_gbs, 4),
         },
+        "parity": par,
+        "parity_1b": par_1b,
         "cpu_baseline": cpu,
         "rows": rows,
         "wall_s_timed": round(wall, 3),
         "gpu_ms_timed": round(gpu_ms, 3),
     }
     print(json.dumps(line), flush=True)
+
+
+def check_set(R, X, ACT, args, layered, label="8B"):
+    """Every output of the last timed step against the oracle run on the same
+    input bytes (copied to the host): s2 and amax of every linear, scale
+    bytes, codes and w' (from the quantizer and from the dequantize call) of
+    every linear, and the per-token activations.  Parity rule as in
+    tests/parity.py: scales and s2 bit-exact, at most 1e-6 of the codes one
+    step apart where sigmoid rounding explains it, w' exact where codes
+    agree.  The layered 70B set checks layers 0, L/2 and L-1 (w' of the last
+    layer only: the per-layer buffer is reused).  The oracle's quantize
+    passes are timed (all host cores, row chunks) and give the CPU baseline.
+    Returns (parity dict, cpu_baseline dict)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import parity as prule
+
+    o = oracle.default()
+    n_thr = prule.threads()
+    lins = R.lins
+    if layered:
+        L = R.ws.layers
+        keep = {0, L // 2, L - 1}
+        todo = [i for i, l in enumerate(lins) if l.layer in keep]
+        with_w = {i for i in todo if lins[i].layer == L - 1}
+    else:
+        todo = list(range(len(lins)))
+        with_w = set(todo)
+    limit = args.cpu_weights if args.cpu_weights > 0 else float("inf")
+    S2h = R.S2.view(-1).cpu().numpy()
+    AMh = R.AMAX.view(-1).cpu().numpy()
+
+    def fetch(i):
+        wb = synth.bits(R.W[i])
+        h = {"wb": wb, "m": R.M[i].cpu().numpy(), "q": R.Q[i].cpu().numpy(),
+             "codes": R.OUT[i].codes.cpu().numpy(), "scales": R.OUT[i].scales.cpu().numpy()}
+        if i in with_w:
+            h["wdq"] = synth.bits(R.WDQ[i])
+            h["deq"] = synth.bits(R.DEQ[i])
+        h["s2o"], h["amaxo"] = o.tensor_scale(wb)  # the oracle's own tensor scale
+        return h
+
+    tot = {"tensors": 0, "weights_checked": 0, "s2_mismatches": 0, "amax_mismatches": 0,
+           "scale_mismatches": 0, "code_mismatches": 0, "wdeq_mismatches": 0, "dequantize_mismatches": 0,
+           "wdeq_weights_checked": 0, "failures": []}
+    oracle_s, oracle_w = 0.0, 0
+    t_all = time.perf_counter()
+    with ThreadPoolExecutor(n_thr) as pool, ThreadPoolExecutor(1) as pre:
+        nxt = pre.submit(fetch, todo[0]) if todo else None
+        for pos, i in enumerate(todo):
+            if tot["weights_checked"] >= limit:
+                break
+            h = nxt.result()
+            nxt = pre.submit(fetch, todo[pos + 1]) if pos + 1 < len(todo) else None
+            rows = lins[i].rows
+            dq = "wdq" in h
+            bounds = np.linspace(0, rows, min(n_thr, rows) + 1).astype(int)
+            parts = [(bounds[k], bounds[k + 1]) for k in range(len(bounds) - 1) if bounds[k + 1] > bounds[k]]
+            t0 = time.perf_counter()
+            refs = list(pool.map(lambda ab: o.quantize(h["wb"][ab[0]:ab[1]], h["m"][ab[0]:ab[1]],
+                                                       h["q"][ab[0]:ab[1]], h["s2o"], dq), parts))
+            oracle_s += time.perf_counter() - t0
+            oracle_w += lins[i].numel
+
+            def compare(k):
+                a, b = parts[k]
+                codes, scales, wdq = refs[k]
+                out = {"scale": int(np.count_nonzero(h["scales"][a:b] != scales)), "code": 0, "wdq": 0,
+                       "deq": 0, "err": None}
+                if np.array_equal(h["codes"][a:b], codes):
+                    agree = None
+                else:
+                    try:  # the full rule: one step, explained by sigmoid rounding, within 1e-6
+                        st = prule.check_quantized(o, h["wb"][a:b], h["m"][a:b], h["q"][a:b], h["s2o"],
+                                                   h["codes"][a:b], h["scales"][a:b],
+                                                   h["wdq"][a:b] if dq else None, ref=refs[k],
+                                                   label=f"{label} linear {i} rows {a}:{b}",
+                                                   count_limit=(b - a) * h["codes"].shape[1] * 2)
+                        out["code"] = st["code_mismatches"]
+                    except AssertionError as e:
+                        out["err"] = str(e)[:300]
+                        out["code"] = -1
+                    agree = (prule.unpack(h["codes"][a:b]) == prule.unpack(codes))
+                if dq:
+                    for key, name in (("wdq", "wdq"), ("deq", "deq")):
+                        diff = h[key][a:b] != wdq
+                        if agree is not None:
+                            diff &= agree
+                        out[name] = int(np.count_nonzero(diff))
+                return out
+
+            res = list(pool.map(compare, range(len(parts))))
+            tot["tensors"] += 1
+            tot["weights_checked"] += lins[i].numel
+            if dq:
+                tot["wdeq_weights_checked"] += lins[i].numel
+            if S2h[i].view(np.uint32) != np.float32(h["s2o"]).view(np.uint32):
+                tot["s2_mismatches"] += 1
+            if AMh[i].view(np.uint32) != np.float32(h["amaxo"]).view(np.uint32):
+                tot["amax_mismatches"] += 1
+            for r in res:
+                tot["scale_mismatches"] += r["scale"]
+                tot["code_mismatches"] += max(r["code"], 0)
+                tot["wdeq_mismatches"] += r["wdq"]
+                tot["dequantize_mismatches"] += r["deq"]
+                if r["err"] and len(tot["failures"]) < 4:
+                    tot["failures"].append(r["err"])
+            if pos % 16 == 15 or pos == len(todo) - 1:
+                log(f"{label} parity: {tot['tensors']}/{len(todo)} linears, {tot['weights_checked']} weights, "
+                    f"{time.perf_counter() - t_all:.0f} s")
+        if X is not None:
+            xb = synth.bits(X)
+            codes, scales, s2t, _ = prule.oracle_act_rows(o, xb, dequant=False, n_threads=n_thr)
+            tot["act_tokens"] = int(xb.shape[0])
+            tot["act_scale_mismatches"] = int(np.count_nonzero(ACT.scales.cpu().numpy() != scales))
+            tot["act_code_mismatches"] = int(np.count_nonzero(prule.unpack(ACT.codes.cpu().numpy()) !=
+                                                              prule.unpack(codes)))
+            tot["act_s2_mismatches"] = int(np.count_nonzero(ACT.s2.cpu().numpy().view(np.uint32) !=
+                                                            s2t.view(np.uint32)))
+    allowed = int(np.floor(prule.CODE_MISMATCH_RATE * tot["weights_checked"]))
+    tot["code_mismatches_allowed"] = allowed
+    tot["seconds"] = round(time.perf_counter() - t_all, 1)
+    tot["ok"] = (not tot["failures"] and tot["s2_mismatches"] == 0 and tot["amax_mismatches"] == 0 and
+                 tot["scale_mismatches"] == 0 and tot["code_mismatches"] <= allowed and
+                 tot["wdeq_mismatches"] == 0 and tot["dequantize_mismatches"] == 0 and
+                 tot.get("act_scale_mismatches", 0) == 0 and tot.get("act_code_mismatches", 0) == 0 and
+                 tot.get("act_s2_mismatches", 0) == 0)
+    if not tot["failures"]:
+        del tot["failures"]
+    log(f"{label} parity: {'ok' if tot['ok'] else 'FAILED'} in {tot['seconds']} s")
+    cpu = None
+    if oracle_w:
+        # one core: the oracle's quantize on the first 32 M weights of the set
+        wb = synth.bits(R.W[0])
+        r1 = max(1, min(wb.shape[0], (1 << 25) // wb.shape[1]))
+        s2o, _ = o.tensor_scale(wb)
+        m1, q1 = R.M[0][:r1].cpu().numpy(), R.Q[0][:r1].cpu().numpy()
+        t1 = time.perf_counter()
+        o.quantize(wb[:r1], m1, q1, s2o, True)
+        per_core = r1 * wb.shape[1] / (time.perf_counter() - t1) / 1e9
+        model = "unknown"
+        try:
+            with open("/proc/cpuinfo") as f:
+                model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+        except OSError:
+            pass
+        cpu = {"value": round(oracle_w / oracle_s / 1e9, 5), "unit": "Gweights/s", "cores": n_thr,
+               "per_core_value": round(per_core, 5), "cpu_model": model, "kind": "oracle",
+               "seconds": round(oracle_s, 2),
+               "sample": f"the oracle's quantize (codes, E4M3 scales, w') of {oracle_w} weights "
+                         f"({tot['tensors']} linears of the {R.ws.name}, whole tensors, row chunks on "
+                         f"{n_thr} host threads), on the same input bytes as the GPU; the same pass "
+                         f"is the parity check"}
+    return tot, cpu
 
 
 def linear_rows(focus, synth, ws, dev, stream):
@@ -475,75 +761,6 @@ def decode_graph_row(focus, synth, ws, dev, m_tok=16, reps=50):
     del graph, keep
     return {key: {"ms": round(ms, 4), "TFLOP_s": round(flop / (ms * 1e-3) / 1e12, 1),
                   "GB_s": round(byts / (ms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
-
-
-def cpu_baseline(lins, W, M, Q, X, budget):
-    """The oracle, unchanged, on the first `budget` weights of the set in
-    linear order (whole tensors, the last one cut by rows): s2 of each full
-    tensor, then quantize (+ w') and dequantize, and per-token activations of
-    the first 512 tokens; row chunks run on the host's cores through ctypes
-    (which releases the GIL)."""
-    from concurrent.futures import ThreadPoolExecutor
-
-    import numpy as np
-
-    import oracle
-    import synth
-
-    o = oracle.default()
-    try:
-        n_thr = len(os.sched_getaffinity(0))
-    except AttributeError:
-        n_thr = os.cpu_count() or 1
-    n_thr = max(1, min(n_thr, 64))
-    host, left = [], int(budget)
-    for i, lin in enumerate(lins):
-        if left <= 0:
-            break
-        wb = synth.bits(W[i])
-        r = max(1, min(lin.rows, left // lin.cols))
-        host.append((wb, M[i][:r].cpu().numpy(), Q[i][:r].cpu().numpy(), r))
-        left -= r * lin.cols
-    xb = synth.bits(X[:512])
-    weights = 0
-    t0 = time.perf_counter()
-    with ThreadPoolExecutor(n_thr) as ex:
-        for wb, m, q, r in host:
-            s2, _ = o.tensor_scale(wb)
-            bounds = np.linspace(0, r, n_thr + 1).astype(int)
-
-            def work(k, wb=wb, m=m, q=q, s2=s2, bounds=bounds):
-                a, b = bounds[k], bounds[k + 1]
-                if b <= a:
-                    return 0
-                codes, scales, _ = o.quantize(wb[a:b], m[a:b], q[a:b], s2, True)
-                o.dequantize(codes, scales, s2)
-                return (b - a) * wb.shape[1]
-
-            weights += sum(ex.map(work, range(n_thr)))
-        tb = np.linspace(0, xb.shape[0], n_thr + 1).astype(int)
-        list(ex.map(lambda k: o.quantize_act_per_token(xb[tb[k]:tb[k + 1]]), range(n_thr)))
-    dt = time.perf_counter() - t0
-    # one core: the first 32 M weights of the same sample on one thread
-    wb, m, q, r = host[0]
-    r1 = max(1, min(r, (1 << 25) // wb.shape[1]))
-    s2, _ = o.tensor_scale(wb)
-    t1 = time.perf_counter()
-    codes, scales, _ = o.quantize(wb[:r1], m[:r1], q[:r1], s2, True)
-    o.dequantize(codes, scales, s2)
-    per_core = r1 * wb.shape[1] / (time.perf_counter() - t1) / 1e9
-    model = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
-    except OSError:
-        pass
-    return {"value": round(weights / dt / 1e9, 5), "unit": "Gweights/s", "cores": n_thr,
-            "per_core_value": round(per_core, 5), "cpu_model": model,
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"the first {weights} weights of the set in linear order ({len(host)} linears, the "
-                      f"last cut by rows): full-tensor s2, then quantize (+w') and dequantize, and "
-                      f"per-token activations of 512 x 4096"}
 
 
 if __name__ == "__main__":

@@ -70,6 +70,26 @@ def build_selftest(verbose: bool = False) -> str:
     return SELFTEST_LIB
 
 
+STREAM_SRC = os.path.join(ROOT, "tests", "hip", "focus_stream.hip")
+STREAM_LIB = os.path.join(ROOT, "tests", "hip", "libfocus_stream.so")
+
+
+def build_stream(verbose: bool = False) -> str:
+    """The streaming-ceiling helper (tests/hip) that bench.py times beside
+    the quantizer."""
+    out = STREAM_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, STREAM_SRC, "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stderr)
+        raise RuntimeError("hipcc failed (stream helper)")
+    os.replace(out, STREAM_LIB)
+    return STREAM_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
     build_selftest(verbose=True)
+    build_stream(verbose=True)

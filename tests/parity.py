@@ -1,5 +1,5 @@
-"""Parity rule between the HIP path and the oracle, shared by the GPU tests,
-smoke() and the benchmark's sampled check.
+"""Parity rule between the HIP path and the oracle, shared by the GPU tests
+and the benchmark's check of every output of the 1B and 8B weight sets.
 
 The bar:
   * scale bytes and s2 bit-exact;
@@ -68,10 +68,14 @@ def oracle_act_rows(o, xb, dequant=False, n_threads=None):
     return tuple(out)
 
 
-def check_quantized(o, wb, m, q, s2, gpu_codes, gpu_scales, gpu_deq, ref=None, label=""):
+def check_quantized(o, wb, m, q, s2, gpu_codes, gpu_scales, gpu_deq, ref=None, label="",
+                    count_limit=None):
     """Compare GPU outputs (numpy, same rows as wb) with the oracle on the
     same inputs.  Returns a dict of counts; raises AssertionError when the
-    parity bar fails."""
+    parity bar fails.  ``count_limit`` replaces the 1e-6 bound on the number
+    of code mismatches (a caller checking a tensor in parts applies the bound
+    to the whole); every mismatch must still be one step explained by sigmoid
+    rounding."""
     if ref is None:
         ref = oracle_quantize_rows(o, wb, m, q, s2, dequant=gpu_deq is not None)
     codes, scales, deq = ref
@@ -82,7 +86,7 @@ def check_quantized(o, wb, m, q, s2, gpu_codes, gpu_scales, gpu_deq, ref=None, l
     gc, oc = unpack(gpu_codes), unpack(codes)
     diff = np.argwhere(gc != oc)
     n = gc.size
-    allowed = int(np.floor(CODE_MISMATCH_RATE * n))
+    allowed = int(np.floor(CODE_MISMATCH_RATE * n)) if count_limit is None else int(count_limit)
     assert len(diff) <= allowed, f"{label}: {len(diff)} code mismatches > {allowed} allowed of {n}; " \
                                  f"first {diff[:4].tolist()}"
     for r, c in diff:

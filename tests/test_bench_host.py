@@ -53,3 +53,60 @@ def test_traffic_only_for_the_measured_code(tmp_path, monkeypatch):
     assert bench.measured_traffic() is None           # taken on other code
     prof.write_text("not json")
     assert bench.measured_traffic() is None
+
+
+def _oracle_set(orc):
+    """A two-layer set of small linears whose 'GPU outputs' are the oracle's
+    own (CPU tensors): the benchmark's parity pass must find no mismatch."""
+    import types
+
+    import numpy as np
+    import torch
+
+    import fp4_post_weight_amd as f
+    import synth
+    ws = synth.WeightSet("two small layers", 256, 64, 512, 2, 0.02, "lognormal")
+    R = types.SimpleNamespace(ws=ws, lins=ws.linears(), W=[], M=[], Q=[], OUT=[], WDQ=[], DEQ=[])
+    s2s, ams = [], []
+    for lin in R.lins:
+        w, m, q = synth.make_linear(ws, lin)
+        wb = synth.bits(w)
+        s2, am = orc.tensor_scale(wb)
+        c, sc, d = orc.quantize(wb, m.numpy(), q.numpy(), s2, True)
+        dt = torch.from_numpy(d.view(np.int16)).view(torch.bfloat16)
+        R.W.append(w)
+        R.M.append(m)
+        R.Q.append(q)
+        R.OUT.append(f.Quantized(torch.from_numpy(c), torch.from_numpy(sc), dt, None))
+        R.WDQ.append(dt)
+        R.DEQ.append(dt.clone())
+        s2s.append(s2)
+        ams.append(am)
+    R.S2 = torch.tensor(s2s).view(-1, 1)
+    R.AMAX = torch.tensor(ams).view(-1, 1)
+    x = synth.make_activations((40, 4096))
+    c, sc, s2t, _ = orc.quantize_act_per_token(synth.bits(x))
+    act = f.Quantized(torch.from_numpy(c), torch.from_numpy(sc), None, torch.from_numpy(s2t))
+    return R, x, act
+
+
+def test_set_parity_pass_counts_and_finds_planted_mismatches(orc):
+    import types
+    args = types.SimpleNamespace(cpu_weights=0)
+    R, x, act = _oracle_set(orc)
+    par, cpu = bench.check_set(R, x, act, args, False, label="small")
+    assert par["ok"] and par["tensors"] == 14 and par["weights_checked"] == sum(l.numel for l in R.lins)
+    assert par["scale_mismatches"] == par["code_mismatches"] == par["wdeq_mismatches"] == 0
+    assert par["act_tokens"] == 40 and cpu["kind"] == "oracle" and cpu["value"] > 0
+    # planted on the 'GPU' side: a scale byte, a code nibble, a dequantized
+    # value, an activation scale byte and one tensor's s2
+    R.OUT[3].scales[5, 2] ^= 1
+    R.OUT[5].codes[7, 9] ^= 0x10
+    R.DEQ[6][1, 1] = 1.0
+    act.scales[3, 3] ^= 2
+    R.S2[2, 0] *= 2
+    par, _ = bench.check_set(R, x, act, args, False, label="small")
+    assert not par["ok"]
+    assert par["scale_mismatches"] == 1 and par["dequantize_mismatches"] == 1
+    assert par["s2_mismatches"] == 1 and par["act_scale_mismatches"] == 1
+    assert any("not explained by sigmoid rounding" in e for e in par["failures"])

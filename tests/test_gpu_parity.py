@@ -6,7 +6,8 @@ that span several 256-lane tiles with a partial tail; edge cases (zero
 blocks, signed zeros, an all-zero tensor, extreme magnitudes, subnormal
 scales, extreme logits); and every linear shape of the 8B and 70B weight
 sets at full size, launched exactly as the benchmark launches them and
-checked on sampled rows (plus the full tensor scale).
+checked on sampled rows (plus the full tensor scale); the benchmark itself
+checks every output of the whole 1B and 8B sets against the oracle.
 """
 import numpy as np
 import pytest
@@ -258,14 +259,16 @@ def test_act_per_token_shapes(focus, orc, shape):
 # full-size linears, sampled rows
 # ---------------------------------------------------------------------------
 
-FULL = [("8B", s) for s in sorted(set(synth.LLAMA_8B.layer_shapes()))] + \
-       [("70B", (28672, 8192)), ("70B", (8192, 28672)), ("70B", (1024, 8192))]
+# every distinct linear shape of the 1B, 8B and 70B weight sets
+FULL = [("1B", s) for s in sorted(set(synth.LLAMA_1B.layer_shapes()))] + \
+       [("8B", s) for s in sorted(set(synth.LLAMA_8B.layer_shapes()))] + \
+       [("70B", s) for s in sorted(set(synth.LLAMA_70B.layer_shapes()))]
 
 
 @pytest.mark.parametrize("ws_name,shape", FULL, ids=lambda v: v if isinstance(v, str) else f"{v[0]}x{v[1]}")
 @pytest.mark.parametrize("dequant", [False, True], ids=["codes", "codes+deq"])
 def test_full_size_sampled(focus, orc, ws_name, shape, dequant):
-    ws = synth.LLAMA_8B if ws_name == "8B" else synth.LLAMA_70B
+    ws = {"1B": synth.LLAMA_1B, "8B": synth.LLAMA_8B, "70B": synth.LLAMA_70B}[ws_name]
     lin = next(l for l in ws.linears() if (l.rows, l.cols) == shape)
     w, m, q = synth.make_linear(ws, lin, device=DEV)
     s2d, amaxd = focus.tensor_scale(w)
