@@ -92,11 +92,14 @@ def _check_buf(name, t, dtype, device, numel):
         raise ValueError(f"{name} holds {t.numel()} elements, expected {numel}")
 
 
-def _quant_outs(out, rows, cols, dev, dequant, s2=None, s2_rows=0, scale_block=16, label="out"):
+def _quant_outs(out, rows, cols, dev, dequant, s2=None, s2_rows=0, scale_block=16, label="out",
+                deq_optional=False):
     """Output buffers of a quantizer call: allocated when `out` is None,
     otherwise checked (codes [rows, cols/2], scales [rows, cols/scale_block],
     deq [rows, cols] when dequant, and s2 [s2_rows] FP32 when s2_rows > 0).
-    Returns (codes, scales, deq or None, s2)."""
+    With deq_optional (the batched calls), an entry without a deq buffer
+    gets no w' even when dequant is set.  Returns (codes, scales, deq or
+    None, s2)."""
     if out is None:
         codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
         scales = torch.empty((rows, cols // scale_block), dtype=torch.uint8, device=dev)
@@ -109,7 +112,7 @@ def _quant_outs(out, rows, cols, dev, dequant, s2=None, s2_rows=0, scale_block=1
     _check_buf(f"{label}.codes", out.codes, torch.uint8, dev, rows * cols // 2)
     _check_buf(f"{label}.scales", out.scales, torch.uint8, dev, rows * cols // scale_block)
     deq = None
-    if dequant:
+    if dequant and not (deq_optional and out.deq is None):
         if out.deq is None:
             raise ValueError(f"dequant=True needs {label}.deq")
         _check_buf(f"{label}.deq", out.deq, torch.bfloat16, dev, rows * cols)
@@ -256,7 +259,8 @@ def quantize_act_per_token_fo6(x: torch.Tensor, dequant: bool = False,
 # ---------------------------------------------------------------------------
 
 def _mx_outs(out, rows, cols, dev, dequant, label="out"):
-    codes, scales, deq, _ = _quant_outs(out, rows, cols, dev, dequant, scale_block=32, label=label)
+    codes, scales, deq, _ = _quant_outs(out, rows, cols, dev, dequant, scale_block=32, label=label,
+                                        deq_optional=label != "out")
     return Quantized(codes, scales, deq, None)
 
 
@@ -352,7 +356,7 @@ def _mix_desc(i, w, tile_map, tile_rows, tile_cols, s2, dev, dequant, out):
     _check_dev(f"s2s[{i}]", s2, torch.float32, dev)
     if s2.numel() < 1:
         raise ValueError(f"s2s[{i}] must hold one float")
-    codes, scales, deq, _ = _quant_outs(out, rows, cols, dev, dequant, label=f"outs[{i}]")
+    codes, scales, deq, _ = _quant_outs(out, rows, cols, dev, dequant, label=f"outs[{i}]", deq_optional=True)
     res = Quantized(codes, scales, deq, s2)
     return res, _lib.MixDesc(_p(w), rows, cols, _p(s2), _p(tile_map), tile_rows, tile_cols, _p(codes),
                              _p(scales), _p(deq))
@@ -564,7 +568,7 @@ def quantize_many(ws, ms, qs, s2s, outs=None, dequant: bool = True, run: bool = 
         if s2.numel() < 1:
             raise ValueError(f"s2s[{i}] must hold one float")
         codes, scales, deq, _ = _quant_outs(None if outs is None else outs[i], rows, cols, dev, dequant,
-                                            label=f"outs[{i}]")
+                                            label=f"outs[{i}]", deq_optional=True)
         res.append(Quantized(codes, scales, deq, s2))
         arr[i] = _lib.QuantDesc(_p(w), rows, cols, _p(m), _p(q), _p(s2), _p(codes), _p(scales), _p(deq))
     b = Batch("focus_quantize_many", arr, (list(ws), list(ms), list(qs), list(s2s), res), dev)
