@@ -93,6 +93,10 @@ unsigned oracle_e2m1_round(float x)
 {
     unsigned sign = (bits_from_f32(x) >> 31) & 1u;
     double a = fabs((double)x);
+    /* the clamp to [-6, 6] of equation c_i: beyond 6 the nearest value is
+     * 6, and for huge magnitudes the binary64 distances below could no
+     * longer tell 4 from 6 */
+    if (a > 6.0) a = 6.0;
     unsigned best = 0;
     double best_d = INFINITY;
     for (unsigned k = 0; k < 8; ++k) {
