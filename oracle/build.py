@@ -16,9 +16,14 @@ LIB = os.path.join(HERE, "liboracle.so")
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
           "-fno-fast-math", "-fno-finite-math-only", "-frounding-math", "-Wall", "-Wextra"]
 
+# A host-only sanitized build (AddressSanitizer + UndefinedBehaviorSanitizer,
+# every finding fatal) for the CPU tests; loading it needs the ASan runtime
+# preloaded (LD_PRELOAD of `gcc -print-file-name=libasan.so`).
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 
-def build(src: str = SRC, out: str = LIB, verbose: bool = False) -> str:
-    cmd = ["gcc", *CFLAGS, src, "-o", out + ".tmp", "-lm"]
+
+def build(src: str = SRC, out: str = LIB, verbose: bool = False, sanitize: bool = False) -> str:
+    cmd = ["gcc", *CFLAGS, *(SANITIZE_FLAGS if sanitize else []), src, "-o", out + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
