@@ -41,7 +41,7 @@ from ._lib import FocusError, FocusLibraryMissing, library_path  # noqa: F401
 __all__ = ["tensor_scale", "quantize", "dequantize", "quantize_act_per_token", "Quantized",
            "quantize_fo6", "quantize_act_per_token_fo6", "quantize_fo6_many",
            "quantize_mixfp4", "quantize_mixfp4_many", "dequantize_mixfp4", "nvfp4_linear",
-           "nvfp4_linear_workspace_bytes",
+           "nvfp4_linear_workspace_bytes", "nvfp4_linear_noalloc", "nvfp4_linear_scratch_bytes",
            "quantize_mx", "quantize_mx_many", "dequantize_mx",
            "tensor_scale_many", "quantize_many", "dequantize_many", "Batch",
            "FocusError", "FocusLibraryMissing", "abi_version", "status_string", "library_path"]
@@ -472,6 +472,38 @@ def nvfp4_linear(x: Quantized, w: Quantized, out_dtype: torch.dtype = torch.bflo
                                              0 if out_dtype == torch.float32 else 1, _p(workspace),
                                              0 if workspace is None else workspace.numel() * 4,
                                              _stream(x.codes)))
+    return out
+
+
+def nvfp4_linear_scratch_bytes() -> int:
+    """Bytes of the per-GPU scratch that ``nvfp4_linear_noalloc`` uses."""
+    return int(_lib.lib().focus_nvfp4_linear_scratch_bytes())
+
+
+def nvfp4_linear_noalloc(x: Quantized, w: Quantized, out: torch.Tensor) -> torch.Tensor:
+    """``nvfp4_linear`` into the caller's ``out`` ([M, N] bfloat16 or float32,
+    contiguous) with the library's per-GPU scratch as the split-k workspace:
+    neither this call nor the library allocates anything (usable under HIP
+    graph capture).  Calls that may overlap on one GPU share that scratch and
+    must be serialized by the caller."""
+    dev = x.codes.device
+    for name, t in (("x.codes", x.codes), ("x.scales", x.scales), ("w.codes", w.codes), ("w.scales", w.scales)):
+        _check_dev(name, t, torch.uint8, dev)
+    _check_dev("x.s2", x.s2, torch.float32, dev)
+    _check_dev("w.s2", w.s2, torch.float32, dev)
+    M, K = x.codes.shape[0], 2 * x.codes.shape[1]
+    N = w.codes.shape[0]
+    if w.codes.shape[1] * 2 != K or tuple(x.scales.shape) != (M, K // 16) or tuple(w.scales.shape) != (N, K // 16):
+        raise ValueError("operand shapes do not match: x [M, K], w [N, K] with K % 16 == 0")
+    if x.s2.numel() not in (1, M) or w.s2.numel() != 1:
+        raise ValueError("x.s2 needs 1 or M values, w.s2 one")
+    if not isinstance(out, torch.Tensor) or out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be a bfloat16 or float32 tensor")
+    _check_buf("out", out, out.dtype, dev, M * N)
+    per_row = 1 if (x.s2.numel() == M and M > 1) else 0
+    _lib.check(_lib.lib().focus_nvfp4_linear_noalloc(_p(x.codes), _p(x.scales), _p(x.s2), per_row, M, _p(w.codes),
+                                                     _p(w.scales), _p(w.s2), N, K, _p(out),
+                                                     0 if out.dtype == torch.float32 else 1, _stream(x.codes)))
     return out
 
 

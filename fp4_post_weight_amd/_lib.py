@@ -58,6 +58,9 @@ _SIGNATURES = {
     "focus_nvfp4_linear": (_INT, [_VP, _VP, _VP, _INT, _I64, _VP, _VP, _VP, _I64, _I64, _VP, _INT, _VP, _I64,
                                   _VP]),
     "focus_nvfp4_linear_workspace_bytes": (_I64, [_I64, _I64, _I64]),
+    "focus_nvfp4_linear_noalloc": (_INT, [_VP, _VP, _VP, _INT, _I64, _VP, _VP, _VP, _I64, _I64, _VP, _INT,
+                                          _VP]),
+    "focus_nvfp4_linear_scratch_bytes": (_I64, []),
 }
 
 EXPORTED = tuple(_SIGNATURES)

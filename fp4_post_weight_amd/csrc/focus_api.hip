@@ -475,4 +475,18 @@ int focus_nvfp4_linear(const uint8_t* x_codes, const uint8_t* x_scales, const fl
                       workspace, workspace_bytes, (hipStream_t)stream);
 }
 
+int64_t focus_nvfp4_linear_scratch_bytes(void) { return focus::kLinearScratchBytes; }
+
+int focus_nvfp4_linear_noalloc(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_s2,
+                               int x_s2_per_row, int64_t M, const uint8_t* w_codes, const uint8_t* w_scales,
+                               const float* w_s2, int64_t N, int64_t K, void* y, int y_dtype, void* stream) {
+    int st = check_linear(x_codes, x_scales, x_s2, x_s2_per_row, M, w_codes, w_scales, w_s2, N, K, y, y_dtype);
+    if (st != FOCUS_OK) return st;
+    if (M == 0 || N == 0) return FOCUS_OK;
+    float* scratch = nullptr;
+    if (focus::nvfp4_linear_scratch(&scratch) != hipSuccess) return FOCUS_ERR_HIP;
+    return run_linear(x_codes, x_scales, x_s2, x_s2_per_row, M, w_codes, w_scales, w_s2, N, K, y, y_dtype,
+                      scratch, focus::kLinearScratchBytes, (hipStream_t)stream);
+}
+
 }  // extern "C"

@@ -40,4 +40,12 @@ int64_t nvfp4_linear_workgroups(int64_t M, int64_t N, int64_t cus);
 // is ksplit * M * N * 4 bytes.
 int64_t nvfp4_linear_splits(int64_t M, int64_t N, int64_t K, int64_t part_bytes, int64_t cus);
 
+// Bytes of the per-device array that the allocation-free linear call uses as
+// its split-k workspace.
+constexpr int64_t kLinearScratchBytes = (int64_t)64 << 20;
+
+// The current device's address of that array (looked up on the first call
+// on each device and kept).
+hipError_t nvfp4_linear_scratch(float** ptr);
+
 }  // namespace focus

@@ -58,6 +58,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "focus_gemm.h"
 #include "focus_launch.h"
 #include "focus_numerics.h"
@@ -732,6 +734,41 @@ int64_t nvfp4_linear_workgroups(int64_t M, int64_t N, int64_t cus) {
         return (N + 16 * t - 1) / (16 * t);
     }
     return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+}
+
+// ---------------------------------------------------------------------------
+// The split-k workspace of the allocation-free entry point: one file-scope
+// device array per GPU (each device holds its own copy at its own address,
+// from the library's load until the process ends).  Host code never passes
+// the array's name to a kernel or a copy -- on the host it is only a handle
+// of the symbol -- but the device address that hipGetSymbolAddress returns
+// for the current device, looked up once per device and kept.
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) float scratch[kLinearScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t nvfp4_linear_scratch(float** ptr) {
+    *ptr = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = static_cast<float*>(p);
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace focus

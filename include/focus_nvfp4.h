@@ -316,6 +316,39 @@ int focus_nvfp4_linear(const uint8_t* x_codes, const uint8_t* x_scales, const fl
  * query of that count failed (the HIP error is left for the caller to read). */
 int64_t focus_nvfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+/*
+ * focus_nvfp4_linear without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The caller passes the operands and y
+ * exactly as for focus_nvfp4_linear; the split-k partials go to a scratch
+ * array that the library holds in device memory, one per GPU, from the
+ * library's load until the process ends, of focus_nvfp4_linear_scratch_bytes()
+ * bytes (64 MiB).  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); its first call on a device looks up that
+ * device's address of the array once.
+ *   Sizes: any M, N, K that focus_nvfp4_linear accepts.  The k split is
+ *   limited to the ranges whose partials fit in the scratch (as when
+ *   focus_nvfp4_linear is given that many workspace bytes), so no call
+ *   needs more than the scratch holds and no size is rejected for it; the
+ *   result equals focus_nvfp4_linear's with a workspace of
+ *   min(focus_nvfp4_linear_workspace_bytes(M, N, K), scratch bytes) bit for
+ *   bit.  Nothing in the scratch has to start at zero (every partial that the
+ *   finalize reads is written first by the same call).
+ *   Concurrency: every call on one GPU shares that GPU's scratch, which keeps
+ *   the last call's contents.  Calls that may overlap on one GPU (different
+ *   streams without ordering between them, several host threads) race on it
+ *   and must be serialized by the caller; calls on one stream are ordered.
+ *   Errors: the shape, range, NULL and alignment rules of focus_nvfp4_linear;
+ *   FOCUS_ERR_HIP if the device or the array's address cannot be queried.
+ */
+int focus_nvfp4_linear_noalloc(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_s2,
+                               int x_s2_per_row, int64_t M, const uint8_t* w_codes,
+                               const uint8_t* w_scales, const float* w_s2, int64_t N, int64_t K,
+                               void* y, int y_dtype, void* stream);
+
+/* Bytes of the per-GPU scratch array of focus_nvfp4_linear_noalloc. */
+int64_t focus_nvfp4_linear_scratch_bytes(void);
+
 #ifdef __cplusplus
 }
 #endif
