@@ -226,12 +226,32 @@ __device__ __forceinline__ void fo6_block(uint4 a, uint4 b, float s2, double rde
         return;
     }
     const float amax = block_amax_bits(a, b);
-    uint32_t sb6, sb4, c60, c61, c40, c41;
-    float S6, S4, e6, e4;
-    fo6_candidate(f, amax, rden6, s2, sb6, S6, c60, c61, e6);
-    fo6_candidate(f, amax, rden4, s2, sb4, S4, c40, c41, e4);
-    const bool four = e4 < e6;
-    const uint32_t c0 = four ? c40 : c60, c1 = four ? c41 : c61;
+    const uint32_t sb6 = e4m3_byte_normal(block_t(amax, 1.0f, rden6));
+    const uint32_t sb4 = e4m3_byte_normal(block_t(amax, 1.0f, rden4));
+    const float S6 = e4m3_normal_value(sb6), S4 = e4m3_normal_value(sb4);
+    const float d6 = S6 * s2, d4 = S4 * s2;
+    uint32_t c0, c1;
+    bool four = false;
+    if (sb4 == sb6) {
+        // identical candidates: equal errors, and a tie keeps 6
+        c0 = encode8(f, d6);
+        c1 = encode8(f + 8, d6);
+    } else if (s2 >= kFo6S2Lo && s2 <= kFo6S2Hi) {
+        const double r6 = recip_f64((double)d6), r4 = recip_f64((double)d4);
+        float e6a = 0.0f, e6b = 0.0f, e4a = 0.0f, e4b = 0.0f;
+        const uint32_t c60 = fo6_encode8_est(f, r6, e6a), c61 = fo6_encode8_est(f + 8, r6, e6b);
+        const uint32_t c40 = fo6_encode8_est(f, r4, e4a), c41 = fo6_encode8_est(f + 8, r4, e4b);
+        four = fo6_choose_four(f, s2, S6, d6, c60, c61, e6a + e6b, S4, d4, c40, c41, e4a + e4b);
+        c0 = four ? c40 : c60;
+        c1 = four ? c41 : c61;
+    } else {
+        // outside the estimate's proven range: both exact error sums
+        const uint32_t c60 = encode8(f, d6), c61 = encode8(f + 8, d6);
+        const uint32_t c40 = encode8(f, d4), c41 = encode8(f + 8, d4);
+        four = fo6_sq_err(f, c40, c41, S4, s2) < fo6_sq_err(f, c60, c61, S6, s2);
+        c0 = four ? c40 : c60;
+        c1 = four ? c41 : c61;
+    }
     const float S = four ? S4 : S6;
     st8(codes_out, 0, make_uint2(c0, c1));
     *scale_out = (uint8_t)(four ? sb4 : sb6);

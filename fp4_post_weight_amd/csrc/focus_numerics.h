@@ -256,15 +256,10 @@ __device__ __forceinline__ float e8m0_value(uint32_t b) {
 // order; the 4-candidate only when strictly lower).  m = 1, no relaxation.
 // ---------------------------------------------------------------------------
 
-// One candidate: scale byte, codes of both halves, and its error.
-__device__ __forceinline__ void fo6_candidate(const float* f, float amax, double rden, float s2,
-                                              uint32_t& sb, float& S, uint32_t& c0, uint32_t& c1,
-                                              float& err) {
-    sb = e4m3_byte_normal(block_t(amax, 1.0f, rden));
-    S = e4m3_normal_value(sb);
-    const float d = S * s2;
-    c0 = encode8(f, d);
-    c1 = encode8(f + 8, d);
+// The exact error of one candidate: binary32 sum, in element order, of
+// (w - (c*S)*s2)^2 over the 16 elements, from its packed codes c0 (elements
+// 0-7) and c1 (8-15).
+__device__ __forceinline__ float fo6_sq_err(const float* f, uint32_t c0, uint32_t c1, float S, float s2) {
     float e = 0.0f;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -284,7 +279,65 @@ __device__ __forceinline__ void fo6_candidate(const float* f, float amax, double
             e = e + e1 * e1;
         }
     }
-    err = e;
+    return e;
+}
+
+// Two elements of a FourOverSix candidate: their exact quotients x = RN(f/d)
+// (r = recip_f64(d), as in encode8) go into byte SEL of `codes`, and the
+// squares of x - c (c the decoded code value; the difference is exact by
+// Sterbenz's lemma, since c/2 <= |x| <= 2c whenever c != 0) are added to
+// `acc` with fused multiply-adds.
+template <int SEL>
+__device__ __forceinline__ void fo6_pair_est(float f0, float f1, double r, uint32_t& codes, float& acc) {
+    const float x0 = (float)((double)f0 * r);
+    const float x1 = (float)((double)f1 * r);
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, x0, x1, 1.0f, SEL);
+    const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, SEL);
+    const float u0 = x0 - c[0], u1 = x1 - c[1];
+    acc = __builtin_fmaf(u0, u0, acc);
+    acc = __builtin_fmaf(u1, u1, acc);
+}
+
+// Codes of 8 elements for the candidate whose binary64 reciprocal is r, plus
+// the running estimate sum (x - c)^2.
+__device__ __forceinline__ uint32_t fo6_encode8_est(const float* f, double r, float& acc) {
+    uint32_t v = 0;
+    fo6_pair_est<0>(f[0], f[1], r, v, acc);
+    fo6_pair_est<1>(f[2], f[3], r, v, acc);
+    fo6_pair_est<2>(f[4], f[5], r, v, acc);
+    fo6_pair_est<3>(f[6], f[7], r, v, acc);
+    return v;
+}
+
+// Range of s2 in which the estimate below is proven to decide exactly:
+// every d = S*s2 lies in [2^-60, 2^57], so d^2 is normal, underflow costs at
+// most 2^-30 in units of d^2, and no error sum overflows.
+constexpr float kFo6S2Lo = 0x1p-54f;
+constexpr float kFo6S2Hi = 0x1p48f;
+
+// The FourOverSix decision (true: the 4-candidate).  The rule compares the
+// two exact binary32 error sums E4 < E6.  Both candidates' codes are exact
+// (exact quotients); their errors are first estimated in units of d^2:
+// Ê = fused sum of (x - c)^2.  For s2 in [kFo6S2Lo, kFo6S2Hi] the exact sum
+// satisfies |E/d^2 - Ê| <= 2^-24 (41.3 + 193.3 Ê) (the derivation uses
+// |x| <= 6.376 and |x - c| <= 1, rounding of d, the quotient, c*S*s2, the
+// difference, the square and 15 additions, and underflow bounded by 2^-150
+// per operation).  With rho = d4/d6, E4/d6^2 is rho^2 E4/d4^2, so with the
+// margins M = 2^-24 (80 + 400 Ê) (which also cover the rounding of rho^2 and
+// of the comparisons) rho^2 (Ê4 + M4) < Ê6 - M6 proves E4 < E6 and
+// rho^2 (Ê4 - M4) > Ê6 + M6 proves E4 > E6.  Anything in between (ties
+// included) is decided by the exact sums.
+__device__ __forceinline__ bool fo6_choose_four(const float* f, float s2, float S6, float d6, uint32_t c60,
+                                                uint32_t c61, float e6, float S4, float d4, uint32_t c40,
+                                                uint32_t c41, float e4) {
+    const float rho = d4 * __builtin_amdgcn_rcpf(d6);
+    const float rho2 = rho * rho;
+    const float p4 = rho2 * e4;
+    const float m4 = rho2 * __builtin_fmaf(400.0f * 0x1p-24f, e4, 80.0f * 0x1p-24f);
+    const float m6 = __builtin_fmaf(400.0f * 0x1p-24f, e6, 80.0f * 0x1p-24f);
+    if (p4 + m4 < e6 - m6) return true;
+    if (p4 - m4 > e6 + m6) return false;
+    return fo6_sq_err(f, c40, c41, S4, s2) < fo6_sq_err(f, c60, c61, S6, s2);
 }
 
 // ---------------------------------------------------------------------------

@@ -499,6 +499,79 @@ def test_fo6_extreme_magnitudes(focus, orc):
         check_fo6(focus, orc, pins.torch_bf16_bits(y), label=f"fo6 tiny 2^{amax_exp}")
 
 
+def _fo6_errors_f32(blocks, s2):
+    """Test-side search aid (never an expected value): numpy binary32
+    emulation of both FourOverSix candidates' error sums and of the kernel's
+    cheap estimate, used only to pick blocks whose decision is close."""
+    f32 = np.float32
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    a = np.abs(blocks).max(1)
+    out = {}
+    for k in (6, 4):
+        t = (a / f32(f32(k) * s2)).astype(f32)
+        t = np.clip(np.where(t == 0, f32(1), t), f32(2 ** -6), f32(448))
+        u = t.view(np.uint32).astype(np.uint64)
+        S = (((u + 0x7FFFF + ((u >> 20) & 1)) >> 20) << 20).astype(np.uint32).view(f32)
+        d = (S * s2).astype(f32)
+        x = (blocks.astype(np.float64) / d[:, None]).astype(f32)
+        dist = np.abs(np.minimum(np.abs(x), 6)[..., None].astype(np.float64) - grid)
+        c = (np.sign(x) * grid[np.argmin(dist + (np.arange(8) % 2) * 1e-12, axis=-1)]).astype(f32)
+        v = ((c * S[:, None]).astype(f32) * s2).astype(f32)
+        q = ((blocks - v).astype(f32) ** 2).astype(f32)
+        E = np.zeros(len(blocks), f32)
+        for i in range(16):
+            E = (E + q[:, i]).astype(f32)
+        out[k] = (E, S, d)
+    return out
+
+
+def test_fo6_near_ties_take_the_exact_path(focus, orc):
+    """Blocks whose two candidates' exact errors are within the estimate's
+    margin (relative gap below 2^-16) or exactly equal with different scales
+    are decided by the exact sums; searched among 2 M Gaussian blocks, with
+    outlier blocks (one large element, the rest small) for exact ties, and
+    checked bit for bit against the oracle."""
+    rng = np.random.default_rng(2024)
+    s2 = np.float32(0.02 * 4.5 / 2688)
+    blocks = pins.torch_bf16_bits((rng.standard_normal((1 << 21, 16)) * 0.02).astype(np.float32))
+    vals = (blocks.astype(np.uint32) << 16).view(np.float32)
+    e = _fo6_errors_f32(vals, s2)
+    (E6, S6, _), (E4, S4, _) = e[6], e[4]
+    gap = np.abs(E4 - E6) / np.maximum(E6, 1e-30)
+    near = np.nonzero((gap < 2.0 ** -16) & (S4 != S6))[0]
+    assert len(near) >= 8, len(near)
+    # outlier blocks: one element of about 1200 s2 (block scale t6 near 200,
+    # so S4 = 1.5 S6 whenever S6 is 128, 160 or 192 times a power of two) and
+    # the others too small for a nonzero code: both candidates dequantize to
+    # the same values, an exact tie
+    ob = (rng.standard_normal((4096, 16)) * 3e-4).astype(np.float32)
+    ob[np.arange(4096), rng.integers(0, 16, 4096)] = rng.uniform(0.03, 0.05, 4096) * np.sign(
+        rng.standard_normal(4096))
+    ob = pins.torch_bf16_bits(ob)
+    ov = (ob.astype(np.uint32) << 16).view(np.float32)
+    eo = _fo6_errors_f32(ov, s2)
+    ties = np.nonzero((eo[4][0] == eo[6][0]) & (eo[4][1] != eo[6][1]))[0]
+    assert len(ties) >= 8, len(ties)
+    sel = np.concatenate([blocks[near], ob[ties]])
+    sel = np.concatenate([sel, np.zeros(((-len(sel)) % 8, 16), np.uint16)])
+    wb = np.ascontiguousarray(sel.reshape(-1, 128))
+    check_fo6(focus, orc, wb, s2=float(s2), label=f"fo6 near ties ({len(near)} close, {len(ties)} exact)")
+    # the same blocks as per-token activations rows (per-row s2)
+    xb = np.ascontiguousarray(sel[: (len(sel) // 16) * 16].reshape(-1, 256))
+    x = torch.from_numpy(xb.view(np.int16).copy()).view(torch.bfloat16)
+    check_act_fo6(focus, orc, x, True, "fo6 act near ties")
+
+
+@pytest.mark.parametrize("s2", [2.0 ** -54, 2.0 ** -54 * 1.5, 2.0 ** 47 * 1.9, 2.0 ** 48, 2.0 ** -55, 2.0 ** 49],
+                         ids=lambda v: f"{v:.3g}")
+def test_fo6_estimate_range_boundaries(focus, orc, s2):
+    """s2 at and just beyond the ends of the range in which the cheap
+    estimate decides (below and above it every block takes the exact sums)."""
+    rng = np.random.default_rng(int(np.log2(s2) * 10) & 0xFFFF)
+    x = (rng.standard_normal((64, 256)) * (s2 * 2688 / 4.5)).astype(np.float32)
+    check_fo6(focus, orc, pins.torch_bf16_bits(x), s2=float(np.float32(s2)), label=f"fo6 s2={s2:.3g}")
+
+
 @pytest.mark.parametrize("shape", sorted(set(synth.LLAMA_8B.layer_shapes())), ids=lambda s: f"{s[0]}x{s[1]}")
 def test_fo6_full_size_sampled(focus, orc, shape):
     lin = next(l for l in synth.LLAMA_8B.linears() if (l.rows, l.cols) == shape)
