@@ -23,7 +23,8 @@ Calls (same names as the C ABI, without the ``focus_`` prefix):
   ``quantize_act_per_token_fo6``; FOCUS on MXFP4: ``quantize_mx``,
   ``quantize_mx_many``, ``dequantize_mx``; FlipQuant MixFP4:
   ``quantize_mixfp4``, ``quantize_mixfp4_many``, ``dequantize_mixfp4``; the
-  NVFP4 linear layer: ``nvfp4_linear``; ``abi_version``, ``status_string``.
+  NVFP4 linear layer: ``nvfp4_linear``, ``nvfp4_linear_grouped`` (several
+  weights sharing one X); ``abi_version``, ``status_string``.
 
 BF16 inputs are ``torch.bfloat16`` tensors; codes and scales are ``uint8``
 ([rows, cols/2] with element 2j in the low nibble, and [rows, cols/16] E4M3
@@ -41,7 +42,7 @@ from ._lib import FocusError, FocusLibraryMissing, library_path  # noqa: F401
 __all__ = ["tensor_scale", "quantize", "dequantize", "quantize_act_per_token", "Quantized",
            "quantize_fo6", "quantize_act_per_token_fo6", "quantize_fo6_many",
            "quantize_mixfp4", "quantize_mixfp4_many", "dequantize_mixfp4", "nvfp4_linear",
-           "nvfp4_linear_workspace_bytes", "nvfp4_linear_noalloc", "nvfp4_linear_scratch_bytes",
+           "nvfp4_linear_workspace_bytes", "nvfp4_linear_grouped", "nvfp4_linear_noalloc", "nvfp4_linear_scratch_bytes",
            "quantize_mx", "quantize_mx_many", "dequantize_mx",
            "tensor_scale_many", "quantize_many", "dequantize_many", "Batch",
            "FocusError", "FocusLibraryMissing", "abi_version", "status_string", "library_path"]
@@ -473,6 +474,57 @@ def nvfp4_linear(x: Quantized, w: Quantized, out_dtype: torch.dtype = torch.bflo
                                              0 if workspace is None else workspace.numel() * 4,
                                              _stream(x.codes)))
     return out
+
+
+def nvfp4_linear_grouped(x: Quantized, ws, out_dtype: torch.dtype = torch.bfloat16, outs=None,
+                         workspace="auto"):
+    """``nvfp4_linear`` of one activation ``x`` through several weights ``ws``
+    (a list of Quantized: codes [N_i, K/2], scales [N_i, K/16], one s2) that
+    share it, e.g. a layer's q, k and v: with up to 128 tokens one launch per
+    run of 8 weights.  Returns the list of outputs [M, N_i] (``outs`` may
+    supply them).  ``workspace`` as for ``nvfp4_linear`` (used only with
+    more than 128 tokens, for the largest member's split)."""
+    dev = x.codes.device
+    for name, t in (("x.codes", x.codes), ("x.scales", x.scales)):
+        _check_dev(name, t, torch.uint8, dev)
+    _check_dev("x.s2", x.s2, torch.float32, dev)
+    M, K = x.codes.shape[0], 2 * x.codes.shape[1]
+    if tuple(x.scales.shape) != (M, K // 16):
+        raise ValueError("x.scales must be [M, K/16]")
+    if x.s2.numel() not in (1, M):
+        raise ValueError("x.s2 needs 1 or M values")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be bfloat16 or float32")
+    n = len(ws)
+    if outs is not None and len(outs) != n:
+        raise ValueError("outs must have one tensor per weight")
+    arr = (_lib.LinearWeight * max(n, 1))()
+    res = []
+    for i, w in enumerate(ws):
+        _check_dev(f"ws[{i}].codes", w.codes, torch.uint8, dev)
+        _check_dev(f"ws[{i}].scales", w.scales, torch.uint8, dev)
+        _check_dev(f"ws[{i}].s2", w.s2, torch.float32, dev)
+        N = w.codes.shape[0]
+        if w.codes.shape[1] * 2 != K or tuple(w.scales.shape) != (N, K // 16) or w.s2.numel() != 1:
+            raise ValueError(f"ws[{i}] must be codes [N, K/2], scales [N, K/16] and one s2")
+        o = outs[i] if outs is not None else torch.empty((M, N), dtype=out_dtype, device=dev)
+        _check_buf(f"outs[{i}]", o, out_dtype, dev, M * N)
+        res.append(o)
+        arr[i] = _lib.LinearWeight(_p(w.codes), _p(w.scales), _p(w.s2), N, _p(o))
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a float32 tensor")
+        nbytes = max([nvfp4_linear_workspace_bytes(M, w.codes.shape[0], K) for w in ws] + [0]) \
+            if M > 128 and K else 0
+        workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=dev) if nbytes else None
+    if workspace is not None:
+        _check_dev("workspace", workspace, torch.float32, dev)
+    per_row = 1 if (x.s2.numel() == M and M > 1) else 0
+    _lib.check(_lib.lib().focus_nvfp4_linear_grouped(_p(x.codes), _p(x.scales), _p(x.s2), per_row, M, K, arr, n,
+                                                     0 if out_dtype == torch.float32 else 1, _p(workspace),
+                                                     0 if workspace is None else workspace.numel() * 4,
+                                                     _stream(x.codes)))
+    return res
 
 
 def nvfp4_linear_scratch_bytes() -> int:

@@ -36,6 +36,10 @@ class MixDesc(ct.Structure):
                 ("w_deq", _VP)]
 
 
+class LinearWeight(ct.Structure):
+    _fields_ = [("w_codes", _VP), ("w_scales", _VP), ("w_s2", _VP), ("N", _I64), ("y", _VP)]
+
+
 _SIGNATURES = {
     "focus_abi_version": (_INT, []),
     "focus_status_string": (ct.c_char_p, [_INT]),
@@ -58,6 +62,8 @@ _SIGNATURES = {
     "focus_nvfp4_linear": (_INT, [_VP, _VP, _VP, _INT, _I64, _VP, _VP, _VP, _I64, _I64, _VP, _INT, _VP, _I64,
                                   _VP]),
     "focus_nvfp4_linear_workspace_bytes": (_I64, [_I64, _I64, _I64]),
+    "focus_nvfp4_linear_grouped": (_INT, [_VP, _VP, _VP, _INT, _I64, _I64, ct.POINTER(LinearWeight), _INT, _INT,
+                                          _VP, _I64, _VP]),
     "focus_nvfp4_linear_noalloc": (_INT, [_VP, _VP, _VP, _INT, _I64, _VP, _VP, _VP, _I64, _I64, _VP, _INT,
                                           _VP]),
     "focus_nvfp4_linear_scratch_bytes": (_I64, []),

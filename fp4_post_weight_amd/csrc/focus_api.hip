@@ -475,6 +475,58 @@ int focus_nvfp4_linear(const uint8_t* x_codes, const uint8_t* x_scales, const fl
                       workspace, workspace_bytes, (hipStream_t)stream);
 }
 
+int focus_nvfp4_linear_grouped(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_s2,
+                               int x_s2_per_row, int64_t M, int64_t K, const focus_linear_weight* weights,
+                               int n, int y_dtype, float* workspace, int64_t workspace_bytes, void* stream) {
+    if (n < 0) return FOCUS_ERR_RANGE;
+    if (n > 0 && !weights) return FOCUS_ERR_NULL;
+    if (workspace_bytes < 0) return FOCUS_ERR_RANGE;
+    for (int i = 0; i < n; ++i) {
+        const focus_linear_weight& w = weights[i];
+        int st = check_linear(x_codes, x_scales, x_s2, x_s2_per_row, M, w.w_codes, w.w_scales, w.w_s2, w.N, K, w.y,
+                              y_dtype);
+        if (st != FOCUS_OK) return st;
+    }
+    if (M == 0 || n == 0) return FOCUS_OK;
+    if (!aligned(workspace, 4)) return FOCUS_ERR_ALIGN;
+    if (M > focus::kLinearDecodeMaxM) {
+        // the tiled kernel, one weight after the other (stream-ordered, so
+        // they may share the workspace)
+        for (int i = 0; i < n; ++i) {
+            const focus_linear_weight& w = weights[i];
+            if (w.N == 0) continue;
+            int st = run_linear(x_codes, x_scales, x_s2, x_s2_per_row, M, w.w_codes, w.w_scales, w.w_s2, w.N, K,
+                                w.y, y_dtype, workspace, workspace_bytes, (hipStream_t)stream);
+            if (st != FOCUS_OK) return st;
+        }
+        return FOCUS_OK;
+    }
+    const focus::GemmArgs a = {x_codes, x_scales, x_s2, x_s2_per_row, M, nullptr, nullptr, nullptr,
+                               0,       K,        nullptr, nullptr, 0, 1, 1};
+    bool fast = K > 0 && K % 64 == 0 && aligned(x_codes, 16) && aligned(x_scales, 4);
+    focus::GemvMembers mem = {};
+    for (int i = 0; i <= n; ++i) {
+        const bool end = i == n;
+        if (!end && weights[i].N == 0) continue;
+        if (mem.n > 0 && (end || mem.n == focus::kGemvMaxMembers)) {
+            int st = hip_status(focus::launch_nvfp4_linear_grouped(a, mem, fast, y_dtype == 1, (hipStream_t)stream));
+            if (st != FOCUS_OK) return st;
+            mem.n = 0;
+            fast = K > 0 && K % 64 == 0 && aligned(x_codes, 16) && aligned(x_scales, 4);
+        }
+        if (end) break;
+        const focus_linear_weight& w = weights[i];
+        const int j = mem.n++;
+        mem.wc[j] = w.w_codes;
+        mem.ws[j] = w.w_scales;
+        mem.ws2[j] = w.w_s2;
+        mem.y[j] = w.y;
+        mem.N[j] = w.N;
+        fast = fast && aligned(w.w_codes, 16) && aligned(w.w_scales, 4);
+    }
+    return FOCUS_OK;
+}
+
 int64_t focus_nvfp4_linear_scratch_bytes(void) { return focus::kLinearScratchBytes; }
 
 int focus_nvfp4_linear_noalloc(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_s2,

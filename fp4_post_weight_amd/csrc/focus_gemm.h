@@ -28,6 +28,27 @@ struct GemmArgs {
 // aligned.
 hipError_t launch_nvfp4_linear(const GemmArgs& a, bool fast, bool bf16_out, hipStream_t stream);
 
+// Weights that share one X, for the decode kernel (M <= 128): member j's
+// output columns take workgroup columns [tile_start[j], tile_start[j + 1])
+// (set by the launcher).
+constexpr int kGemvMaxMembers = 8;
+constexpr int64_t kLinearDecodeMaxM = 128;
+struct GemvMembers {
+    const uint8_t* wc[kGemvMaxMembers];
+    const uint8_t* ws[kGemvMaxMembers];
+    const float* ws2[kGemvMaxMembers];
+    void* y[kGemvMaxMembers];
+    int64_t N[kGemvMaxMembers];
+    int64_t tile_start[kGemvMaxMembers + 1];
+    int n;
+};
+
+// One launch of the decode kernel over every member (M <= 128, no k split;
+// a's weight fields, part and split are ignored).  fast: as above, with every
+// member's arrays aligned.
+hipError_t launch_nvfp4_linear_grouped(const GemmArgs& a, const GemvMembers& members, bool fast, bool bf16_out,
+                                       hipStream_t stream);
+
 // Compute units of the current device (the split model depends on them).
 hipError_t nvfp4_linear_cus(int64_t& cus);
 

@@ -433,13 +433,20 @@ __device__ __forceinline__ uint32_t gemv_dword(const GemvChunk& c, int j) {
 }
 
 template <bool FAST, bool BF16_OUT, int WAVES, int T, int MT>
-__global__ __launch_bounds__(64 * WAVES) void k_nvfp4_linear_gemv(GemmArgs a) {
+__global__ __launch_bounds__(64 * WAVES) void k_nvfp4_linear_gemv(GemmArgs a, GemvMembers mem) {
     __shared__ float red[WAVES][MT * T * 16 * 16];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int c16 = lane & 15, g = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * (16 * T);
+    // the weight (member) this workgroup's columns belong to: members share X
+    // and take consecutive ranges of workgroup columns (uniform, scalar)
+    int j = 0;
+    while (j + 1 < mem.n && (int64_t)blockIdx.x >= mem.tile_start[j + 1]) ++j;
+    const uint8_t* __restrict__ wc = mem.wc[j];
+    const uint8_t* __restrict__ wsc = mem.ws[j];
+    const int64_t N = mem.N[j];
+    const int64_t n0 = ((int64_t)blockIdx.x - mem.tile_start[j]) * (16 * T);
     const int64_t nsteps_all = (a.K + kGemvK - 1) / kGemvK;
     const int64_t sb = (int64_t)blockIdx.y * a.kchunk;
     const int64_t se = sb + a.kchunk < nsteps_all ? sb + a.kchunk : nsteps_all;
@@ -459,7 +466,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_nvfp4_linear_gemv(GemmArgs a) {
         for (int64_t i = 0; i < my; ++i) {
             const int64_t k0 = (sb + wave + (int64_t)WAVES * i) * kGemvK;
 #pragma unroll
-            for (int t = 0; t < T; ++t) w[t] = load_gemv<FAST>(a.wc, a.ws, n0 + 16 * t + c16, a.N, a.K, k0, g);
+            for (int t = 0; t < T; ++t) w[t] = load_gemv<FAST>(wc, wsc, n0 + 16 * t + c16, N, a.K, k0, g);
 #pragma unroll
             for (int m = 0; m < MT; ++m) x[m] = load_gemv<FAST>(a.xc, a.xs, 16 * m + c16, a.M, a.K, k0, g);
             f16x2 w01[T], w23[T], x01[MT], x23[MT];
@@ -504,16 +511,16 @@ __global__ __launch_bounds__(64 * WAVES) void k_nvfp4_linear_gemv(GemmArgs a) {
         for (int w = 0; w < WAVES; ++w) v += red[w][e];
         const int mt = e >> 8;
         const int64_t row = 16 * (mt / T) + ((e >> 4) & 15), col = n0 + 16 * (mt % T) + (e & 15);
-        if (row < a.M && col < a.N) {
-            if (a.ksplit > 1) {
-                a.part[((int64_t)blockIdx.y * a.M + row) * a.N + col] = v;
+        if (row < a.M && col < N) {
+            if (a.ksplit > 1) {  // a single member
+                a.part[((int64_t)blockIdx.y * a.M + row) * N + col] = v;
             } else {
-                const float y = v * (a.xs2[a.xs2_per_row ? row : 0] * a.ws2[0]);
+                const float y = v * (a.xs2[a.xs2_per_row ? row : 0] * mem.ws2[j][0]);
                 if (BF16_OUT) {
                     const uint32_t p = bf16_pair(y, 0.0f);
-                    reinterpret_cast<uint16_t*>(a.y)[row * a.N + col] = (uint16_t)(p & 0xFFFFu);
+                    reinterpret_cast<uint16_t*>(mem.y[j])[row * N + col] = (uint16_t)(p & 0xFFFFu);
                 } else {
-                    reinterpret_cast<float*>(a.y)[row * a.N + col] = y;
+                    reinterpret_cast<float*>(mem.y[j])[row * N + col] = y;
                 }
             }
         }
@@ -675,9 +682,10 @@ int64_t nvfp4_linear_splits(int64_t M, int64_t N, int64_t K, int64_t part_bytes,
 }
 
 template <bool F, bool B>
-static hipError_t launch_gemv(const GemvConfig& c, dim3 grid, dim3 block, hipStream_t stream, const GemmArgs& a) {
+static hipError_t launch_gemv(const GemvConfig& c, dim3 grid, dim3 block, hipStream_t stream, const GemmArgs& a,
+                              const GemvMembers& mem) {
 #define FOCUS_GV(MT, W, T) \
-    case 256 * MT + 16 * T + W: return launch(&k_nvfp4_linear_gemv<F, B, W, T, MT>, grid, block, stream, a);
+    case 256 * MT + 16 * T + W: return launch(&k_nvfp4_linear_gemv<F, B, W, T, MT>, grid, block, stream, a, mem);
     switch (c.mt * 256 + c.t * 16 + c.waves) {
         FOCUS_GV(1, 8, 1) FOCUS_GV(1, 4, 1) FOCUS_GV(1, 8, 2) FOCUS_GV(1, 4, 2)
         FOCUS_GV(2, 8, 1) FOCUS_GV(2, 4, 1) FOCUS_GV(2, 8, 2) FOCUS_GV(2, 4, 2)
@@ -686,6 +694,36 @@ static hipError_t launch_gemv(const GemvConfig& c, dim3 grid, dim3 block, hipStr
     }
 #undef FOCUS_GV
     return hipErrorInvalidValue;
+}
+
+static hipError_t launch_gemv_members(const GemmArgs& a, GemvMembers& mem, const GemvConfig& c, bool f,
+                                      bool bf16_out, unsigned splits, hipStream_t stream) {
+    const dim3 grid((unsigned)mem.tile_start[mem.n], splits), block(64 * c.waves);
+    if (f) return bf16_out ? launch_gemv<true, true>(c, grid, block, stream, a, mem)
+                           : launch_gemv<true, false>(c, grid, block, stream, a, mem);
+    return bf16_out ? launch_gemv<false, true>(c, grid, block, stream, a, mem)
+                    : launch_gemv<false, false>(c, grid, block, stream, a, mem);
+}
+
+hipError_t launch_nvfp4_linear_grouped(const GemmArgs& a, const GemvMembers& members, bool fast, bool bf16_out,
+                                       hipStream_t stream) {
+    int64_t cus = 0;
+    hipError_t e = device_cus(cus);
+    if (e != hipSuccess) return e;
+    GemmArgs g = a;
+    g.part = nullptr;
+    g.part_bytes = 0;
+    g.ksplit = 1;
+    const int64_t nsteps = (a.K + kGemvK - 1) / kGemvK;
+    g.kchunk = nsteps > 0 ? nsteps : 1;
+    int64_t ntot = 0;
+    for (int j = 0; j < members.n; ++j) ntot += members.N[j];
+    g.N = ntot;
+    const GemvConfig c = gemv_config(a.M, ntot, g.kchunk, cus);
+    GemvMembers mem = members;
+    mem.tile_start[0] = 0;
+    for (int j = 0; j < mem.n; ++j) mem.tile_start[j + 1] = mem.tile_start[j] + (mem.N[j] + 16 * c.t - 1) / (16 * c.t);
+    return launch_gemv_members(g, mem, c, fast && a.K % kGemvK == 0, bf16_out, 1, stream);
 }
 
 hipError_t launch_nvfp4_linear(const GemmArgs& args, bool fast, bool bf16_out, hipStream_t stream) {
@@ -701,12 +739,16 @@ hipError_t launch_nvfp4_linear(const GemmArgs& args, bool fast, bool bf16_out, h
     if (gemv) {
         const bool f = fast && a.K % kGemvK == 0;
         const GemvConfig c = gemv_config(a.M, a.N, a.kchunk, cus);
-        const int64_t wgs = (a.N + 16 * c.t - 1) / (16 * c.t);
-        const dim3 grid((unsigned)wgs, splits), block(64 * c.waves);
-        if (f) e = bf16_out ? launch_gemv<true, true>(c, grid, block, stream, a)
-                            : launch_gemv<true, false>(c, grid, block, stream, a);
-        else e = bf16_out ? launch_gemv<false, true>(c, grid, block, stream, a)
-                          : launch_gemv<false, false>(c, grid, block, stream, a);
+        GemvMembers mem = {};
+        mem.wc[0] = a.wc;
+        mem.ws[0] = a.ws;
+        mem.ws2[0] = a.ws2;
+        mem.y[0] = a.y;
+        mem.N[0] = a.N;
+        mem.tile_start[0] = 0;
+        mem.tile_start[1] = (a.N + 16 * c.t - 1) / (16 * c.t);
+        mem.n = 1;
+        e = launch_gemv_members(a, mem, c, f, bf16_out, splits, stream);
     } else {
         const int64_t tiles_m = (a.M + kBM - 1) / kBM, tiles_n = (a.N + kBN - 1) / kBN;
         const dim3 grid((unsigned)(tiles_m * tiles_n), splits), block(kGemmThreads);

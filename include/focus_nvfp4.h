@@ -317,6 +317,36 @@ int focus_nvfp4_linear(const uint8_t* x_codes, const uint8_t* x_scales, const fl
 int64_t focus_nvfp4_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
+ * Several NVFP4 weights that share one activation X (a layer's q, k and v
+ * projections; gate and up), as in focus_nvfp4_linear for each of them:
+ *     y_i [M, N_i] = X' W_i'^T        (same section of the same page)
+ * With few tokens (M <= 128) the layer streams W, and one launch per weight
+ * would cost a launch each: here every run of up to 8 weights is one launch
+ * of the decode kernel, whose workgroups take the weights' output columns in
+ * turn (no k split, so no workspace is used).  With more tokens the weights
+ * run one after the other as focus_nvfp4_linear calls on `stream`, sharing
+ * the workspace (caller-owned, as for focus_nvfp4_linear).
+ *   x_codes, x_scales, x_s2, x_s2_per_row, M, K: as focus_nvfp4_linear.
+ *   weights  HOST array of n descriptors (read during the call only): codes
+ *            [N, K/2], scales [N, K/16], w_s2 one float, output y [M, N] of
+ *            type y_dtype (shared by all); N == 0 entries are skipped.
+ * Every descriptor is validated (the rules of focus_nvfp4_linear) before
+ * anything is launched.  Outputs must not overlap each other or the inputs.
+ */
+typedef struct focus_linear_weight {
+    const uint8_t* w_codes;   /* [N, K/2] */
+    const uint8_t* w_scales;  /* [N, K/16] */
+    const float* w_s2;        /* one float */
+    int64_t N;
+    void* y;                  /* [M, N] FP32 or BF16 */
+} focus_linear_weight;
+
+int focus_nvfp4_linear_grouped(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_s2,
+                               int x_s2_per_row, int64_t M, int64_t K,
+                               const focus_linear_weight* weights, int n, int y_dtype,
+                               float* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * focus_nvfp4_linear without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  The caller passes the operands and y

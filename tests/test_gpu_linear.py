@@ -299,3 +299,58 @@ def test_split_model_workspace(focus):
     assert ws(16, 1024, 28672) > 0                    # few tokens, few columns, long rows
     assert ws(16, 4096, 64) == 0                      # one k-step: nothing to split
     assert ws(0, 16, 16) == 0 and ws(16, 16, 0) == 0
+
+
+# members sharing one X: a layer's q, k, v (and gate, up) at small and full
+# sizes; ragged N, K not a multiple of 256 (masked loads), M on both kernels
+GROUPS = [(16, [4096, 1024, 1024], 4096), (1, [14336, 14336], 4096), (5, [17, 300, 1], 1040),
+          (64, [520, 100, 33, 7, 1, 2, 3, 4, 5], 512), (128, [256, 130], 2064), (129, [130, 60], 192),
+          (300, [520, 96], 1040)]
+
+
+@pytest.mark.parametrize("M,Ns,K", GROUPS, ids=lambda v: str(v))
+def test_linear_grouped_matches_oracle(focus, orc, M, Ns, K):
+    """nvfp4_linear_grouped against the oracle for every member (within the
+    bound; bit for bit where all partial sums are exact), FP32 and BF16
+    output; nine members take two launches."""
+    xc, xs = synth.nvfp4_operand(M, K, seed=M + K, tensor_id=48)
+    rng = np.random.default_rng(M * 7 + K)
+    s2x = (rng.uniform(0.5, 2.0, M) * 2.0 ** -9).astype(np.float32)
+    ws = [synth.nvfp4_operand(N, K, seed=N + i, tensor_id=49) for i, N in enumerate(Ns)]
+    s2w = [np.float32(3.0e-4 * (i + 1)) for i in range(len(Ns))]
+    x = focus.Quantized(xc.to(DEV), xs.to(DEV), None, torch.from_numpy(s2x).to(DEV))
+    wq = [focus.Quantized(c.to(DEV), s.to(DEV), None, torch.tensor([v], device=DEV)) for (c, s), v in zip(ws, s2w)]
+    for dt in (torch.float32, torch.bfloat16):
+        ys = focus.nvfp4_linear_grouped(x, wq, out_dtype=dt)
+        torch.cuda.synchronize()
+        for i, ((c, s), v) in enumerate(zip(ws, s2w)):
+            ref, refabs = oracle_linear(orc, xc.numpy(), xs.numpy(), s2x, c.numpy(), s.numpy(), v)
+            check_bound(ys[i].float().cpu().numpy().astype(np.float64), ref, refabs, K, dt == torch.bfloat16,
+                        f"member {i} of {(M, Ns, K)} {dt}")
+    # exact partial sums: all scales 1, power-of-two s2
+    one_x = torch.full((M, K // 16), 0x38, dtype=torch.uint8)
+    x1 = focus.Quantized(xc.to(DEV), one_x.to(DEV), None, torch.full((M,), 0.25, device=DEV))
+    w1 = [focus.Quantized(c.to(DEV), torch.full((c.shape[0], K // 16), 0x38, dtype=torch.uint8, device=DEV), None,
+                          torch.tensor([0.5], device=DEV)) for c, _ in ws]
+    ys = focus.nvfp4_linear_grouped(x1, w1, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for i, (c, _) in enumerate(ws):
+        ref, _ = oracle_linear(orc, xc.numpy(), one_x.numpy(), np.full(M, 0.25, np.float32), c.numpy(),
+                               np.full((c.shape[0], K // 16), 0x38, np.uint8), np.float32(0.5))
+        assert np.array_equal(ys[i].cpu().numpy().astype(np.float64), ref), f"member {i} of {(M, Ns, K)}"
+
+
+def test_linear_grouped_validation(focus):
+    lib = focus._lib.lib()
+    LW = focus._lib.LinearWeight
+    FAKE = 0x10000
+    g = lib.focus_nvfp4_linear_grouped
+    good = LW(FAKE, FAKE, FAKE, 8, FAKE)
+    assert g(FAKE, FAKE, FAKE, 1, 4, 64, (LW * 2)(good, LW(FAKE, FAKE, None, 8, FAKE)), 2, 0, None, 0,
+             None) == 1   # a member's NULL s2, before any launch
+    assert g(FAKE, FAKE, FAKE, 1, 4, 60, (LW * 1)(good), 1, 0, None, 0, None) == 2          # K % 16
+    assert g(FAKE, FAKE, FAKE, 1, 4, 64, (LW * 1)(LW(FAKE + 4, FAKE, FAKE, 8, FAKE)), 1, 0, None, 0,
+             None) == 3   # misaligned member codes
+    assert g(FAKE, FAKE, FAKE, 1, 4, 64, None, 1, 0, None, 0, None) == 1
+    assert g(FAKE, FAKE, FAKE, 1, 4, 64, (LW * 1)(good), -1, 0, None, 0, None) == 5
+    assert g(FAKE, FAKE, FAKE, 1, 0, 64, (LW * 1)(good), 1, 0, None, 0, None) == 0           # M == 0: no-op
