@@ -197,43 +197,86 @@ class WeightSetRun:
         rec(3)
 
 
-def stream_ceiling(dev, read_bytes, write_bytes, reps=5):
-    """The hand-written streaming kernel (tests/hip/focus_stream.hip) moving
-    `read_bytes` in and `write_bytes` out in one launch, timed with HIP
-    events on the stream it runs on; the faster of plain and nontemporal
-    loads.  Returns (ms, GB/s)."""
+def _stream_lib():
     import ctypes as ct
+    lib = ct.CDLL(os.path.join(ROOT, "tests", "hip", "libfocus_stream.so"))
+    lib.focus_stream_pattern.restype = ct.c_int
+    lib.focus_stream_pattern.argtypes = [ct.c_void_p] * 3 + [ct.c_int64] + [ct.c_void_p] * 3 + [ct.c_int, ct.c_void_p]
+    lib.focus_stream_act_pattern.restype = ct.c_int
+    lib.focus_stream_act_pattern.argtypes = [ct.c_void_p, ct.c_int64, ct.c_int] + [ct.c_void_p] * 3 + \
+        [ct.c_int64, ct.c_void_p]
+    return lib
 
+
+def _time_stream(fn, reps=5):
     import torch
-    path = os.path.join(ROOT, "tests", "hip", "libfocus_stream.so")
-    lib = ct.CDLL(path)
-    lib.focus_stream.restype = ct.c_int
-    lib.focus_stream.argtypes = [ct.c_void_p, ct.c_int64, ct.c_void_p, ct.c_int64, ct.c_void_p, ct.c_int,
-                                 ct.c_int64, ct.c_void_p]
-    nr, nw = int(read_bytes) // 16, int(write_bytes) // 16
-    src = torch.ones(nr * 4, dtype=torch.int32, device=dev)
-    dst = torch.empty(nw * 4, dtype=torch.int32, device=dev)
-    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def stream_ceiling(dev, nblk, reps=5):
+    """The hand-written kernel of tests/hip/focus_stream.hip: the memory
+    traffic of one quantize + w' launch over `nblk` 16-element blocks (W, m
+    and q in; codes, scales and w' out, 85 bytes per block) with the
+    quantizer's work layout and no arithmetic, at 1, 2 and 4 blocks per lane,
+    timed with HIP events; the fastest.  Returns (ms, GB/s, blocks per lane)."""
+    import torch
+    lib = _stream_lib()
+    w = torch.ones(nblk * 16, dtype=torch.bfloat16, device=dev)
+    m = torch.ones(nblk, dtype=torch.float32, device=dev)
+    q = torch.ones(nblk * 2, dtype=torch.float32, device=dev)
+    codes = torch.empty(nblk * 8, dtype=torch.uint8, device=dev)
+    scales = torch.empty(nblk, dtype=torch.uint8, device=dev)
+    wdeq = torch.empty_like(w)
     stream = torch.cuda.current_stream(dev)
     best = None
-    for nt in (0, 1):
-        def call():
-            st = lib.focus_stream(src.data_ptr(), nr, dst.data_ptr(), nw, sink.data_ptr(), nt, 0,
-                                  stream.cuda_stream)
+    for u in (1, 2, 4):
+        def call(u=u):
+            st = lib.focus_stream_pattern(w.data_ptr(), m.data_ptr(), q.data_ptr(), nblk, codes.data_ptr(),
+                                          scales.data_ptr(), wdeq.data_ptr(), u, stream.cuda_stream)
             if st != 0:
-                raise RuntimeError(f"focus_stream failed with HIP error {st}")
-        call()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            call()
-        b.record(stream)
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / reps
-        best = ms if best is None else min(best, ms)
-    del src, dst, sink
-    return best, (nr + nw) * 16 / (best * 1e-3) / 1e9
+                raise RuntimeError(f"focus_stream_pattern failed with HIP error {st}")
+        ms = _time_stream(call, reps)
+        if best is None or ms < best[0]:
+            best = (ms, u)
+    del w, m, q, codes, scales, wdeq
+    return best[0], nblk * 85.0 / (best[0] * 1e-3) / 1e9, best[1]
+
+
+def act_ceiling(dev, tokens, hidden, reps=20):
+    """The activation kernel's traffic (X [tokens, hidden] in; codes, scale
+    bytes and one float per token out) with its work layout (a wavefront per
+    row, rows taken in turn, two per wavefront, at least 1024 workgroups) and
+    no arithmetic.  Returns (ms, GB/s)."""
+    import torch
+    lib = _stream_lib()
+    rb = hidden // 1024
+    x = torch.ones((tokens, hidden), dtype=torch.bfloat16, device=dev)
+    codes = torch.empty(tokens * hidden // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(tokens * hidden // 16, dtype=torch.uint8, device=dev)
+    s2 = torch.empty(tokens, dtype=torch.float32, device=dev)
+    g1 = (tokens + 3) // 4
+    g = (tokens + 7) // 8
+    if g < 1024:
+        g = g1 if g1 < 1024 else 1024
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        st = lib.focus_stream_act_pattern(x.data_ptr(), tokens, rb, codes.data_ptr(), scales.data_ptr(), s2.data_ptr(),
+                                          g, stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"focus_stream_act_pattern failed with HIP error {st}")
+    ms = _time_stream(call, reps)
+    nbytes = B_ACT * tokens * hidden + 4 * tokens
+    del x, codes, scales, s2
+    return ms, nbytes / (ms * 1e-3) / 1e9
 
 
 def main():
@@ -327,6 +370,9 @@ def main():
     par, cpu = None, None
     if not args.no_parity:
         par, cpu = check_set(R, X, ACT, args, layered)
+        for _ in range(2):  # the GPU idled during the oracle pass
+            step()
+        torch.cuda.synchronize()
 
     # ---- per-call rows outside the steps: each call alone, same buffers ----
     def time_calls(fn, reps=5):
@@ -409,13 +455,16 @@ def main():
     torch.cuda.synchronize()
     log("rows after the steps done")
 
-    # ---- streaming ceiling: a hand-written kernel moving the bytes of one
-    # quantize + w' launch (W, m, q in; codes, scales, w' out), same process
-    per_launch_w = n_weights / nq
-    rd, wr = (2.0 + 0.25 + 0.5) * per_launch_w, (0.5 + 0.0625 + 2.0) * per_launch_w
-    t_sc, ceil_gbs = stream_ceiling(dev, rd, wr)
-    rows["streaming kernel at one quantize + w' launch's read and write bytes (ceiling, after the steps)"] = \
-        row(t_sc, rd + wr, per_launch_w)
+    # ---- streaming ceiling: a hand-written kernel with the memory traffic of
+    # one quantize + w' launch and none of its arithmetic, same process
+    per_launch_blk = n_weights // 16 // nq
+    t_sc, ceil_gbs, ceil_u = stream_ceiling(dev, per_launch_blk)
+    rows[f"quantizer's traffic pattern without arithmetic, one launch's blocks, {ceil_u} per lane "
+         f"(ceiling, after the steps)"] = row(t_sc, per_launch_blk * 85.0, per_launch_blk * 16)
+    for tok in (8192, 131072):
+        t_ac, _ = act_ceiling(dev, tok, 4096, reps=20 if tok == 8192 else 10)
+        rows[f"per-token activation traffic without arithmetic [{tok},4096] (ceiling, after the steps)"] = \
+            row(t_ac, B_ACT * tok * 4096 + 4 * tok, tok * 4096)
     csrc = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
     cdst = torch.empty_like(csrc)
     t_cp = time_calls(lambda: cdst.copy_(csrc), reps=5)
@@ -425,6 +474,7 @@ def main():
     if extra_rows:
         rows.update(linear_rows(focus, synth, ws, dev, stream))
         rows.update(decode_graph_row(focus, synth, ws, dev))
+        rows.update(decode_layer_rows(focus, synth, ws, dev))
         log("linear-layer rows done")
 
     # ---- the Llama-3.2-1B-shaped set: the same step, with parity --------------
@@ -761,6 +811,80 @@ def decode_graph_row(focus, synth, ws, dev, m_tok=16, reps=50):
     del graph, keep
     return {key: {"ms": round(ms, 4), "TFLOP_s": round(flop / (ms * 1e-3) / 1e12, 1),
                   "GB_s": round(byts / (ms * 1e-3) / 1e9, 1), "frac_hbm_peak": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+
+
+def decode_layer_rows(focus, synth, ws, dev, m_tok=16, reps=50):
+    """One decoder layer's seven linears at 16 tokens, captured once in a HIP
+    graph and replayed: q, k and v share the attention input, gate and up the
+    MLP input, so the layer is grouped(q, k, v), o, grouped(gate, up), down
+    (four launches); the same seven linears as seven single calls for
+    comparison.  Operand bytes: codes and scales of X and W (0.5625 B per
+    element) and the BF16 outputs."""
+    import torch
+    h, kv, f = ws.hidden, ws.kv, ws.inter
+
+    def w(n, k, tid):
+        c, s = synth.nvfp4_operand(n, k, seed=5, tensor_id=tid, device=dev)
+        return focus.Quantized(c, s, None, torch.full((1,), 1e-3, dtype=torch.float32, device=dev))
+
+    def x(k, tid):
+        c, s = synth.nvfp4_operand(m_tok, k, seed=5, tensor_id=tid, device=dev)
+        return focus.Quantized(c, s, None, torch.full((m_tok,), 1e-3, dtype=torch.float32, device=dev))
+
+    xa, xo, xm, xd = x(h, 70), x(h, 71), x(h, 72), x(f, 73)
+    q, k, v, o = w(h, h, 80), w(kv, h, 81), w(kv, h, 82), w(h, h, 83)
+    gate, up, down = w(f, h, 84), w(f, h, 85), w(h, f, 86)
+    calls = [(xa, [q, k, v]), (xo, [o]), (xm, [gate, up]), (xd, [down])]
+    outs = [[torch.empty((m_tok, wt.codes.shape[0]), dtype=torch.bfloat16, device=dev) for wt in g] for _, g in calls]
+    wsp = {}
+    for xx, g in calls:
+        for wt in g:
+            n_ = int(focus.nvfp4_linear_workspace_bytes(m_tok, wt.codes.shape[0], xx.codes.shape[1] * 2))
+            wsp[id(wt)] = torch.empty(max(n_ // 4, 1), dtype=torch.float32, device=dev) if n_ else None
+
+    def grouped():
+        for (xx, g), og in zip(calls, outs):
+            if len(g) == 1:
+                focus.nvfp4_linear(xx, g[0], out=og[0], workspace=wsp[id(g[0])])
+            else:
+                focus.nvfp4_linear_grouped(xx, g, outs=og, workspace=None)
+
+    def single():
+        for (xx, g), og in zip(calls, outs):
+            for wt, yy in zip(g, og):
+                focus.nvfp4_linear(xx, wt, out=yy, workspace=wsp[id(wt)])
+
+    nbytes = sum((m_tok + sum(wt.codes.shape[0] for wt in g)) * xx.codes.shape[1] * 2 * 0.5625 +
+                 2.0 * m_tok * sum(wt.codes.shape[0] for wt in g) for xx, g in calls)
+    flop = sum(2.0 * m_tok * wt.codes.shape[0] * xx.codes.shape[1] * 2 for xx, g in calls for wt in g)
+    res = {}
+    for name, fn, launches in (("grouped (4 launches)", grouped, 4), ("seven single calls", single, 7)):
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        key = (f"NVFP4 linear, one {ws.name.split(' (')[0]} layer (q, k, v, o, gate, up, down) at {m_tok} tokens, "
+               f"{name}, one HIP graph replay (after the steps)")
+        res[key] = {"ms": round(ms, 4), "TFLOP_s": round(flop / (ms * 1e-3) / 1e12, 1), "GB_s": round(gbs, 1),
+                    "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        del graph
+    return res
 
 
 if __name__ == "__main__":

@@ -838,10 +838,12 @@ hipError_t launch_act_per_token(const uint16_t* x, int64_t tokens, int64_t hidde
     // workgroups while there are rows for them.  Measured on X [T, 4096]:
     // 17.2 us at T = 8192 and 125 us at 65536 against 19.1 and 129 us with
     // one row per wavefront; 16 or more rows per wavefront were slower.
-    // FourOverSix, bound by its arithmetic, keeps one row per wavefront.
+    // FourOverSix likewise: 400 us at T = 131072 against 421 us with one row
+    // per wavefront (31.5 against 30.9 us at T = 8192).  Issuing the second
+    // row's loads before quantizing the first was slower (25 us at 8192).
     const int64_t g1 = (tokens + kActWaves - 1) / kActWaves;
     int64_t g = (tokens + 2 * kActWaves - 1) / (2 * kActWaves);
-    if (g < 1024 || fo6) g = g1 < 1024 || fo6 ? g1 : 1024;
+    if (g < 1024) g = g1 < 1024 ? g1 : 1024;
     const dim3 grid((unsigned)g), block(64 * kActWaves);
     auto X = reinterpret_cast<const uint4*>(x);
     auto C = reinterpret_cast<uint2*>(codes);
