@@ -371,9 +371,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
 // Measured on MI355X: the launch and load latency of a few-microsecond kernel
 // dominate, so the wavefronts keep one step in flight each and there are
 // many of them (8 per workgroup; 2 or 4 steps in flight per wavefront, or 16
-// wavefronts per workgroup, were slower), and T = 2 pays only where the
-// output still has a workgroup per CU with it (X is then read and
-// dequantized half as often).  Against 32 x 32 tiles with four steps in
+// wavefronts per workgroup, were slower), and T = 2 (T = 4 with one token
+// tile) pays only where the output still has a workgroup per CU with it (X
+// is then read and dequantized half or a quarter as often).  Against 32 x 32 tiles with four steps in
 // flight per wavefront (its predecessor for 16 < M <= 64), 17 to 64 tokens
 // through the Llama-3.1-8B layer shapes took 36-68 us instead of 58-96 us;
 // 65 to 128 tokens take about 15 % less time than the tiled kernel's
@@ -603,18 +603,22 @@ static hipError_t device_cus(int64_t& cus) {
 hipError_t nvfp4_linear_cus(int64_t& cus) { return device_cus(cus); }
 
 // Decode launch configuration for an [M, N] output and `steps` 256-wide
-// k-steps per k range: 16-column tiles per wavefront (2 when that still
-// leaves a workgroup per CU), wavefronts per workgroup (8; 4 for fewer than
-// 8 steps, for eight token tiles, and for four on 32 columns, where 8
-// measured slower) and 16-token tiles (1, 2, 4 or 8).
+// k-steps per k range: 16-column tiles per wavefront (with one token tile 4
+// when that still leaves a workgroup per CU, else 2 when that does, else 1:
+// every X fragment is dequantized once per T W fragments; measured on 16
+// tokens, T = 4 took gate and up of an 8B layer in 18.0 us against 19.4 and
+// 28672 x 8192 in 32.6 against 35.4, and nothing below a workgroup per CU),
+// wavefronts per workgroup (8; 4 for fewer than 8 steps, for eight token
+// tiles, and for four on 32 columns, where 8 measured slower) and 16-token
+// tiles (1, 2, 4 or 8).
 struct GemvConfig {
     int t, waves, mt;
 };
 
 static GemvConfig gemv_config(int64_t M, int64_t N, int64_t steps, int64_t cus) {
     GemvConfig c;
-    c.t = (N + 31) / 32 >= cus ? 2 : 1;
     c.mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
+    c.t = c.mt == 1 && (N + 63) / 64 >= cus ? 4 : (N + 31) / 32 >= cus ? 2 : 1;
     c.waves = steps >= 8 && c.mt < 8 && !(c.mt == 4 && c.t == 2) ? 8 : 4;
     return c;
 }
@@ -691,6 +695,7 @@ static hipError_t launch_gemv(const GemvConfig& c, dim3 grid, dim3 block, hipStr
         FOCUS_GV(2, 8, 1) FOCUS_GV(2, 4, 1) FOCUS_GV(2, 8, 2) FOCUS_GV(2, 4, 2)
         FOCUS_GV(4, 8, 1) FOCUS_GV(4, 4, 1) FOCUS_GV(4, 8, 2) FOCUS_GV(4, 4, 2)
         FOCUS_GV(8, 4, 1) FOCUS_GV(8, 4, 2)
+        FOCUS_GV(1, 8, 4) FOCUS_GV(1, 4, 4)
     }
 #undef FOCUS_GV
     return hipErrorInvalidValue;
