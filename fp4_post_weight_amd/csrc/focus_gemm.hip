@@ -370,8 +370,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
 //
 // Measured on MI355X: the launch and load latency of a few-microsecond kernel
 // dominate, so the wavefronts keep one step in flight each and there are
-// many of them (8 per workgroup; 2 or 4 steps in flight per wavefront, or 16
-// wavefronts per workgroup, were slower), and T = 2 (T = 4 with one token
+// many of them (8 per workgroup, 16 for long rows of one column tile; 2 or 4
+// steps in flight per wavefront, or 16 wavefronts per workgroup elsewhere,
+// were slower), and T = 2 (T = 4 with one token
 // tile) pays only where the output still has a workgroup per CU with it (X
 // is then read and dequantized half or a quarter as often).  Against 32 x 32 tiles with four steps in
 // flight per wavefront (its predecessor for 16 < M <= 64), 17 to 64 tokens
@@ -609,8 +610,12 @@ hipError_t nvfp4_linear_cus(int64_t& cus) { return device_cus(cus); }
 // tokens, T = 4 took gate and up of an 8B layer in 18.0 us against 19.4 and
 // 28672 x 8192 in 32.6 against 35.4, and nothing below a workgroup per CU),
 // wavefronts per workgroup (8; 4 for fewer than 8 steps, for eight token
-// tiles, and for four on 32 columns, where 8 measured slower) and 16-token
-// tiles (1, 2, 4 or 8).
+// tiles, and for four on 32 columns, where 8 measured slower; 16 for one
+// token tile and one column tile with at least 32 steps, where two
+// wavefronts per SIMD keep too little of W in flight, when the output has a
+// workgroup per CU: 4096 x 14336 at 16 tokens 12.5-13.1 against 13.3-13.9
+// us, no gain with T = 2 or 4) and
+// 16-token tiles (1, 2, 4 or 8).
 struct GemvConfig {
     int t, waves, mt;
 };
@@ -620,6 +625,7 @@ static GemvConfig gemv_config(int64_t M, int64_t N, int64_t steps, int64_t cus) 
     c.mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
     c.t = c.mt == 1 && (N + 63) / 64 >= cus ? 4 : (N + 31) / 32 >= cus ? 2 : 1;
     c.waves = steps >= 8 && c.mt < 8 && !(c.mt == 4 && c.t == 2) ? 8 : 4;
+    if (c.mt == 1 && c.t == 1 && steps >= 32 && (N + 15) / 16 >= cus) c.waves = 16;
     return c;
 }
 
@@ -696,6 +702,7 @@ static hipError_t launch_gemv(const GemvConfig& c, dim3 grid, dim3 block, hipStr
         FOCUS_GV(4, 8, 1) FOCUS_GV(4, 4, 1) FOCUS_GV(4, 8, 2) FOCUS_GV(4, 4, 2)
         FOCUS_GV(8, 4, 1) FOCUS_GV(8, 4, 2)
         FOCUS_GV(1, 8, 4) FOCUS_GV(1, 4, 4)
+        FOCUS_GV(1, 16, 1)
     }
 #undef FOCUS_GV
     return hipErrorInvalidValue;
