@@ -103,7 +103,8 @@ SHAPES = [(1, 1, 16), (3, 17, 256), (7, 33, 48), (12, 4111, 320), (16, 200, 1040
           (17, 64, 64), (32, 4096, 4096), (33, 1000, 1040), (64, 512, 8192), (64, 300, 14336),
           (32, 1000, 28672), (100, 520, 28672), (100, 8200, 80), (65, 130, 192), (100, 8200, 512), (128, 1000, 4160), (129, 130, 192), (255, 257, 64), (257, 255, 1040),
           (300, 520, 4096), (513, 96, 80),
-          (16, 16400, 256), (9, 16448, 1040)]  # four 16-column tiles per wavefront, ragged
+          (16, 16400, 256), (9, 16448, 1040),  # four 16-column tiles per wavefront, ragged
+          (16, 6200, 512)]  # two tiles at three workgroups per four CUs, ragged
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES, ids=lambda v: str(v))
