@@ -604,14 +604,16 @@ static hipError_t device_cus(int64_t& cus) {
 hipError_t nvfp4_linear_cus(int64_t& cus) { return device_cus(cus); }
 
 // Decode launch configuration for an [M, N] output and `steps` 256-wide
-// k-steps per k range: 16-column tiles per wavefront (with one token tile 4
-// when that still leaves a workgroup per CU, else 2 when that leaves three
-// workgroups per four CUs -- a workgroup per CU with more token tiles --
-// else 1: every X fragment is dequantized once per T W fragments; measured
-// on 16 tokens, T = 4 took gate and up of an 8B layer in 18.0 us against
-// 19.4 and 28672 x 8192 in 32.6 against 35.4, and gained nothing below a
-// workgroup per CU; T = 2 took q, k and v (6144 columns, 192 workgroups) in
-// 7.3-7.5 us against 8.1),
+// k-steps per k range: 16-column tiles per wavefront (4 when that still
+// leaves a workgroup per CU, else 2 when that leaves three workgroups per
+// four CUs, else 1: every X fragment is dequantized once per T W fragments;
+// measured on 16 tokens, T = 4 took gate and up of an 8B layer in 18.0 us
+// against 19.4 and 28672 x 8192 in 32.6 against 35.4, and gained nothing
+// below a workgroup per CU; T = 2 took q, k and v (6144 columns, 192
+// workgroups) in 7.3-7.5 us against 8.1; with more token tiles the same
+// rules took 28672 x 8192 in 41.4 against 48.1 us at 32 tokens, 59.1
+// against 70.7 at 64 and 113 against 151 at 128, and q, k and v in 9.2
+// against 10.9 at 32 and 13.9 against 17.1 at 64),
 // wavefronts per workgroup (8; 4 for fewer than 8 steps, for eight token
 // tiles, and for four on 32 columns, where 8 measured slower; 16 for one
 // token tile and one column tile with at least 32 steps, where two
@@ -626,7 +628,7 @@ struct GemvConfig {
 static GemvConfig gemv_config(int64_t M, int64_t N, int64_t steps, int64_t cus) {
     GemvConfig c;
     c.mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
-    c.t = c.mt == 1 && (N + 63) / 64 >= cus ? 4 : (N + 31) / 32 >= (c.mt == 1 ? (3 * cus) / 4 : cus) ? 2 : 1;
+    c.t = (N + 63) / 64 >= cus ? 4 : (N + 31) / 32 >= (3 * cus) / 4 ? 2 : 1;
     c.waves = steps >= 8 && c.mt < 8 && !(c.mt == 4 && c.t == 2) ? 8 : 4;
     if (c.mt == 1 && c.t == 1 && steps >= 32 && (N + 15) / 16 >= cus) c.waves = 16;
     return c;
@@ -704,7 +706,8 @@ static hipError_t launch_gemv(const GemvConfig& c, dim3 grid, dim3 block, hipStr
         FOCUS_GV(2, 8, 1) FOCUS_GV(2, 4, 1) FOCUS_GV(2, 8, 2) FOCUS_GV(2, 4, 2)
         FOCUS_GV(4, 8, 1) FOCUS_GV(4, 4, 1) FOCUS_GV(4, 8, 2) FOCUS_GV(4, 4, 2)
         FOCUS_GV(8, 4, 1) FOCUS_GV(8, 4, 2)
-        FOCUS_GV(1, 8, 4) FOCUS_GV(1, 4, 4)
+        FOCUS_GV(1, 8, 4) FOCUS_GV(1, 4, 4) FOCUS_GV(2, 8, 4) FOCUS_GV(2, 4, 4)
+        FOCUS_GV(4, 8, 4) FOCUS_GV(4, 4, 4) FOCUS_GV(8, 4, 4)
         FOCUS_GV(1, 16, 1)
     }
 #undef FOCUS_GV

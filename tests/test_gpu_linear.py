@@ -105,7 +105,9 @@ SHAPES = [(1, 1, 16), (3, 17, 256), (7, 33, 48), (12, 4111, 320), (16, 200, 1040
           (300, 520, 4096), (513, 96, 80),
           (16, 16400, 256), (9, 16448, 1040),  # four 16-column tiles per wavefront, ragged
           (16, 6200, 512),  # two tiles at three workgroups per four CUs, ragged
-          (16, 4100, 8224)]  # 16 wavefronts per workgroup (33 k-steps, the last one masked), ragged
+          (16, 4100, 8224),  # 16 wavefronts per workgroup (33 k-steps, the last one masked), ragged
+          (24, 16400, 512), (33, 16448, 2064), (100, 16400, 256),  # four tiles with 2, 4, 8 token tiles
+          (33, 6200, 512), (97, 6200, 1040)]  # two tiles at three workgroups per four CUs, 4 and 8 token tiles
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES, ids=lambda v: str(v))
@@ -308,7 +310,7 @@ def test_split_model_workspace(focus):
 # sizes; ragged N, K not a multiple of 256 (masked loads), M on both kernels
 GROUPS = [(16, [4096, 1024, 1024], 4096), (1, [14336, 14336], 4096), (5, [17, 300, 1], 1040),
           (64, [520, 100, 33, 7, 1, 2, 3, 4, 5], 512), (128, [256, 130], 2064), (129, [130, 60], 192),
-          (300, [520, 96], 1040), (16, [16000, 417], 512)]  # last: four tiles, ragged member
+          (300, [520, 96], 1040), (16, [16000, 417], 512), (64, [16000, 417], 512)]  # last two: four tiles, ragged member
 
 
 @pytest.mark.parametrize("M,Ns,K", GROUPS, ids=lambda v: str(v))
