@@ -158,12 +158,13 @@ __device__ __forceinline__ void wave_gather_blocks(uint4& lo, uint4& hi, uint4* 
 
 // One 16-element block: codes (two dwords) and scale byte are stored here;
 // w' (32 bytes) is returned in deq0 / deq1 for the caller's wavefront-wide
-// contiguous store.
-template <bool HAS_SIG, bool DEQ>
+// contiguous store.  PRE: the caller already holds the block maximum
+// (block_amax_bits of a, b) and passes it in amax_pre.
+template <bool HAS_SIG, bool DEQ, bool PRE = false>
 __device__ __forceinline__ void quantize_block(uint4 a, uint4 b, float mb, float q0, float q1,
                                                float s2, double rden, const double* tab,
                                                uint2* codes_out, uint8_t* scale_out, uint4& deq0,
-                                               uint4& deq1) {
+                                               uint4& deq1, float amax_pre = 0.0f) {
     const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     float f[16];
 #pragma unroll
@@ -182,7 +183,7 @@ __device__ __forceinline__ void quantize_block(uint4 a, uint4 b, float mb, float
         }
         return;
     }
-    const float amax = block_amax_bits(a, b);
+    const float amax = PRE ? amax_pre : block_amax_bits(a, b);
     const uint32_t sb = e4m3_byte_normal(block_t(amax, mb, rden));
     const float S = e4m3_normal_value(sb);
     float sig0 = 1.0f, sig1 = 1.0f;
@@ -204,10 +205,10 @@ __device__ __forceinline__ void quantize_block(uint4 a, uint4 b, float mb, float
 
 // FourOverSix for one block; same interface as quantize_block (rden6 and
 // rden4 are RN64(1/RN32(6*s2)) and RN64(1/RN32(4*s2))).
-template <bool DEQ>
+template <bool DEQ, bool PRE = false>
 __device__ __forceinline__ void fo6_block(uint4 a, uint4 b, float s2, double rden6, double rden4,
                                           uint2* codes_out, uint8_t* scale_out, uint4& deq0,
-                                          uint4& deq1) {
+                                          uint4& deq1, float amax_pre = 0.0f) {
     const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     float f[16];
 #pragma unroll
@@ -225,7 +226,7 @@ __device__ __forceinline__ void fo6_block(uint4 a, uint4 b, float s2, double rde
         }
         return;
     }
-    const float amax = block_amax_bits(a, b);
+    const float amax = PRE ? amax_pre : block_amax_bits(a, b);
     const uint32_t sb6 = e4m3_byte_normal(block_t(amax, 1.0f, rden6));
     const uint32_t sb4 = e4m3_byte_normal(block_t(amax, 1.0f, rden4));
     const float S6 = e4m3_normal_value(sb6), S4 = e4m3_normal_value(sb4);
@@ -659,6 +660,7 @@ __global__ __launch_bounds__(64 * kActWaves) void k_act(const uint4* __restrict_
         float amax = 0.0f;
         constexpr int R = RB > 0 ? RB : 1;
         uint4 va[R], vb[R];
+        float bam[R];  // block maxima, kept for the quantize pass
         if (RB > 0 && kActGather && nb % 64 == 0) {
             // contiguous 1 KB per load instruction, regrouped through LDS so
             // that lane l holds block 64 k + l
@@ -674,7 +676,8 @@ __global__ __launch_bounds__(64 * kActWaves) void k_act(const uint4* __restrict_
             for (int k = 0; k < R; ++k) {
                 if (64 * k < nb) {
                     wave_gather_blocks(va[k], vb[k], xg, lane);
-                    amax = fmaxf(amax, block_amax_bits(va[k], vb[k]));
+                    bam[k] = block_amax_bits(va[k], vb[k]);
+                    amax = fmaxf(amax, bam[k]);
                 }
             }
         } else if (RB > 0) {
@@ -684,7 +687,8 @@ __global__ __launch_bounds__(64 * kActWaves) void k_act(const uint4* __restrict_
                 if (j < nb) {
                     va[k] = x[2 * (base + j)];
                     vb[k] = x[2 * (base + j) + 1];
-                    amax = fmaxf(amax, block_amax_bits(va[k], vb[k]));
+                    bam[k] = block_amax_bits(va[k], vb[k]);
+                    amax = fmaxf(amax, bam[k]);
                 }
             }
         } else {
@@ -704,11 +708,12 @@ __global__ __launch_bounds__(64 * kActWaves) void k_act(const uint4* __restrict_
                 uint4 d0 = make_uint4(0, 0, 0, 0), d1 = d0;
                 if (j < nb) {
                     if (FO6)
-                        fo6_block<DEQ>(va[k], vb[k], s2, rden, rden4, codes + base + j, scales + base + j,
-                                       d0, d1);
+                        fo6_block<DEQ, true>(va[k], vb[k], s2, rden, rden4, codes + base + j,
+                                             scales + base + j, d0, d1, bam[k]);
                     else
-                        quantize_block<false, DEQ>(va[k], vb[k], 1.0f, 0.0f, 0.0f, s2, rden, nullptr,
-                                                   codes + base + j, scales + base + j, d0, d1);
+                        quantize_block<false, DEQ, true>(va[k], vb[k], 1.0f, 0.0f, 0.0f, s2, rden, nullptr,
+                                                         codes + base + j, scales + base + j, d0, d1,
+                                                         bam[k]);
                 }
                 if (DEQ && j0 < nb) wave_store_blocks(xdeq + 2 * (base + j0), d0, d1, xw, lane, nb - j0);
             }
