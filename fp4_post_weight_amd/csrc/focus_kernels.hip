@@ -383,8 +383,19 @@ __device__ __forceinline__ bool mix_block_is_e0m3(const Batch& bt, int j, int64_
 // 2j and 2j+1 share one 32-block: m[blk/2], scale byte stored by the even
 // lane, no tensor scale); 3: FlipQuant MixFP4 (Batch = MixBatch; each block
 // looks up its tile's map byte: E0M3 if set, FourOverSix otherwise).
+// Minimum wavefronts per SIMD the register allocation must allow (1: no
+// limit).  FourOverSix codes-only fits 96 VGPRs without spilling, which
+// leaves room for 5 wavefronts instead of 4 (100 VGPRs): 1.12 against
+// 1.15-1.18 ms on 64 linears of the 8B set, identical outputs.  With w' the
+// FourOverSix and MixFP4 kernels spill at that limit and were 25 % slower.
+template <bool DEQ, int MODE>
+struct QuantWaves {
+    static constexpr int value = MODE == 1 && !DEQ ? 5 : 1;
+};
+
 template <bool HAS_M, bool HAS_Q, bool DEQ, int MODE = 0, typename Batch = QuantBatch>
-__global__ __launch_bounds__(kThreads) void k_quantize(Batch bt, int64_t ntiles) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QuantWaves<DEQ, MODE>::value)))
+void k_quantize(Batch bt, int64_t ntiles) {
     constexpr bool FO6 = MODE == 1 || MODE == 3, MX = MODE == 2, MIX = MODE == 3;
     constexpr int kQuantU = QuantU<DEQ, MODE>::value;
     __shared__ uint4 xch[DEQ ? kThreads / 64 : 1][128];
