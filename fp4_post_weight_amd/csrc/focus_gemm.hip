@@ -50,7 +50,7 @@
 //    row past the end of X or W reads the last row instead; it only feeds
 //    outputs that are never stored.
 //  * With few tokens (M <= 128) the layer is bound by streaming W, and a
-//    decode kernel without LDS operand tiles takes over
+//    decode kernel without shared LDS operand tiles takes over
 //    (v_mfma_f32_16x16x32_f16, 1, 2, 4 or 8 tiles of 16 tokens).  When an output
 //    has too few columns to fill the GPU, the sum over k is split into ranges
 //    whose partials a finalize kernel adds in order.
@@ -355,7 +355,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
 // Decode (M <= 128): v_mfma_f32_16x16x32_f16 on MT = 1, 2, 4 or 8 tiles of
 // 16 tokens (every weight element feeds at most 128 outputs, so the layer is
 // bound by streaming W, or by the vector work of dequantizing X, and no
-// operand needs sharing through LDS).  A workgroup of WAVES wavefronts owns
+// operand needs sharing between wavefronts; with aligned operands and up to
+// 4 token tiles each wavefront still passes its W step through an LDS area of
+// its own, so that its loads take whole cache lines).  A workgroup of WAVES
+// wavefronts owns
 // 16 T output columns (16 T rows of W); the 256-wide k-steps of its k range
 // are dealt round-robin to its wavefronts, each accumulates MT x T partial
 // 16 x 16 tiles (a dequantized W fragment feeds all MT token tiles, an X
@@ -370,11 +373,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_nvfp4_linear(GemmArgs a, int64
 //
 // Measured on MI355X: the launch and load latency of a few-microsecond kernel
 // dominate, so the wavefronts keep one step in flight each and there are
-// many of them (8 per workgroup, 16 for long rows of one column tile; 2 or 4
+// many of them (8 per workgroup, 16 for long rows with one token tile; 2 or 4
 // steps in flight per wavefront, or 16 wavefronts per workgroup elsewhere,
-// were slower), and T = 2 (T = 4 with one token
-// tile) pays only where the output still has a workgroup per CU with it (X
-// is then read and dequantized half or a quarter as often).  Against 32 x 32 tiles with four steps in
+// were slower), and T = 2 (T = 4 with 4 or 8 token tiles) pays only where the
+// output still has most of a workgroup per CU with it (X is then read and
+// dequantized half or a quarter as often).  Against 32 x 32 tiles with four steps in
 // flight per wavefront (its predecessor for 16 < M <= 64), 17 to 64 tokens
 // through the Llama-3.1-8B layer shapes took 36-68 us instead of 58-96 us;
 // 65 to 128 tokens take about 15 % less time than the tiled kernel's
@@ -433,9 +436,26 @@ __device__ __forceinline__ uint32_t gemv_dword(const GemvChunk& c, int j) {
     return j < 4 ? dword_of(c.c0, j) : dword_of(c.c1, j - 4);
 }
 
+// W's step through the wavefront's own LDS area (FAST loads, at most 4 token
+// tiles and 2 column tiles).  In the matrix-instruction layout lanes 0-15
+// hold 16 different rows, so each quad of lanes of a direct load touches 4
+// cache lines; here 8 lanes load one row's whole 128-byte line (4 lanes its
+// 16 scale bytes), rows are stored 144 bytes apart, so that the reads in the
+// matrix layout (16 rows, 16 bytes each) hit distinct banks, and read back.
+// Measured on the read pattern alone (28672 x 8192): 6.8 against 5.8 TB/s.
+constexpr int kStageRow = 144;
+template <int T>
+struct GemvStage {
+    static constexpr int bytes = 16 * T * (kStageRow + 16);  // codes, then 16 scale bytes per row
+};
+
 template <bool FAST, bool BF16_OUT, int WAVES, int T, int MT>
 __global__ __launch_bounds__(64 * WAVES) void k_nvfp4_linear_gemv(GemmArgs a, GemvMembers mem) {
-    __shared__ float red[WAVES][MT * T * 16 * 16];
+    constexpr bool kStaged = FAST && MT <= 4 && T <= 2;
+    constexpr int kRed = WAVES * MT * T * 256 * 4;
+    constexpr int kStage = kStaged ? WAVES * GemvStage<T>::bytes : 0;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kRed > kStage ? kRed : kStage];
+    float(*red)[MT * T * 16 * 16] = reinterpret_cast<float(*)[MT * T * 16 * 16]>(lds);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -466,8 +486,43 @@ __global__ __launch_bounds__(64 * WAVES) void k_nvfp4_linear_gemv(GemmArgs a, Ge
         GemvChunk w[T], x[MT];
         for (int64_t i = 0; i < my; ++i) {
             const int64_t k0 = (sb + wave + (int64_t)WAVES * i) * kGemvK;
+            if (kStaged) {
+                uint8_t* st = lds + wave * GemvStage<T>::bytes;
+                uint4 v[2 * T];
+                uint32_t sv[T];
+                // rows past N read the last row, as in load_gemv
 #pragma unroll
-            for (int t = 0; t < T; ++t) w[t] = load_gemv<FAST>(wc, wsc, n0 + 16 * t + c16, N, a.K, k0, g);
+                for (int i = 0; i < 2 * T; ++i) {
+                    const int64_t row = n0 + 8 * i + (lane >> 3);
+                    const int64_t rr = row < N ? row : N - 1;
+                    v[i] = *reinterpret_cast<const uint4*>(wc + rr * (a.K / 2) + k0 / 2 + 16 * (lane & 7));
+                }
+#pragma unroll
+                for (int i = 0; i < T; ++i) {
+                    const int64_t row = n0 + 16 * i + (lane >> 2);
+                    const int64_t rr = row < N ? row : N - 1;
+                    sv[i] = *reinterpret_cast<const uint32_t*>(wsc + rr * (a.K / 16) + k0 / 16 + 4 * (lane & 3));
+                }
+#pragma unroll
+                for (int i = 0; i < 2 * T; ++i)
+                    *reinterpret_cast<uint4*>(st + (8 * i + (lane >> 3)) * kStageRow + 16 * (lane & 7)) = v[i];
+#pragma unroll
+                for (int i = 0; i < T; ++i)
+                    *reinterpret_cast<uint32_t*>(st + 16 * T * kStageRow + (16 * i + (lane >> 2)) * 16 + 4 * (lane & 3)) =
+                        sv[i];
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const uint8_t* rp = st + (16 * t + c16) * kStageRow + 32 * g;
+                    w[t].c0 = *reinterpret_cast<const uint4*>(rp);
+                    w[t].c1 = *reinterpret_cast<const uint4*>(rp + 16);
+                    w[t].s = *reinterpret_cast<const uint32_t*>(st + 16 * T * kStageRow + (16 * t + c16) * 16 + 4 * g);
+                }
+                __builtin_amdgcn_wave_barrier();
+            } else {
+#pragma unroll
+                for (int t = 0; t < T; ++t) w[t] = load_gemv<FAST>(wc, wsc, n0 + 16 * t + c16, N, a.K, k0, g);
+            }
 #pragma unroll
             for (int m = 0; m < MT; ++m) x[m] = load_gemv<FAST>(a.xc, a.xs, 16 * m + c16, a.M, a.K, k0, g);
             f16x2 w01[T], w23[T], x01[MT], x23[MT];
@@ -498,7 +553,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_nvfp4_linear_gemv(GemmArgs a, Ge
     }
 
     // register r of lane l in tile (m, t): token 16 m + 4 (l / 16) + r,
-    // column 16 t + l % 16; red holds (m, t, token % 16, column % 16)
+    // column 16 t + l % 16; red holds (m, t, token % 16, column % 16).  It
+    // shares LDS with the staging areas, so every wavefront leaves the loop
+    // first.
+    if (kStaged) __syncthreads();
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -604,23 +662,21 @@ static hipError_t device_cus(int64_t& cus) {
 hipError_t nvfp4_linear_cus(int64_t& cus) { return device_cus(cus); }
 
 // Decode launch configuration for an [M, N] output and `steps` 256-wide
-// k-steps per k range: 16-column tiles per wavefront (4 when that still
-// leaves a workgroup per CU, else 2 when that leaves three workgroups per
-// four CUs, else 1: every X fragment is dequantized once per T W fragments;
-// measured on 16 tokens, T = 4 took gate and up of an 8B layer in 18.0 us
-// against 19.4 and 28672 x 8192 in 32.6 against 35.4, and gained nothing
-// below a workgroup per CU; T = 2 took q, k and v (6144 columns, 192
-// workgroups) in 7.3-7.5 us against 8.1; with more token tiles the same
-// rules took 28672 x 8192 in 41.4 against 48.1 us at 32 tokens, 59.1
-// against 70.7 at 64 and 113 against 151 at 128, and q, k and v in 9.2
-// against 10.9 at 32 and 13.9 against 17.1 at 64),
-// wavefronts per workgroup (8; 4 for fewer than 8 steps, for eight token
-// tiles, and for four on 32 columns, where 8 measured slower; 16 for one
-// token tile and one column tile with at least 32 steps, where two
-// wavefronts per SIMD keep too little of W in flight, when the output has a
-// workgroup per CU: 4096 x 14336 at 16 tokens 12.5-13.1 against 13.3-13.9
-// us, no gain with T = 2 or 4) and
-// 16-token tiles (1, 2, 4 or 8).
+// k-steps per k range.  16-column tiles per wavefront T: with 4 or 8 token
+// tiles 4 when that still leaves a workgroup per CU (every X fragment is then
+// dequantized once per 4 W fragments: 28672 x 8192 at 64 tokens 59.1 against
+// 70.7 us, at 128 tokens 113 against 151), else 2 when that leaves three
+// workgroups per four CUs, else 1.  With 1 or 2 token tiles, where W goes
+// through the LDS staging area, 2 at most: gate and up of an 8B layer at 16
+// tokens took 13.7-15.4 us against 18.1-18.9 with 4 tiles and direct loads,
+// 28672 x 8192 29.2-29.7 against 32.8-33.4.  Wavefronts per workgroup: 8; 4
+// for fewer than 8 steps, for eight token tiles, and for four on 32 columns,
+// where 8 measured slower; 16 with one token tile for rows of at least 32
+// steps, where two wavefronts per SIMD keep too little of W in flight -- with
+// one column tile when the output has a workgroup per CU (4096 x 14336 at 16
+// tokens 12.5-13.1 against 13.3-13.9 us with direct loads), with two when it
+// has at most one (8192 x 28672 at 1 token 23.2-23.8 against 26.8-27.1 us).
+// 16-token tiles: 1, 2, 4 or 8.
 struct GemvConfig {
     int t, waves, mt;
 };
@@ -628,9 +684,10 @@ struct GemvConfig {
 static GemvConfig gemv_config(int64_t M, int64_t N, int64_t steps, int64_t cus) {
     GemvConfig c;
     c.mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
-    c.t = (N + 63) / 64 >= cus ? 4 : (N + 31) / 32 >= (3 * cus) / 4 ? 2 : 1;
+    c.t = c.mt >= 4 && (N + 63) / 64 >= cus ? 4 : (N + 31) / 32 >= (3 * cus) / 4 ? 2 : 1;
     c.waves = steps >= 8 && c.mt < 8 && !(c.mt == 4 && c.t == 2) ? 8 : 4;
     if (c.mt == 1 && c.t == 1 && steps >= 32 && (N + 15) / 16 >= cus) c.waves = 16;
+    if (c.mt == 1 && c.t == 2 && steps >= 32 && (N + 31) / 32 <= cus) c.waves = 16;
     return c;
 }
 
@@ -706,9 +763,8 @@ static hipError_t launch_gemv(const GemvConfig& c, dim3 grid, dim3 block, hipStr
         FOCUS_GV(2, 8, 1) FOCUS_GV(2, 4, 1) FOCUS_GV(2, 8, 2) FOCUS_GV(2, 4, 2)
         FOCUS_GV(4, 8, 1) FOCUS_GV(4, 4, 1) FOCUS_GV(4, 8, 2) FOCUS_GV(4, 4, 2)
         FOCUS_GV(8, 4, 1) FOCUS_GV(8, 4, 2)
-        FOCUS_GV(1, 8, 4) FOCUS_GV(1, 4, 4) FOCUS_GV(2, 8, 4) FOCUS_GV(2, 4, 4)
         FOCUS_GV(4, 8, 4) FOCUS_GV(4, 4, 4) FOCUS_GV(8, 4, 4)
-        FOCUS_GV(1, 16, 1)
+        FOCUS_GV(1, 16, 1) FOCUS_GV(1, 16, 2)
     }
 #undef FOCUS_GV
     return hipErrorInvalidValue;

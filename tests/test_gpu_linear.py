@@ -96,18 +96,22 @@ def test_exact_when_partial_sums_are_exact(focus, orc, M):
 
 
 # M <= 128 takes the decode kernel (1, 2, 4 or 8 tiles of 16 tokens; K % 256
-# != 0: masked loads), larger M the tiled kernel (K % 64 != 0: masked loads);
-# some shapes split k.
+# != 0: masked loads; K % 256 == 0 with up to 4 token tiles and 2 column tiles
+# per wavefront: W through the wavefront's LDS area), larger M the tiled
+# kernel (K % 64 != 0: masked loads); some shapes split k.
 SHAPES = [(1, 1, 16), (3, 17, 256), (7, 33, 48), (12, 4111, 320), (16, 200, 1040), (16, 4096, 4096),
           (5, 1000, 28672), (16, 1024, 28688), (1, 14336, 512), (3, 8200, 80), (20, 8192, 256), (50, 8200, 512),
           (17, 64, 64), (32, 4096, 4096), (33, 1000, 1040), (64, 512, 8192), (64, 300, 14336),
           (32, 1000, 28672), (100, 520, 28672), (100, 8200, 80), (65, 130, 192), (100, 8200, 512), (128, 1000, 4160), (129, 130, 192), (255, 257, 64), (257, 255, 1040),
           (300, 520, 4096), (513, 96, 80),
-          (16, 16400, 256), (9, 16448, 1040),  # four 16-column tiles per wavefront, ragged
+          (16, 16400, 256), (9, 16448, 1040),  # two 16-column tiles per wavefront, through LDS and direct, ragged
           (16, 6200, 512),  # two tiles at three workgroups per four CUs, ragged
           (16, 4100, 8224),  # 16 wavefronts per workgroup (33 k-steps, the last one masked), ragged
-          (24, 16400, 512), (33, 16448, 2064), (100, 16400, 256),  # four tiles with 2, 4, 8 token tiles
-          (33, 6200, 512), (97, 6200, 1040)]  # two tiles at three workgroups per four CUs, 4 and 8 token tiles
+          (24, 16400, 512),  # two tiles with 2 token tiles
+          (33, 16448, 2064), (33, 16400, 1024), (100, 16400, 256),  # four tiles with 4 and 8 token tiles
+          (33, 6200, 512), (97, 6200, 1040),  # two tiles at three workgroups per four CUs, 4 and 8 token tiles
+          (7, 1000, 4096),  # one tile through LDS, rows past N read the last row, ragged
+          (5, 8180, 8192)]  # 16 wavefronts with two tiles (32 k-steps, a workgroup per CU), ragged
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES, ids=lambda v: str(v))
@@ -310,7 +314,8 @@ def test_split_model_workspace(focus):
 # sizes; ragged N, K not a multiple of 256 (masked loads), M on both kernels
 GROUPS = [(16, [4096, 1024, 1024], 4096), (1, [14336, 14336], 4096), (5, [17, 300, 1], 1040),
           (64, [520, 100, 33, 7, 1, 2, 3, 4, 5], 512), (128, [256, 130], 2064), (129, [130, 60], 192),
-          (300, [520, 96], 1040), (16, [16000, 417], 512), (64, [16000, 417], 512)]  # last two: four tiles, ragged member
+          (300, [520, 96], 1040), (16, [16000, 417], 512),  # two tiles through LDS, ragged member
+          (64, [16000, 417], 512)]  # four tiles, ragged member
 
 
 @pytest.mark.parametrize("M,Ns,K", GROUPS, ids=lambda v: str(v))
