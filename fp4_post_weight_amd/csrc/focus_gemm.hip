@@ -670,8 +670,12 @@ hipError_t nvfp4_linear_cus(int64_t& cus) { return device_cus(cus); }
 // through the LDS staging area, 2 at most: gate and up of an 8B layer at 16
 // tokens took 13.7-15.4 us against 18.1-18.9 with 4 tiles and direct loads,
 // 28672 x 8192 29.2-29.7 against 32.8-33.4.  Wavefronts per workgroup: 8; 4
-// for fewer than 8 steps, for eight token tiles, and for four on 32 columns,
-// where 8 measured slower; 16 with one token tile for rows of at least 32
+// for fewer than 8 steps, for eight token tiles, for four on 32 columns, where
+// 8 measured slower, and for two column tiles that leave at least three
+// workgroups per CU with 1 or 2 token tiles, which are then all resident at
+// once (gate and up at 16 tokens 13.0-13.4 against 14.2-14.9 us, 28672 x 8192
+// 25.9-26.4 against 29.5-29.6; below that 4 were slower); 16 with one token
+// tile for rows of at least 32
 // steps, where two wavefronts per SIMD keep too little of W in flight -- with
 // one column tile when the output has a workgroup per CU (4096 x 14336 at 16
 // tokens 12.5-13.1 against 13.3-13.9 us with direct loads), with two when it
@@ -686,6 +690,7 @@ static GemvConfig gemv_config(int64_t M, int64_t N, int64_t steps, int64_t cus) 
     c.mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
     c.t = c.mt >= 4 && (N + 63) / 64 >= cus ? 4 : (N + 31) / 32 >= (3 * cus) / 4 ? 2 : 1;
     c.waves = steps >= 8 && c.mt < 8 && !(c.mt == 4 && c.t == 2) ? 8 : 4;
+    if (c.mt <= 2 && c.t == 2 && (N + 31) / 32 >= 3 * cus) c.waves = 4;
     if (c.mt == 1 && c.t == 1 && steps >= 32 && (N + 15) / 16 >= cus) c.waves = 16;
     if (c.mt == 1 && c.t == 2 && steps >= 32 && (N + 31) / 32 <= cus) c.waves = 16;
     return c;

@@ -108,6 +108,7 @@ SHAPES = [(1, 1, 16), (3, 17, 256), (7, 33, 48), (12, 4111, 320), (16, 200, 1040
           (16, 6200, 512),  # two tiles at three workgroups per four CUs, ragged
           (16, 4100, 8224),  # 16 wavefronts per workgroup (33 k-steps, the last one masked), ragged
           (24, 16400, 512),  # two tiles with 2 token tiles
+          (16, 24600, 256), (24, 24600, 512),  # two tiles, 4 wavefronts at three workgroups per CU, ragged
           (33, 16448, 2064), (33, 16400, 1024), (100, 16400, 256),  # four tiles with 4 and 8 token tiles
           (33, 6200, 512), (97, 6200, 1040),  # two tiles at three workgroups per four CUs, 4 and 8 token tiles
           (7, 1000, 4096),  # one tile through LDS, rows past N read the last row, ragged
