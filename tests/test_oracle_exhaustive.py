@@ -9,7 +9,14 @@ an independent formulation.
   the clamp leaves, against torch's float8_e4m3fn conversion.
 * BF16 (equation w'_i's rounding): every finite binary32 against torch's
   bfloat16 conversion.
+* expf (the sigmoid's exponential, read as correctly rounded): every binary32
+  argument in [-104, 89] (outside, the result is 0 or +inf), against binary64
+  exp rounded once to binary32, which is the correctly rounded result unless
+  the binary64 value lies within its own error of a binary32 midpoint; the
+  arguments within 2^-40 (relative) of one are settled with decimal
+  arithmetic at 60 digits.
 """
+from decimal import Decimal, localcontext
 import os
 from concurrent.futures import ThreadPoolExecutor
 
@@ -74,3 +81,42 @@ def test_bf16_every_finite_binary32(orc):
             out += int(np.count_nonzero(orc.bf16_round_array(x) != ref))
         return out
     assert _sweep(0, 0x7F800000, check) == 0  # every finite magnitude, both signs
+
+
+def _f32_nearest(d):
+    """The binary32 nearest to the Decimal d (d > 0, never a midpoint here:
+    exp of a nonzero binary32 is irrational)."""
+    f = np.float32(float(d))
+    best = None
+    for c in (np.nextafter(f, np.float32(0)), f, np.nextafter(f, np.float32(np.inf))):
+        err = abs(Decimal(float(c)) - d)
+        if best is None or err < best[0]:
+            best = (err, c)
+    return best[1]
+
+
+def test_expf_every_binary32_in_range(orc):
+    def check(bits):
+        x = bits.view(np.float32)
+        got = orc.expf_array(x)
+        with np.errstate(over="ignore", under="ignore"):
+            y = np.exp(x.astype(np.float64))
+            f = y.astype(np.float32)
+            toward = np.where(y > f.astype(np.float64), np.float32(np.inf), np.float32(-np.inf))
+            mid = (f.astype(np.float64) + np.nextafter(f, toward).astype(np.float64)) * 0.5
+        hard = np.abs(y - mid) <= np.abs(y) * 2.0 ** -40
+        bad = int(np.count_nonzero((got.view(np.uint32) != f.view(np.uint32)) & ~hard))
+        with localcontext() as ctx:
+            ctx.prec = 60
+            for xi, gi in zip(x[hard], got[hard]):
+                want = _f32_nearest(Decimal(float(xi)).exp())
+                bad += int(np.float32(gi).view(np.uint32) != want.view(np.uint32))
+        return bad
+
+    neg_hi = np.float32(-104.0).view(np.uint32).item() + 1
+    pos_hi = np.float32(89.0).view(np.uint32).item() + 1
+    assert _sweep(0x80000000, neg_hi, check) == 0  # -0 .. -104
+    assert _sweep(0, pos_hi, check) == 0           # +0 .. 89
+    edge = np.array([-200.0, -104.5, 89.5, 1e30, np.inf, -np.inf], dtype=np.float32)
+    assert np.array_equal(orc.expf_array(edge), np.array([0, 0, np.inf, np.inf, np.inf, 0], dtype=np.float32))
+
