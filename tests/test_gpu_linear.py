@@ -134,6 +134,37 @@ def test_linear_within_bound(focus, orc, M, N, K):
         check_bound(y0, ref, refabs, K, dt == torch.bfloat16, f"{(M, N, K)} {dt} no workspace")
 
 
+def _random_shapes(n, seed):
+    """Seeded random shapes over the decode and tiled kernels' configurations:
+    M in each token-tile band and past 128, N from one column to a few
+    thousand (ragged tiles), K aligned to 256 (LDS-staged loads in the decode
+    kernel) or not (masked loads), M * N * K kept small for the oracle."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = int(rng.choice([1, 2, 7, 16, 17, 31, 32, 33, 48, 64, 65, 100, 128, 129, 200]))
+        N = int(rng.integers(1, 4000))
+        K = int(256 * rng.integers(1, 24) + (0 if i % 2 == 0 else 16 * rng.integers(1, 16)))
+        while M * N * K > 60_000_000:
+            N = max(1, N // 2)
+        out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", _random_shapes(40, 2026), ids=lambda v: str(v))
+def test_linear_random_shapes(focus, orc, M, N, K):
+    """Seeded random shapes within the derived bound, with and without the
+    split-k workspace."""
+    xc, xs, wc, ws = operands(M, N, K, 7 * M + 3 * N + K)
+    rng = np.random.default_rng(N)
+    s2x = (rng.uniform(0.5, 2.0, M) * 2.0 ** -9).astype(np.float32)
+    s2w = np.float32(2.5e-4)
+    ref, refabs = oracle_linear(orc, xc.numpy(), xs.numpy(), s2x, wc.numpy(), ws.numpy(), s2w)
+    for ws_arg in ("auto", None):
+        y = gpu_linear(focus, xc, xs, s2x, wc, ws, s2w, torch.bfloat16, workspace=ws_arg)
+        check_bound(y, ref, refabs, K, True, f"{(M, N, K)} workspace={ws_arg}")
+
+
 @pytest.mark.parametrize("M,N,K", [(16, 1024, 28672), (100, 520, 28672), (8, 14336, 512), (2048, 1024, 4096)],
                          ids=lambda v: str(v))
 def test_linear_deterministic(focus, M, N, K):
