@@ -492,24 +492,24 @@ __global__ __launch_bounds__(64 * WAVES) void k_nvfp4_linear_gemv(GemmArgs a, Ge
                 uint32_t sv[T];
                 // rows past N read the last row, as in load_gemv
 #pragma unroll
-                for (int i = 0; i < 2 * T; ++i) {
-                    const int64_t row = n0 + 8 * i + (lane >> 3);
+                for (int r = 0; r < 2 * T; ++r) {
+                    const int64_t row = n0 + 8 * r + (lane >> 3);
                     const int64_t rr = row < N ? row : N - 1;
-                    v[i] = *reinterpret_cast<const uint4*>(wc + rr * (a.K / 2) + k0 / 2 + 16 * (lane & 7));
+                    v[r] = *reinterpret_cast<const uint4*>(wc + rr * (a.K / 2) + k0 / 2 + 16 * (lane & 7));
                 }
 #pragma unroll
-                for (int i = 0; i < T; ++i) {
-                    const int64_t row = n0 + 16 * i + (lane >> 2);
+                for (int r = 0; r < T; ++r) {
+                    const int64_t row = n0 + 16 * r + (lane >> 2);
                     const int64_t rr = row < N ? row : N - 1;
-                    sv[i] = *reinterpret_cast<const uint32_t*>(wsc + rr * (a.K / 16) + k0 / 16 + 4 * (lane & 3));
+                    sv[r] = *reinterpret_cast<const uint32_t*>(wsc + rr * (a.K / 16) + k0 / 16 + 4 * (lane & 3));
                 }
 #pragma unroll
-                for (int i = 0; i < 2 * T; ++i)
-                    *reinterpret_cast<uint4*>(st + (8 * i + (lane >> 3)) * kStageRow + 16 * (lane & 7)) = v[i];
+                for (int r = 0; r < 2 * T; ++r)
+                    *reinterpret_cast<uint4*>(st + (8 * r + (lane >> 3)) * kStageRow + 16 * (lane & 7)) = v[r];
 #pragma unroll
-                for (int i = 0; i < T; ++i)
-                    *reinterpret_cast<uint32_t*>(st + 16 * T * kStageRow + (16 * i + (lane >> 2)) * 16 + 4 * (lane & 3)) =
-                        sv[i];
+                for (int r = 0; r < T; ++r)
+                    *reinterpret_cast<uint32_t*>(st + 16 * T * kStageRow + (16 * r + (lane >> 2)) * 16 + 4 * (lane & 3)) =
+                        sv[r];
                 __builtin_amdgcn_wave_barrier();
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
