@@ -279,6 +279,40 @@ def act_ceiling(dev, tokens, hidden, reps=20):
     return ms, nbytes / (ms * 1e-3) / 1e9
 
 
+def act_step_position(focus, R, X, ACT, dev, reps=6):
+    """Mean time of the activation phase in the step's position (tensor scale,
+    quantize and dequantize of the set run first, so X is not in the caches),
+    for the quantizer and for the no-arithmetic kernel with its traffic and
+    work layout writing the same buffers, alternated.  Returns (ms, ms)."""
+    import torch
+    lib = _stream_lib()
+    tokens, hidden = X.shape
+    g1 = (tokens + 3) // 4
+    g = (tokens + 7) // 8
+    if g < 1024:
+        g = g1 if g1 < 1024 else 1024
+    stream = torch.cuda.current_stream(dev)
+
+    def pattern():
+        st = lib.focus_stream_act_pattern(X.data_ptr(), tokens, hidden // 1024, ACT.codes.data_ptr(),
+                                          ACT.scales.data_ptr(), ACT.s2.data_ptr(), g, stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"focus_stream_act_pattern failed with HIP error {st}")
+
+    calls = (lambda: focus.quantize_act_per_token(X, out=ACT), pattern)
+    tot = [0.0, 0.0]
+    for r in range(reps):
+        for i, fn in enumerate(calls):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            R.step()
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            tot[i] += a.elapsed_time(b)
+    return tot[0] / reps, tot[1] / reps
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -465,6 +499,14 @@ def main():
         t_ac, _ = act_ceiling(dev, tok, 4096, reps=20 if tok == 8192 else 10)
         rows[f"per-token activation traffic without arithmetic [{tok},4096] (ceiling, after the steps)"] = \
             row(t_ac, B_ACT * tok * 4096 + 4 * tok, tok * 4096)
+    # the activation phase's position in the step (right after the dequantize
+    # phase, caches cold for X): the quantizer and the same traffic without
+    # arithmetic, alternated over a few more steps
+    t_pos = act_step_position(focus, R, X, ACT, dev)
+    rows["act per token [8192,4096] in the step's position, alternated with the ceiling below (after the steps)"] = \
+        row(t_pos[0], B_ACT * X.numel() + 4 * X.shape[0], X.numel())
+    rows["per-token activation traffic without arithmetic [8192,4096] in the step's position (ceiling, after the steps)"] = \
+        row(t_pos[1], B_ACT * X.numel() + 4 * X.shape[0], X.numel())
     csrc = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
     cdst = torch.empty_like(csrc)
     t_cp = time_calls(lambda: cdst.copy_(csrc), reps=5)
