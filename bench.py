@@ -21,9 +21,12 @@ focus_quantize with w', against the 8 TB/s HBM peak: algorithmic bytes
 (5.3125 B per weight) / mean launch duration, every launch bracketed by HIP
 events on the stream it runs on, and against a hand-written streaming
 kernel that moves one launch's read and write bytes in the same process.
-``rows`` breaks the step down per call and adds rows timed after the steps
-(codes-only quantize, the adjacent formats, the linear layer, and the
-Llama-3.2-1B-shaped set's step).
+``rows`` breaks the step down per call and adds rows timed after the steps:
+codes-only quantize, the adjacent formats, traffic-pattern ceilings (back to
+back, and for the activations also in the activation phase's position in the
+step), the linear layer (8192, 2048 and 16 tokens; one decoder layer as a
+HIP graph replay, and eight distinct layers whose weights stream from HBM),
+and the Llama-3.2-1B-shaped set's step.
 
 ``parity``: right after the timed steps, every output of the last step
 (s2, amax, scale bytes, codes, w' and the dequantized copy of all 224
