@@ -358,13 +358,14 @@ __device__ __forceinline__ int find_tensor(const int64_t* tile_start, int n, int
 
 // Blocks per lane per tile (loads in flight per lane).  Measured on the 8B
 // set: plain NVFP4 without w' streams best with 3 (2: 69.6 %, 3: 71.8 %,
-// 4: 70.5 %, 6: 69.1 %, 8: 68.1 % of peak), every other variant with 2 (4
-// costs the w' kernel about 5 % through its larger register file).
+// 4: 70.5 %, 6: 69.1 %, 8: 68.1 % of peak), MixFP4 with w' with 1 (it then
+// fits 96 VGPRs, five wavefronts per SIMD, see QuantWaves), every other
+// variant with 2 (4 costs the w' kernel about 5 % through its larger
+// register file).
 template <bool DEQ, int MODE>
 struct QuantU {
-    static constexpr int value = (DEQ || MODE != 0) ? 2 : 3;
+    static constexpr int value = MODE == 3 && DEQ ? 1 : (DEQ || MODE != 0) ? 2 : 3;
 };
-constexpr int64_t kQuantTile = (int64_t)kThreads * 2;  // the tile of every U = 2 variant
 
 // FlipQuant MixFP4: is block `blk` of tensor j in an E0M3 tile?  block ->
 // (row, block in row) -> (tile row, tile column) with the batch's div_magic
@@ -386,11 +387,14 @@ __device__ __forceinline__ bool mix_block_is_e0m3(const Batch& bt, int j, int64_
 // Minimum wavefronts per SIMD the register allocation must allow (1: no
 // limit).  FourOverSix codes-only fits 96 VGPRs without spilling, which
 // leaves room for 5 wavefronts instead of 4 (100 VGPRs): 1.12 against
-// 1.15-1.18 ms on 64 linears of the 8B set, identical outputs.  With w' the
-// FourOverSix and MixFP4 kernels spill at that limit and were 25 % slower.
+// 1.15-1.18 ms on 64 linears of the 8B set, identical outputs.  MixFP4 with
+// w' fits them at one block per lane (110 VGPRs and 4 wavefronts at two):
+// 1.91-1.92 against 1.94-1.96 ms on the same linears with 8 x 64 maps.  With
+// w' and two blocks per lane the FourOverSix and MixFP4 kernels spill at
+// that limit and were 25 % slower.
 template <bool DEQ, int MODE>
 struct QuantWaves {
-    static constexpr int value = MODE == 1 && !DEQ ? 5 : 1;
+    static constexpr int value = (MODE == 1 && !DEQ) || (MODE == 3 && DEQ) ? 5 : 1;
 };
 
 template <bool HAS_M, bool HAS_Q, bool DEQ, int MODE = 0, typename Batch = QuantBatch>
@@ -813,10 +817,11 @@ hipError_t launch_quantize(QuantBatch& bt, int key, hipStream_t stream) {
 }
 
 hipError_t launch_quantize_mix(MixBatch& bt, bool deq, hipStream_t stream) {
+    const int64_t tb = (int64_t)kThreads * (deq ? QuantU<true, 3>::value : QuantU<false, 3>::value);
     int64_t t = 0;
     for (int j = 0; j < bt.n; ++j) {
         bt.tile_start[j] = t;
-        t += (bt.nblk[j] + kQuantTile - 1) / kQuantTile;
+        t += (bt.nblk[j] + tb - 1) / tb;
     }
     bt.tile_start[bt.n] = t;
     const dim3 grid(grid_for_tiles(t)), block(kThreads);
