@@ -101,3 +101,65 @@ def test_graph_replays_match_eager(focus):
             a, b = v.view(torch.uint8) if v.dtype != torch.uint8 else v, got[k]
             b = b.view(torch.uint8) if b.dtype != torch.uint8 else b
             assert torch.equal(a, b), f"replay {rep}: {k} differs from the eager result"
+
+
+def test_batched_graph_replays_match_eager(focus):
+    """The batched calls of a weight-set step (tensor scale, quantize with w',
+    dequantize) and the batched FourOverSix and MixFP4 quantizers, prepared
+    once, captured together and replayed: every replay gives the eager bytes."""
+    shapes = [(256, 4096), (1024, 1024), (48, 1536), (8, 64), (200, 14336)]
+    ws = [(torch.randn(s, device=DEV) * (0.01 * (i + 1))).to(torch.bfloat16) for i, s in enumerate(shapes)]
+    ms = [1.0 + 0.2 * (torch.rand((r, c // 16), device=DEV) - 0.5) for r, c in shapes]
+    qs = [6.0 + 2.0 * torch.randn((r, c // 8), device=DEV) for r, c in shapes]
+    maps = [synth.tile_map(r, c, (8, 64), frac=0.3, seed=9, tensor_id=i, device=DEV)
+            for i, (r, c) in enumerate(shapes)]
+    n = len(shapes)
+    s2 = torch.empty((n, 1), dtype=torch.float32, device=DEV)
+    amax = torch.empty((n, 1), dtype=torch.float32, device=DEV)
+    s2s = [s2[i] for i in range(n)]
+
+    def outs():
+        return [focus.Quantized(torch.empty((r, c // 2), dtype=torch.uint8, device=DEV),
+                                torch.empty((r, c // 16), dtype=torch.uint8, device=DEV),
+                                torch.empty((r, c), dtype=torch.bfloat16, device=DEV), s2s[i])
+                for i, (r, c) in enumerate(shapes)]
+
+    oq, of, om = outs(), outs(), outs()
+    deq = [torch.empty(s, dtype=torch.bfloat16, device=DEV) for s in shapes]
+    batches = [
+        focus.tensor_scale_many(ws, s2, amax, run=False),
+        focus.quantize_many(ws, ms, qs, s2s, outs=oq, dequant=True, run=False),
+        focus.dequantize_many([o.codes for o in oq], [o.scales for o in oq], s2s, outs=deq, run=False),
+        focus.quantize_fo6_many(ws, s2s, outs=of, dequant=True, run=False),
+        focus.quantize_mixfp4_many(ws, maps, [(8, 64)] * n, s2s, outs=om, dequant=True, run=False),
+    ]
+    bufs = [s2, amax] + deq + [t for o in oq + of + om for t in (o.codes, o.scales, o.deq)]
+
+    def step():
+        for b in batches:
+            b.run()
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [t.clone() for t in bufs]
+
+    step()
+    eager = snapshot()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in bufs:  # eager work between replays
+            t.fill_(float("nan") if t.is_floating_point() else 0x5A)
+        torch.cuda.synchronize()
+        graph.replay()
+        got = snapshot()
+        for k, (a, b) in enumerate(zip(eager, got)):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep}: buffer {k} differs"
