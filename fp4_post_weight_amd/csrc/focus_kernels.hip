@@ -359,12 +359,17 @@ __device__ __forceinline__ int find_tensor(const int64_t* tile_start, int n, int
 // Blocks per lane per tile (loads in flight per lane).  Measured on the 8B
 // set: plain NVFP4 without w' streams best with 3 (2: 69.6 %, 3: 71.8 %,
 // 4: 70.5 %, 6: 69.1 %, 8: 68.1 % of peak), MixFP4 with w' with 1 (it then
-// fits 96 VGPRs, five wavefronts per SIMD, see QuantWaves), every other
+// fits 96 VGPRs, five wavefronts per SIMD, see QuantWaves), FourOverSix
+// without w' with 5 at four wavefronts per SIMD (the arithmetic of a block
+// is long, so more of the next blocks' loads are in flight while it runs:
+// 3.82 against 3.96 ms with 2 blocks at five wavefronts, medians of four
+// interleaved runs on the same box, identical outputs; 4 blocks 3.84, 6 and
+// 8 at three wavefronts 3.93 and 3.91, 1 block 50-70 % slower), every other
 // variant with 2 (4 costs the w' kernel about 5 % through its larger
 // register file).
 template <bool DEQ, int MODE>
 struct QuantU {
-    static constexpr int value = MODE == 3 && DEQ ? 1 : (DEQ || MODE != 0) ? 2 : 3;
+    static constexpr int value = MODE == 3 && DEQ ? 1 : MODE == 1 && !DEQ ? 5 : (DEQ || MODE != 0) ? 2 : 3;
 };
 
 // FlipQuant MixFP4: is block `blk` of tensor j in an E0M3 tile?  block ->
@@ -385,16 +390,16 @@ __device__ __forceinline__ bool mix_block_is_e0m3(const Batch& bt, int j, int64_
 // lane, no tensor scale); 3: FlipQuant MixFP4 (Batch = MixBatch; each block
 // looks up its tile's map byte: E0M3 if set, FourOverSix otherwise).
 // Minimum wavefronts per SIMD the register allocation must allow (1: no
-// limit).  FourOverSix codes-only fits 96 VGPRs without spilling, which
-// leaves room for 5 wavefronts instead of 4 (100 VGPRs): 1.12 against
-// 1.15-1.18 ms on 64 linears of the 8B set, identical outputs.  MixFP4 with
-// w' fits them at one block per lane (110 VGPRs and 4 wavefronts at two):
-// 1.91-1.92 against 1.94-1.96 ms on the same linears with 8 x 64 maps.  With
-// w' and two blocks per lane the FourOverSix and MixFP4 kernels spill at
-// that limit and were 25 % slower.
+// limit).  FourOverSix codes-only with 5 blocks per lane fits 128 VGPRs
+// without spilling (4 wavefronts; with 2 blocks it fit 96 VGPRs and 5
+// wavefronts, which beat 4 at that block count: 1.12 against 1.15-1.18 ms on
+// 64 linears of the 8B set).  MixFP4 with w' fits 96 VGPRs at one block per
+// lane (110 VGPRs and 4 wavefronts at two): 1.91-1.92 against 1.94-1.96 ms
+// on the same linears with 8 x 64 maps.  With w' and two blocks per lane the
+// FourOverSix and MixFP4 kernels spill at that limit and were 25 % slower.
 template <bool DEQ, int MODE>
 struct QuantWaves {
-    static constexpr int value = (MODE == 1 && !DEQ) || (MODE == 3 && DEQ) ? 5 : 1;
+    static constexpr int value = MODE == 1 && !DEQ ? 4 : MODE == 3 && DEQ ? 5 : 1;
 };
 
 template <bool HAS_M, bool HAS_Q, bool DEQ, int MODE = 0, typename Batch = QuantBatch>
@@ -778,8 +783,14 @@ hipError_t launch_tensor_scale(ScaleBatch& bt, hipStream_t stream) {
 }
 
 hipError_t launch_quantize(QuantBatch& bt, int key, hipStream_t stream) {
-    // keys 0-7: plain NVFP4 (bit 0: w'), 8-9: FourOverSix, 16-23: MXFP4
-    const int64_t tb = (int64_t)kThreads * (key < 8 && !(key & 1) ? QuantU<false, 0>::value : 2);
+    // keys 0-7: plain NVFP4 (bit 0: w'), 8-9: FourOverSix, 16-23: MXFP4; the
+    // tile of the kernel the key selects is kThreads * QuantU blocks
+    const bool dq = key & 1;
+    const int mode = key < 8 ? 0 : key < 16 ? 1 : 2;
+    const int u = mode == 0 ? (dq ? QuantU<true, 0>::value : QuantU<false, 0>::value)
+                : mode == 1 ? (dq ? QuantU<true, 1>::value : QuantU<false, 1>::value)
+                            : (dq ? QuantU<true, 2>::value : QuantU<false, 2>::value);
+    const int64_t tb = (int64_t)kThreads * u;
     int64_t t = 0;
     for (int j = 0; j < bt.n; ++j) {
         bt.tile_start[j] = t;

@@ -639,6 +639,17 @@ def test_fo6_many_matches_single(focus, orc):
         torch.cuda.synchronize()
         assert torch.equal(b.outs[i].codes, single.codes) and torch.equal(b.outs[i].scales, single.scales)
         assert torch.equal(b.outs[i].deq.view(torch.int16), single.deq.view(torch.int16))
+    # the codes-only kernel (a tile size of its own) on the same batch: the
+    # same codes and scales, and the oracle's on a few members
+    bn = focus.quantize_fo6_many(ws, [ts.s2[i] for i in range(len(ws))], dequant=False)
+    torch.cuda.synchronize()
+    for i in range(len(ws)):
+        assert torch.equal(bn.outs[i].codes, b.outs[i].codes), i
+        assert torch.equal(bn.outs[i].scales, b.outs[i].scales), i
+    for i in (0, 5, len(ws) - 1):
+        c, sc, _ = orc.fo6_quantize(np_bits(ws[i].cpu()), np.float32(ts.s2[i].item()), dequant=False)
+        assert np.array_equal(bn.outs[i].codes.cpu().numpy(), c), i
+        assert np.array_equal(bn.outs[i].scales.cpu().numpy(), sc), i
 
 
 # ---------------------------------------------------------------------------
