@@ -208,6 +208,10 @@ def _stream_lib():
     lib.focus_stream_act_pattern.restype = ct.c_int
     lib.focus_stream_act_pattern.argtypes = [ct.c_void_p, ct.c_int64, ct.c_int] + [ct.c_void_p] * 3 + \
         [ct.c_int64, ct.c_void_p]
+    lib.focus_stream_read_pattern.restype = ct.c_int
+    lib.focus_stream_read_pattern.argtypes = [ct.c_void_p, ct.c_int64, ct.c_void_p, ct.c_int, ct.c_int64, ct.c_void_p]
+    lib.focus_stream_deq_pattern.restype = ct.c_int
+    lib.focus_stream_deq_pattern.argtypes = [ct.c_void_p, ct.c_void_p, ct.c_int64, ct.c_void_p, ct.c_void_p]
     return lib
 
 
@@ -280,6 +284,52 @@ def act_ceiling(dev, tokens, hidden, reps=20):
     nbytes = B_ACT * tokens * hidden + 4 * tokens
     del x, codes, scales, s2
     return ms, nbytes / (ms * 1e-3) / 1e9
+
+
+def read_ceiling(dev, nvec, reps=5):
+    """The tensor scale's traffic (nvec 16-byte vectors read once, nothing
+    written but one word per lane) with its work layout (256-lane workgroups
+    striding over tiles, u nontemporal 16-byte loads per lane per tile) and no
+    arithmetic, at u = 4 or 8 and 1024, 2048 or 8192 workgroups; the fastest.
+    Returns (ms, GB/s, u, workgroups)."""
+    import torch
+    lib = _stream_lib()
+    w = torch.ones(nvec * 8, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(8192 * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    best = None
+    for u in (4, 8):
+        for g in (1024, 2048, 8192):
+            def call(u=u, g=g):
+                st = lib.focus_stream_read_pattern(w.data_ptr(), nvec, out.data_ptr(), u, g, stream.cuda_stream)
+                if st != 0:
+                    raise RuntimeError(f"focus_stream_read_pattern failed with HIP error {st}")
+            ms = _time_stream(call, reps)
+            if best is None or ms < best[0]:
+                best = (ms, u, g)
+    del w, out
+    return best[0], nvec * 16.0 / (best[0] * 1e-3) / 1e9, best[1], best[2]
+
+
+def deq_ceiling(dev, nblk, reps=5):
+    """The dequantize's traffic (codes and a scale byte per 16-element block
+    in, 32 bytes of BF16 out) with its work layout (two blocks per lane per
+    tile, output regrouped through LDS into 1 KB contiguous nontemporal
+    stores) and no arithmetic.  Returns (ms, GB/s)."""
+    import torch
+    lib = _stream_lib()
+    codes = torch.ones(nblk * 8, dtype=torch.uint8, device=dev)
+    scales = torch.ones(nblk, dtype=torch.uint8, device=dev)
+    out = torch.empty(nblk * 32, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        st = lib.focus_stream_deq_pattern(codes.data_ptr(), scales.data_ptr(), nblk, out.data_ptr(), stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"focus_stream_deq_pattern failed with HIP error {st}")
+    ms = _time_stream(call, reps)
+    del codes, scales, out
+    return ms, nblk * 41.0 / (ms * 1e-3) / 1e9
 
 
 def act_step_position(focus, R, X, ACT, dev, reps=6):
@@ -512,6 +562,12 @@ def main():
     t_sc, ceil_gbs, ceil_u = stream_ceiling(dev, per_launch_blk)
     rows[f"quantizer's traffic pattern without arithmetic, one launch's blocks, {ceil_u} per lane "
          f"(ceiling, after the steps)"] = row(t_sc, per_launch_blk * 85.0, per_launch_blk * 16)
+    t_rc, _, rc_u, rc_g = read_ceiling(dev, per_launch_blk * 2)
+    rows[f"tensor scale's traffic pattern without arithmetic, one launch's weights, {rc_u} loads per lane, "
+         f"{rc_g} workgroups (ceiling, after the steps)"] = row(t_rc, per_launch_blk * 32.0, per_launch_blk * 16)
+    t_dc, _ = deq_ceiling(dev, per_launch_blk)
+    rows["dequantize's traffic pattern without arithmetic, one launch's blocks (ceiling, after the steps)"] = \
+        row(t_dc, per_launch_blk * 41.0, per_launch_blk * 16)
     for tok in (8192, 131072):
         t_ac, _ = act_ceiling(dev, tok, 4096, reps=20 if tok == 8192 else 10)
         rows[f"per-token activation traffic without arithmetic [{tok},4096] (ceiling, after the steps)"] = \

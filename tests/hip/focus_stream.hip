@@ -9,7 +9,9 @@
 // Each output is a cheap function of the inputs (so no load is dead), and
 // the copy of the weights comes back unchanged.  Its rate is how fast this
 // GPU moves the quantizer's traffic pattern at all: the ceiling for a
-// streaming kernel of that shape.  Loaded by bench.py and by its test.
+// streaming kernel of that shape.  The same for the per-token activations,
+// the tensor scale (reads only) and the dequantize (mostly writes).  Loaded
+// by bench.py and by its test.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -86,6 +88,73 @@ __global__ __launch_bounds__(256) void k_act_pattern(const u32x4* __restrict__ x
     }
 }
 
+
+// The traffic of the tensor scale: nvec 16-byte vectors read once, with the
+// reduction kernel's layout (workgroups of 256 lanes striding over tiles of
+// 256 * U vectors, U nontemporal 16-byte loads per lane per tile), each lane
+// folding what it reads into one word (the maximum of the XOR of each
+// vector's four words), written once at the end.
+template <int U>
+__global__ __launch_bounds__(256) void k_read_pattern(const u32x4* __restrict__ w, int64_t nvec,
+                                                       uint32_t* __restrict__ out) {
+    constexpr int64_t tv = 256 * U;
+    const int64_t ntiles = (nvec + tv - 1) / tv;
+    uint32_t acc = 0;
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int64_t base = t * tv + threadIdx.x;
+        u32x4 v[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t i = base + (int64_t)k * 256;
+            v[k] = i < nvec ? __builtin_nontemporal_load(w + i) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) acc = max(acc, v[k].x ^ v[k].y ^ v[k].z ^ v[k].w);
+    }
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+// The traffic of the dequantize: per 16-element block 8 bytes of codes and
+// one scale byte in, 32 bytes out, with the dequantize kernel's layout (two
+// blocks per lane per tile of 512 blocks; each wavefront's 2 KB of output
+// regrouped through LDS so that every store instruction writes 1 KB of
+// contiguous memory; nontemporal stores).  Block b's output is the two
+// vectors (c.x, c.y, s, c.x ^ s) and (c.y, c.x, s ^ 255, c.y ^ s), c its
+// codes and s its scale byte.
+__global__ __launch_bounds__(256) void k_deq_pattern(const u32x2* __restrict__ codes,
+                                                     const uint8_t* __restrict__ scales, int64_t nblk,
+                                                     u32x4* __restrict__ out, int64_t ntiles) {
+    __shared__ u32x4 xch[4][128];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t tile0 = tile * 512;
+        u32x2 c[2] = {};
+        uint32_t sb[2] = {};
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int64_t blk = tile0 + (int64_t)k * 256 + threadIdx.x;
+            if (blk < nblk) {
+                c[k] = codes[blk];
+                sb[k] = scales[blk];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int64_t first = tile0 + (int64_t)k * 256 + wave * 64;
+            if (first < nblk) {  // uniform per wavefront
+                xch[wave][2 * lane] = u32x4{c[k].x, c[k].y, sb[k], c[k].x ^ sb[k]};
+                xch[wave][2 * lane + 1] = u32x4{c[k].y, c[k].x, sb[k] ^ 255u, c[k].y ^ sb[k]};
+                __builtin_amdgcn_wave_barrier();
+                const u32x4 h0 = xch[wave][lane], h1 = xch[wave][64 + lane];
+                __builtin_amdgcn_wave_barrier();
+                const int64_t halves = 2 * (nblk - first);
+                if (lane < halves) __builtin_nontemporal_store(h0, out + 2 * first + lane);
+                if (64 + lane < halves) __builtin_nontemporal_store(h1, out + 2 * first + 64 + lane);
+            }
+        }
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -142,6 +211,41 @@ int focus_stream_act_pattern(const void* x, int64_t tokens, int rb, void* codes,
                    : rb == 8 ? reinterpret_cast<const void*>(&k_act_pattern<8>) : nullptr;
     if (!fn) return (int)hipErrorInvalidValue;
     return (int)hipLaunchKernel(fn, dim3((unsigned)(grid < (1 << 20) ? grid : (1 << 20))), dim3(256), args, 0,
+                                (hipStream_t)stream);
+}
+
+
+// w [nvec] 16-byte vectors in (16-byte aligned); out [grid * 256] words: word
+// 256 g + t is the maximum over the vectors i with i mod 256 == t and
+// (i / (256 u)) mod grid == g of the XOR of their four words (0 if none).
+// u: 4 or 8 vectors per lane per tile.  Returns 0 or a HIP error code.
+int focus_stream_read_pattern(const void* w, int64_t nvec, void* out, int u, int64_t grid, void* stream) {
+    if (nvec < 0 || grid < 1 || grid > (1 << 20) || !out || (nvec > 0 && !w)) return (int)hipErrorInvalidValue;
+    if (u != 4 && u != 8) return (int)hipErrorInvalidValue;
+    auto W = reinterpret_cast<const u32x4*>(w);
+    auto O = reinterpret_cast<uint32_t*>(out);
+    int64_t n = nvec;
+    void* args[] = {&W, &n, &O};
+    const void* fn = u == 4 ? reinterpret_cast<const void*>(&k_read_pattern<4>)
+                            : reinterpret_cast<const void*>(&k_read_pattern<8>);
+    return (int)hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, (hipStream_t)stream);
+}
+
+// codes [nblk] 8-byte pairs (8-byte aligned) and scales [nblk] bytes in;
+// out [2 * nblk] 16-byte vectors (16-byte aligned): out[2b] = (c.x, c.y, s,
+// c.x ^ s), out[2b + 1] = (c.y, c.x, s ^ 255, c.y ^ s) for c = codes[b],
+// s = scales[b].  Returns 0 or a HIP error code.
+int focus_stream_deq_pattern(const void* codes, const void* scales, int64_t nblk, void* out, void* stream) {
+    if (nblk < 0 || (nblk > 0 && (!codes || !scales || !out))) return (int)hipErrorInvalidValue;
+    if (nblk == 0) return 0;
+    const int64_t ntiles = (nblk + 511) / 512;
+    const int64_t g = ntiles < (1 << 20) ? ntiles : (1 << 20);
+    auto C = reinterpret_cast<const u32x2*>(codes);
+    auto S = reinterpret_cast<const uint8_t*>(scales);
+    auto O = reinterpret_cast<u32x4*>(out);
+    int64_t n = nblk, nt = ntiles;
+    void* args[] = {&C, &S, &n, &O, &nt};
+    return (int)hipLaunchKernel(reinterpret_cast<const void*>(&k_deq_pattern), dim3((unsigned)g), dim3(256), args, 0,
                                 (hipStream_t)stream);
 }
 

@@ -68,3 +68,46 @@ def test_act_pattern_outputs(tokens, rb, grid):
     assert np.array_equal(scales.cpu().numpy().reshape(tokens, nb), ((A[..., 0] ^ B[..., 2]) & 0xFF).astype(np.uint8))
     acc = np.bitwise_xor.reduce(want[:, :, 0].reshape(tokens, rb, 64)[:, :, 0], axis=1) & 0x3FFFFFFF
     assert np.array_equal(s2.cpu().numpy().view(np.uint32), acc.astype(np.uint32))
+
+
+@pytest.mark.parametrize("u", [4, 8])
+@pytest.mark.parametrize("nvec,grid", [(1, 1), (1000, 3), (257 * 8 + 5, 2), (100003, 7)])
+def test_read_pattern_outputs(nvec, grid, u):
+    lib = ct.CDLL(LIB)
+    lib.focus_stream_read_pattern.restype = ct.c_int
+    lib.focus_stream_read_pattern.argtypes = [ct.c_void_p, ct.c_int64, ct.c_void_p, ct.c_int, ct.c_int64, ct.c_void_p]
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(nvec + u)
+    w = torch.randint(-2 ** 31, 2 ** 31 - 1, (nvec * 4,), generator=g, dtype=torch.int64).to(torch.int32)
+    out = torch.full((grid * 256,), -1, dtype=torch.int32, device=dev)
+    assert lib.focus_stream_read_pattern(w.to(dev).data_ptr(), nvec, out.data_ptr(), u, grid,
+                                         torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    wv = w.numpy().view(np.uint32).reshape(nvec, 4)
+    x = wv[:, 0] ^ wv[:, 1] ^ wv[:, 2] ^ wv[:, 3]
+    i = np.arange(nvec)
+    slot = ((i // (256 * u)) % grid) * 256 + i % 256  # the lane that reads vector i
+    want = np.zeros(grid * 256, np.uint32)
+    np.maximum.at(want, slot, x)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), want)
+
+
+@pytest.mark.parametrize("nblk", [1, 63, 64, 513, 100003])
+def test_deq_pattern_outputs(nblk):
+    lib = ct.CDLL(LIB)
+    lib.focus_stream_deq_pattern.restype = ct.c_int
+    lib.focus_stream_deq_pattern.argtypes = [ct.c_void_p, ct.c_void_p, ct.c_int64, ct.c_void_p, ct.c_void_p]
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(nblk)
+    c = torch.randint(-2 ** 31, 2 ** 31 - 1, (nblk * 2,), generator=g, dtype=torch.int64).to(torch.int32)
+    s = torch.randint(0, 256, (nblk,), generator=g, dtype=torch.int64).to(torch.uint8)
+    out = torch.zeros(nblk * 8 + 8, dtype=torch.int32, device=dev)
+    assert lib.focus_stream_deq_pattern(c.to(dev).data_ptr(), s.to(dev).data_ptr(), nblk, out.data_ptr(),
+                                        torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    cv = c.numpy().view(np.uint32).reshape(nblk, 2)
+    sv = s.numpy().astype(np.uint32)
+    want = np.stack([cv[:, 0], cv[:, 1], sv, cv[:, 0] ^ sv, cv[:, 1], cv[:, 0], sv ^ 255, cv[:, 1] ^ sv], 1)
+    o = out.cpu().numpy().view(np.uint32)
+    assert np.array_equal(o[:nblk * 8].reshape(nblk, 8), want)
+    assert not o[nblk * 8:].any()  # nothing written past the end
