@@ -456,7 +456,7 @@ def main():
     # is also the CPU baseline
     par, cpu = None, None
     if not args.no_parity:
-        par, cpu = check_set(R, X, ACT, args, layered)
+        par, cpu = check_set(R, X, ACT, args, layered, label=args.workload.upper())
         for _ in range(2):  # the GPU idled during the oracle pass
             step()
         torch.cuda.synchronize()
