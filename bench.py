@@ -313,7 +313,7 @@ def read_ceiling(dev, nvec, reps=5):
 
 def deq_ceiling(dev, nblk, reps=5):
     """The dequantize's traffic (codes and a scale byte per 16-element block
-    in, 32 bytes of BF16 out) with its work layout (two blocks per lane per
+    in, 32 bytes of BF16 out) with its work layout (one block per lane per
     tile, output regrouped through LDS into 1 KB contiguous nontemporal
     stores) and no arithmetic.  Returns (ms, GB/s)."""
     import torch

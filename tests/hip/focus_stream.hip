@@ -115,8 +115,8 @@ __global__ __launch_bounds__(256) void k_read_pattern(const u32x4* __restrict__ 
 }
 
 // The traffic of the dequantize: per 16-element block 8 bytes of codes and
-// one scale byte in, 32 bytes out, with the dequantize kernel's layout (two
-// blocks per lane per tile of 512 blocks; each wavefront's 2 KB of output
+// one scale byte in, 32 bytes out, with the dequantize kernel's layout (one
+// block per lane per tile of 256 blocks; each wavefront's 2 KB of output
 // regrouped through LDS so that every store instruction writes 1 KB of
 // contiguous memory; nontemporal stores).  Block b's output is the two
 // vectors (c.x, c.y, s, c.x ^ s) and (c.y, c.x, s ^ 255, c.y ^ s), c its
@@ -127,30 +127,23 @@ __global__ __launch_bounds__(256) void k_deq_pattern(const u32x2* __restrict__ c
     __shared__ u32x4 xch[4][128];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int64_t tile0 = tile * 512;
-        u32x2 c[2] = {};
-        uint32_t sb[2] = {};
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int64_t blk = tile0 + (int64_t)k * 256 + threadIdx.x;
-            if (blk < nblk) {
-                c[k] = codes[blk];
-                sb[k] = scales[blk];
-            }
+        const int64_t first = tile * 256 + wave * 64;  // block of lane 0
+        const int64_t blk = first + lane;
+        u32x2 c = {0, 0};
+        uint32_t sb = 0;
+        if (blk < nblk) {
+            c = codes[blk];
+            sb = scales[blk];
         }
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int64_t first = tile0 + (int64_t)k * 256 + wave * 64;
-            if (first < nblk) {  // uniform per wavefront
-                xch[wave][2 * lane] = u32x4{c[k].x, c[k].y, sb[k], c[k].x ^ sb[k]};
-                xch[wave][2 * lane + 1] = u32x4{c[k].y, c[k].x, sb[k] ^ 255u, c[k].y ^ sb[k]};
-                __builtin_amdgcn_wave_barrier();
-                const u32x4 h0 = xch[wave][lane], h1 = xch[wave][64 + lane];
-                __builtin_amdgcn_wave_barrier();
-                const int64_t halves = 2 * (nblk - first);
-                if (lane < halves) __builtin_nontemporal_store(h0, out + 2 * first + lane);
-                if (64 + lane < halves) __builtin_nontemporal_store(h1, out + 2 * first + 64 + lane);
-            }
+        if (first < nblk) {  // uniform per wavefront
+            xch[wave][2 * lane] = u32x4{c.x, c.y, sb, c.x ^ sb};
+            xch[wave][2 * lane + 1] = u32x4{c.y, c.x, sb ^ 255u, c.y ^ sb};
+            __builtin_amdgcn_wave_barrier();
+            const u32x4 h0 = xch[wave][lane], h1 = xch[wave][64 + lane];
+            __builtin_amdgcn_wave_barrier();
+            const int64_t halves = 2 * (nblk - first);
+            if (lane < halves) __builtin_nontemporal_store(h0, out + 2 * first + lane);
+            if (64 + lane < halves) __builtin_nontemporal_store(h1, out + 2 * first + 64 + lane);
         }
     }
 }
@@ -238,7 +231,7 @@ int focus_stream_read_pattern(const void* w, int64_t nvec, void* out, int u, int
 int focus_stream_deq_pattern(const void* codes, const void* scales, int64_t nblk, void* out, void* stream) {
     if (nblk < 0 || (nblk > 0 && (!codes || !scales || !out))) return (int)hipErrorInvalidValue;
     if (nblk == 0) return 0;
-    const int64_t ntiles = (nblk + 511) / 512;
+    const int64_t ntiles = (nblk + 255) / 256;
     const int64_t g = ntiles < (1 << 20) ? ntiles : (1 << 20);
     auto C = reinterpret_cast<const u32x2*>(codes);
     auto S = reinterpret_cast<const uint8_t*>(scales);
