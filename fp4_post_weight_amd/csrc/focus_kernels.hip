@@ -358,18 +358,23 @@ __device__ __forceinline__ int find_tensor(const int64_t* tile_start, int n, int
 
 // Blocks per lane per tile (loads in flight per lane).  Measured on the 8B
 // set: plain NVFP4 without w' streams best with 3 (2: 69.6 %, 3: 71.8 %,
-// 4: 70.5 %, 6: 69.1 %, 8: 68.1 % of peak), MixFP4 with w' with 1 (it then
-// fits 96 VGPRs, five wavefronts per SIMD, see QuantWaves), FourOverSix
+// 4: 70.5 %, 6: 69.1 %, 8: 68.1 % of peak); MXFP4 with w' with 1 (56
+// VGPRs, eight wavefronts per SIMD: 6.15 against 6.34 ms with 2 blocks and
+// 6.55 with 3, medians of four interleaved runs on one box, identical
+// outputs); NVFP4 with w' with 2 (1 block was 1 % faster back to back but
+// not in the step, where each launch follows the tensor scale: 0.897 and
+// 0.912 against 0.893 and 0.895 ms per launch, alternated runs on one box);
+// MixFP4 with w' with 1 (it
+// then fits 96 VGPRs, five wavefronts per SIMD, see QuantWaves), FourOverSix
 // without w' with 5 at four wavefronts per SIMD (the arithmetic of a block
 // is long, so more of the next blocks' loads are in flight while it runs:
 // 3.82 against 3.96 ms with 2 blocks at five wavefronts, medians of four
 // interleaved runs on the same box, identical outputs; 4 blocks 3.84, 6 and
 // 8 at three wavefronts 3.93 and 3.91, 1 block 50-70 % slower), every other
-// variant with 2 (4 costs the w' kernel about 5 % through its larger
-// register file).
+// variant with 2 (FourOverSix with w', MXFP4 and MixFP4 without).
 template <bool DEQ, int MODE>
 struct QuantU {
-    static constexpr int value = MODE == 3 && DEQ ? 1 : MODE == 1 && !DEQ ? 5 : (DEQ || MODE != 0) ? 2 : 3;
+    static constexpr int value = DEQ ? (MODE <= 1 ? 2 : 1) : MODE == 0 ? 3 : MODE == 1 ? 5 : 2;
 };
 
 // FlipQuant MixFP4: is block `blk` of tensor j in an E0M3 tile?  block ->
