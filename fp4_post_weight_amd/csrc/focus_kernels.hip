@@ -364,17 +364,21 @@ __device__ __forceinline__ int find_tensor(const int64_t* tile_start, int n, int
 // outputs); NVFP4 with w' with 2 (1 block was 1 % faster back to back but
 // not in the step, where each launch follows the tensor scale: 0.897 and
 // 0.912 against 0.893 and 0.895 ms per launch, alternated runs on one box);
-// MixFP4 with w' with 1 (it
-// then fits 96 VGPRs, five wavefronts per SIMD, see QuantWaves), FourOverSix
+// MixFP4 with w' with 3 at four wavefronts per SIMD (127 VGPRs: 6.47
+// against 6.60 ms with 1 block at five wavefronts, 6.75 with 2 at four and
+// 6.95 with 4 at three, medians of four interleaved runs, identical
+// outputs), FourOverSix
 // without w' with 5 at four wavefronts per SIMD (the arithmetic of a block
 // is long, so more of the next blocks' loads are in flight while it runs:
 // 3.82 against 3.96 ms with 2 blocks at five wavefronts, medians of four
 // interleaved runs on the same box, identical outputs; 4 blocks 3.84, 6 and
 // 8 at three wavefronts 3.93 and 3.91, 1 block 50-70 % slower), every other
-// variant with 2 (FourOverSix with w', MXFP4 and MixFP4 without).
+// variant with 2 (FourOverSix with w', MXFP4 and MixFP4 without; MXFP4
+// without w' at 3 was no faster, NVFP4 without w' at 1 or 2 5 and 3 %
+// slower than at 3).
 template <bool DEQ, int MODE>
 struct QuantU {
-    static constexpr int value = DEQ ? (MODE <= 1 ? 2 : 1) : MODE == 0 ? 3 : MODE == 1 ? 5 : 2;
+    static constexpr int value = DEQ ? (MODE <= 1 ? 2 : MODE == 2 ? 1 : 3) : MODE == 0 ? 3 : MODE == 1 ? 5 : 2;
 };
 
 // FlipQuant MixFP4: is block `blk` of tensor j in an E0M3 tile?  block ->
@@ -398,13 +402,12 @@ __device__ __forceinline__ bool mix_block_is_e0m3(const Batch& bt, int j, int64_
 // limit).  FourOverSix codes-only with 5 blocks per lane fits 128 VGPRs
 // without spilling (4 wavefronts; with 2 blocks it fit 96 VGPRs and 5
 // wavefronts, which beat 4 at that block count: 1.12 against 1.15-1.18 ms on
-// 64 linears of the 8B set).  MixFP4 with w' fits 96 VGPRs at one block per
-// lane (110 VGPRs and 4 wavefronts at two): 1.91-1.92 against 1.94-1.96 ms
-// on the same linears with 8 x 64 maps.  With w' and two blocks per lane the
-// FourOverSix and MixFP4 kernels spill at that limit and were 25 % slower.
+// 64 linears of the 8B set).  MixFP4 with w' at 3 blocks per lane fits 127
+// VGPRs (4 wavefronts).  With w' and two blocks per lane the FourOverSix and
+// MixFP4 kernels spill at five wavefronts and were 25 % slower.
 template <bool DEQ, int MODE>
 struct QuantWaves {
-    static constexpr int value = MODE == 1 && !DEQ ? 4 : MODE == 3 && DEQ ? 5 : 1;
+    static constexpr int value = (MODE == 1 && !DEQ) || (MODE == 3 && DEQ) ? 4 : 1;
 };
 
 template <bool HAS_M, bool HAS_Q, bool DEQ, int MODE = 0, typename Batch = QuantBatch>
