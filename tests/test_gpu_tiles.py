@@ -114,3 +114,41 @@ def test_dequantize_tiles(focus, orc):
         want = orc.dequantize(q.outs[i].codes.cpu().numpy(), q.outs[i].scales.cpu().numpy(),
                               np.float32(s2s[i].item()))
         assert np.array_equal(_bits(dq.outs[i]), want), NBLK[i]
+
+
+def test_mixed_runs_in_one_batch(focus, orc):
+    """A batched call whose entries alternate between codes only and codes
+    + w' is split into runs of one kernel each, and the two kernels use
+    different tile sizes (FourOverSix 1280 and 512 blocks, MXFP4 512 and
+    256): every entry against the oracle."""
+    ws = _weights(NBLK, 1500)
+    ts = focus.tensor_scale_many(ws)
+    s2s = [ts.s2[i] for i in range(len(ws))]
+    outs = [focus.Quantized(torch.empty((1, w.shape[1] // 2), dtype=torch.uint8, device=DEV),
+                            torch.empty((1, w.shape[1] // 16), dtype=torch.uint8, device=DEV),
+                            torch.empty((1, w.shape[1]), dtype=torch.bfloat16, device=DEV) if i % 2 else None,
+                            s2s[i]) for i, w in enumerate(ws)]
+    b = focus.quantize_fo6_many(ws, s2s, outs=outs, dequant=True)
+    torch.cuda.synchronize()
+    for i, w in enumerate(ws):
+        c, sc, d = orc.fo6_quantize(_bits(w.cpu()), np.float32(s2s[i].item()), dequant=True)
+        assert np.array_equal(b.outs[i].scales.cpu().numpy(), sc), NBLK[i]
+        assert np.array_equal(b.outs[i].codes.cpu().numpy(), c), NBLK[i]
+        if i % 2:
+            assert np.array_equal(_bits(b.outs[i].deq), d), NBLK[i]
+        else:
+            assert b.outs[i].deq is None
+    nb32 = [max(1, n // 2) for n in NBLK]
+    wm = _weights(nb32, 1600, cols_mult=32)
+    om = [focus.Quantized(torch.empty((1, w.shape[1] // 2), dtype=torch.uint8, device=DEV),
+                          torch.empty((1, w.shape[1] // 32), dtype=torch.uint8, device=DEV),
+                          torch.empty((1, w.shape[1]), dtype=torch.bfloat16, device=DEV) if i % 2 else None,
+                          None) for i, w in enumerate(wm)]
+    bm = focus.quantize_mx_many(wm, [None] * len(wm), [None] * len(wm), outs=om, dequant=True)
+    torch.cuda.synchronize()
+    for i, w in enumerate(wm):
+        c, sc, d = orc.mx_quantize(_bits(w.cpu()), None, None, dequant=True)
+        assert np.array_equal(bm.outs[i].scales.cpu().numpy(), sc), nb32[i]
+        assert np.array_equal(bm.outs[i].codes.cpu().numpy(), c), nb32[i]
+        if i % 2:
+            assert np.array_equal(_bits(bm.outs[i].deq), d), nb32[i]
