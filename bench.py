@@ -22,9 +22,11 @@ focus_quantize with w', against the 8 TB/s HBM peak: algorithmic bytes
 events on the stream it runs on, and against a hand-written streaming
 kernel that moves one launch's read and write bytes in the same process.
 ``rows`` breaks the step down per call and adds rows timed after the steps:
-codes-only quantize, the adjacent formats, traffic-pattern ceilings (back to
-back, and for the activations also in the activation phase's position in the
-step), the linear layer (8192, 2048 and 16 tokens; one decoder layer as a
+codes-only quantize, the adjacent formats (FourOverSix also with its weights
+served from the last-level cache, which isolates its arithmetic),
+traffic-pattern ceilings of the quantizer, the tensor scale, the dequantize
+and the activations (back to back, and for the activations also in the
+activation phase's position in the step), the linear layer (8192, 2048 and 16 tokens; one decoder layer as a
 HIP graph replay, and eight distinct layers whose weights stream from HBM),
 and the Llama-3.2-1B-shaped set's step.
 
